@@ -1,0 +1,310 @@
+"""Benchmark of the FlashAttention backward pass on one MI355X.
+
+Default workload: the long-context bf16 GQA causal backward (B=1, Hq=32,
+Hkv=8, S=16384, D=128, scale 1/sqrt(128)), seeded synthetic inputs.  One
+step = the whole backward path: Delta preprocess + dK/dV pass + dQ pass, all
+inputs resident in HBM.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|extras|causal_f32|decode]
+                  [--no-cpu-baseline]
+
+O and L (inputs of the backward) are produced once, before timing, by a plain
+torch fp32 reference forward on the GPU (chunked QK^T / softmax / PV); they are
+inputs only, never part of the timed path.  The cpu_baseline leg times the
+CPU fp64 oracle on one head of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_F32_TFLOPS = 157.3     # fp32 matrix peak
+PEAK_HBM_GBS = 8000.0       # HBM3E
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long", choices=["long", "extras", "causal_f32", "decode"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def _visible_pairs(w) -> int:
+    """Exact count of visible (i, j) pairs per (b, h), from the window/causal geometry."""
+    import numpy as np
+
+    i = np.arange(w.seq_q, dtype=np.int64)
+    qa = i + w.causal_offset
+    hi = np.minimum(w.seq_k, qa + 1) if w.causal else np.full_like(i, w.seq_k)
+    lo = np.zeros_like(i)
+    if w.window > 0:
+        lo = np.maximum(0, qa - w.window + 1)
+        if not w.causal:
+            hi = np.minimum(w.seq_k, qa + w.window)
+    return int(np.maximum(hi - lo, 0).sum())
+
+
+def _torch_reference_forward(q, k, v, w, mask=None, keep=None):
+    """O, L of the workload from plain torch fp32 ops on the GPU (input preparation only)."""
+    import torch
+
+    B, Sq, Hq, D = q.shape
+    Sk = k.shape[1]
+    g = w.num_heads // w.num_kv_heads
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    inv = 1.0 / (1.0 - w.dropout_p) if w.dropout_p > 0 else 1.0
+    chunk = 2048
+    jj = torch.arange(Sk, device=q.device)
+    for b in range(B):
+        for h in range(Hq):
+            kf = k[b, :, h // g, :].float().contiguous()
+            vf = v[b, :, h // g, :].float().contiguous()
+            kt = kf.t().contiguous()
+            for r0 in range(0, Sq, chunk):
+                r1 = min(Sq, r0 + chunk)
+                qf = q[b, r0:r1, h, :].float().contiguous()
+                s = (qf @ kt) * w.scale
+                ii = torch.arange(r0, r1, device=q.device)[:, None] + w.causal_offset
+                vis = torch.ones_like(s, dtype=torch.bool)
+                if w.causal:
+                    vis &= jj[None, :] <= ii
+                if w.window > 0:
+                    vis &= (jj[None, :] - ii).abs() < w.window
+                if mask is not None:
+                    mv = mask[b, 0, r0:r1, :]
+                    vis &= mv > -1e30
+                    s = s + mv
+                s = torch.where(vis, s, torch.full_like(s, -float("inf")))
+                L = torch.logsumexp(s, dim=-1)
+                L = torch.where(torch.isfinite(L), L, torch.full_like(L, float("inf")))
+                p = torch.exp(s - L[:, None])
+                p = torch.where(vis, p, torch.zeros_like(p))
+                if keep is not None:
+                    p = p * keep[b, h, r0:r1, :].float() * inv
+                o[b, r0:r1, h, :] = (p @ vf).to(o.dtype)
+                lse[b, h, r0:r1] = L
+    return o, lse
+
+
+def _cpu_baseline(w, q, k, v, o, do, lse):
+    """Time the fp64 oracle backward on one query head (its KV head) of the workload."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    g = w.num_heads // w.num_kv_heads
+
+    def head(x, h):  # [B,S,H,D] device -> logical [1,1,S,D] float64 host
+        return x[0:1, :, h:h + 1, :].float().cpu().numpy().transpose(0, 2, 1, 3).astype(np.float64)
+
+    qs, dos, os_ = head(q, 0), head(do, 0), head(o, 0)
+    ks, vs = head(k, 0), head(v, 0)
+    ls = lse[0:1, 0:1, :].cpu().numpy().astype(np.float64)
+    spec = oracle.Spec(scale=w.scale, causal=w.causal, causal_offset=w.causal_offset, window=w.window)
+    t0 = time.perf_counter()
+    oracle.backward(qs, ks, vs, os_, dos, ls, spec, None, chunk=2048)
+    dt = time.perf_counter() - t0
+    flops = 10.0 * w.seq_q * w.seq_k * w.head_dim * (0.5 if w.causal else 1.0)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"numpy fp64 oracle backward of one query head (b=0, h=0, its KV head, all "
+                      f"{w.seq_q} rows) of the same workload: {dt:.1f} s for {flops / 1e9:.1f} nominal GFLOP; "
+                      f"group size {g} not included (one head)", "seconds": dt}
+
+
+def bench_prefill(args, w):
+    import numpy as np
+    import torch
+
+    from flashattention_backward_pass_bwd_amd import api, synth
+
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    inp = synth.prefill_inputs(w)
+
+    def up(x):  # logical [B,H,S,D] -> device view [B,S,H,D] in the workload layout
+        t = torch.from_numpy(x)
+        if w.layout == "bshd":
+            return t.permute(0, 2, 1, 3).contiguous().to(tdt).to(dev)
+        return t.contiguous().to(tdt).to(dev).transpose(1, 2)
+
+    q, k, v, do = (up(inp[n]) for n in ("q", "k", "v", "do"))
+    mask = torch.from_numpy(inp["mask"]).to(dev) if inp["mask"] is not None else None
+    del inp
+    p = api.make_params(q, k, scale=w.scale, causal=w.causal, causal_offset=w.causal_offset, window=w.window,
+                        dropout_p=w.dropout_p, seed=w.dropout_seed, mask=mask)
+    keep = api.debug_dropout_keep(p, dev) if w.dropout_p > 0 else None
+    o, lse = _torch_reference_forward(q, k, v, w, mask, keep)
+    del keep
+    torch.cuda.synchronize()
+
+    delta = torch.empty((w.batch, w.num_heads, w.seq_q), dtype=torch.float32, device=dev)
+    dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=dev)
+    dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=dev)
+    dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        api.preprocess(p, o, do, delta)
+        if ev is not None:
+            ev[1].record()
+        api.dkdv(p, q, k, v, do, lse, delta, dk, dv)
+        if ev is not None:
+            ev[2].record()
+        api.dq(p, q, k, v, do, lse, delta, dq)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        step(evs[s])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    ms = total_ms / args.steps
+    t_pre = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    t_dkdv = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    t_dq = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+
+    nominal = 10.0 * w.batch * w.num_heads * w.seq_q * w.seq_k * w.head_dim * (0.5 if w.causal else 1.0)
+    pairs = _visible_pairs(w) * w.batch * w.num_heads
+    value = nominal / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    # dominant kernel: the dK/dV pass executes 4 of the contractions (QK^T, dO V^T, dV, dK): 8*D FLOP per visible pair
+    dkdv_flops = 8.0 * w.head_dim * pairs
+    achieved = dkdv_flops / (t_dkdv * 1e-3) / 1e12
+    out = {
+        "metric": "attention-backward TFLOP/s and % of MI355X bf16 MFMA peak, 1 GPU",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "wall_s_timed": round(wall, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs; O, L from a torch fp32 reference forward)",
+        "config": {"workload": w.name, "batch": w.batch, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+                   "seq_q": w.seq_q, "seq_k": w.seq_k, "head_dim": w.head_dim, "layout": w.layout,
+                   "causal": w.causal, "window": w.window, "mask_density": w.mask_density,
+                   "dropout_p": w.dropout_p, "nominal_gflop": round(nominal / 1e9, 3),
+                   "window_aware_gflop": round(10.0 * w.head_dim * pairs / 1e9, 3)},
+        "kernels_ms": {"preprocess": round(t_pre, 4), "dkdv": round(t_dkdv, 4), "dq": round(t_dq, 4)},
+        "roofline": {"kernel": "dkdv_kernel", "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "per_unit": "8*D FLOP per visible (b,h,i,j) pair", "units": pairs},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = _cpu_baseline(w, q, k, v, o, do, lse)
+    return out
+
+
+def bench_decode(args):
+    import torch
+
+    from flashattention_backward_pass_bwd_amd import api, synth
+
+    w = synth.DECODE_F32
+    dev = torch.device("cuda:0")
+    N, H, Hkv, D, L = w.num_seqs, w.n_heads, w.n_kv_heads, w.head_dim, w.history_len
+    k_hist = torch.empty((N, L, Hkv, D), dtype=torch.float32, device=dev)
+    v_hist = torch.empty_like(k_hist)
+    q = torch.empty((N, H, D), dtype=torch.float32, device=dev)
+    d_out = torch.empty_like(q)
+    for n in range(N):  # per-sequence seeded draws (same recipe as the tests)
+        x = synth.decode_inputs(w, [n])
+        k_hist[n].copy_(torch.from_numpy(x["k_hist"][0]))
+        v_hist[n].copy_(torch.from_numpy(x["v_hist"][0]))
+        q[n].copy_(torch.from_numpy(x["q"][0]))
+        d_out[n].copy_(torch.from_numpy(x["d_out"][0]))
+    g = H // Hkv
+    # probs = softmax(q K^T), unscaled, from plain torch fp32 ops (input preparation only)
+    probs = torch.empty((N, H, L), dtype=torch.float32, device=dev)
+    for n in range(N):
+        kk = k_hist[n].permute(1, 2, 0).contiguous()                 # [Hkv, D, L]
+        qq = q[n].view(Hkv, g, D)
+        probs[n] = torch.softmax(torch.matmul(qq, kk), dim=-1).reshape(H, L)
+    d_scores = torch.empty_like(probs)
+    d_q = torch.empty_like(q)
+    for _ in range(args.warmup):
+        api.decode_backward(k_hist, v_hist, probs, d_out, d_scores, d_q)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        api.decode_backward(k_hist, v_hist, probs, d_out, d_scores, d_q)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = start.elapsed_time(stop) / args.steps
+    nbytes = 4 * (2 * N * L * Hkv * D + 2 * N * H * L + 2 * N * H * D)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": "decode-step attention-backward HBM GB/s, 1 GPU",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "wall_s_timed": round(wall, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "num_seqs": N, "n_heads": H, "n_kv_heads": Hkv, "head_dim": D,
+                   "history_len": L, "algorithmic_bytes": nbytes},
+        "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "per_unit": "bytes of K,V rows + probs/d_scores + d_out/d_q", "units": nbytes},
+    }
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
+              "the per-GPU kernel is what one GPU runs when the work is sharded by (batch, KV head).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from flashattention_backward_pass_bwd_amd import synth
+
+    if args.workload == "decode":
+        out = bench_decode(args)
+    else:
+        w = {"long": synth.LONG_BF16, "extras": synth.EXTRAS_BF16, "causal_f32": synth.CAUSAL_F32}[args.workload]
+        out = bench_prefill(args, w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

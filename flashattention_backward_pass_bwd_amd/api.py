@@ -1,0 +1,158 @@
+"""torch-facing wrappers over the C ABI (marshalling only).
+
+Tensor convention: query-side tensors (q, o, do, dq) are indexed [B, Sq, Hq, D]
+and key-side tensors (k, v, dk, dv) [B, Sk, Hkv, D]; any strides are accepted
+as long as D is unit-stride, rows are 16-byte aligned and the tensors of one
+side share one stride set (so [B,H,S,D] storage is passed as ``x.transpose(1, 2)``).
+lse and delta are fp32 contiguous [B, Hq, Sq].  All calls enqueue on torch's
+current HIP stream and return without synchronising.
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+
+def _vp(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.FA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return _lib.FA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float32")
+
+
+def make_params(q: torch.Tensor, k: torch.Tensor, *, scale: float, causal: bool = False,
+                causal_offset: int = 0, window: int = 0, dropout_p: float = 0.0, seed: int = 0,
+                mask: torch.Tensor | None = None) -> _lib.FaBwdParams:
+    """Fill ``fa_bwd_params`` from a query-side and a key-side tensor.
+
+    ``mask``: fp32 tensor broadcastable to [B, Hq, Sq, Sk] (e.g. [B, 1, Sq, Sk]);
+    broadcast dimensions become stride-0.
+    """
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-d [B, S, H, D] views")
+    B, Sq, Hq, D = q.shape
+    Bk, Sk, Hkv, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError("q and k disagree on batch or head_dim")
+    if q.dtype != k.dtype:
+        raise TypeError("q and k must share a dtype")
+    p = _lib.FaBwdParams()
+    p.dtype = _dtype_code(q)
+    p.batch, p.num_heads, p.num_kv_heads, p.seq_q, p.seq_k, p.head_dim = B, Hq, Hkv, Sq, Sk, D
+    p.q_stride_b, p.q_stride_s, p.q_stride_h = (int(s) for s in q.stride()[:3])
+    p.kv_stride_b, p.kv_stride_s, p.kv_stride_h = (int(s) for s in k.stride()[:3])
+    if q.stride(3) != 1 or k.stride(3) != 1:
+        raise ValueError("head_dim must be unit-stride")
+    p.scale = float(scale)
+    p.causal = 1 if causal else 0
+    p.causal_offset = int(causal_offset)
+    p.window = int(window)
+    p.dropout_p = float(dropout_p)
+    p.seed = int(seed) & 0xFFFFFFFF
+    if mask is not None:
+        if mask.dtype != torch.float32:
+            raise TypeError("mask must be float32")
+        m = mask.expand(B, Hq, Sq, Sk)
+        p.mask = m.data_ptr()
+        p.mask_stride_b, p.mask_stride_h, p.mask_stride_q, p.mask_stride_k = (int(s) for s in m.stride())
+    return p
+
+
+def _same_layout(ref: torch.Tensor, *others: torch.Tensor) -> None:
+    for t in others:
+        if t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype:
+            raise ValueError("tensors of one side must share shape, strides and dtype")
+
+
+def _like(t: torch.Tensor) -> torch.Tensor:
+    return torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
+
+
+def preprocess(p: _lib.FaBwdParams, o: torch.Tensor, do: torch.Tensor, delta: torch.Tensor | None = None):
+    _same_layout(o, do)
+    if delta is None:
+        delta = torch.empty((p.batch, p.num_heads, p.seq_q), dtype=torch.float32, device=o.device)
+    _lib.check("fa_bwd_preprocess", _lib.lib().fa_bwd_preprocess(
+        ctypes.byref(p), _vp(o), _vp(do), _vp(delta), _stream()))
+    return delta
+
+
+def dkdv(p: _lib.FaBwdParams, q, k, v, do, lse, delta, dk=None, dv=None):
+    _same_layout(q, do)
+    _same_layout(k, v)
+    dk = _like(k) if dk is None else dk
+    dv = _like(v) if dv is None else dv
+    _same_layout(k, dk, dv)
+    _lib.check("fa_bwd_dkdv", _lib.lib().fa_bwd_dkdv(
+        ctypes.byref(p), _vp(q), _vp(k), _vp(v), _vp(do), _vp(lse), _vp(delta), _vp(dk), _vp(dv),
+        _stream()))
+    return dk, dv
+
+
+def dq(p: _lib.FaBwdParams, q, k, v, do, lse, delta, dq_out=None):
+    _same_layout(q, do)
+    _same_layout(k, v)
+    dq_out = _like(q) if dq_out is None else dq_out
+    _same_layout(q, dq_out)
+    _lib.check("fa_bwd_dq", _lib.lib().fa_bwd_dq(
+        ctypes.byref(p), _vp(q), _vp(k), _vp(v), _vp(do), _vp(lse), _vp(delta), _vp(dq_out),
+        _stream()))
+    return dq_out
+
+
+def backward(q, k, v, o, do, lse, *, scale, causal=False, causal_offset=0, window=0, dropout_p=0.0,
+             seed=0, mask=None):
+    """Delta preprocess, then the dK/dV and dQ passes; returns (dq, dk, dv, delta)."""
+    p = make_params(q, k, scale=scale, causal=causal, causal_offset=causal_offset, window=window,
+                    dropout_p=dropout_p, seed=seed, mask=mask)
+    _same_layout(q, o, do)
+    delta = preprocess(p, o, do)
+    dk_, dv_ = dkdv(p, q, k, v, do, lse, delta)
+    dq_ = dq(p, q, k, v, do, lse, delta)
+    return dq_, dk_, dv_, delta
+
+
+def decode_params(k_hist: torch.Tensor, probs: torch.Tensor) -> _lib.FaDecodeParams:
+    N, L, Hkv, D = k_hist.shape
+    p = _lib.FaDecodeParams()
+    p.num_seqs, p.n_heads, p.n_kv_heads, p.head_dim, p.history_len = N, probs.shape[1], Hkv, D, L
+    return p
+
+
+def decode_backward(k_hist, v_hist, probs, d_out, d_scores=None, d_q=None):
+    """Decode-step backward: returns (d_scores [N,H,len], d_q [N,H,D]); fp32 contiguous tensors."""
+    for t in (k_hist, v_hist, probs, d_out):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous float32")
+    p = decode_params(k_hist, probs)
+    d_scores = torch.empty_like(probs) if d_scores is None else d_scores
+    d_q = torch.empty_like(d_out) if d_q is None else d_q
+    _lib.check("fa_bwd_decode", _lib.lib().fa_bwd_decode(
+        ctypes.byref(p), _vp(k_hist), _vp(v_hist), _vp(probs), _vp(d_out), _vp(d_scores), _vp(d_q),
+        _stream()))
+    return d_scores, d_q
+
+
+def debug_visibility(p: _lib.FaBwdParams, device) -> torch.Tensor:
+    out = torch.empty((p.batch, p.num_heads, p.seq_q, p.seq_k), dtype=torch.uint8, device=device)
+    _lib.check("fa_bwd_debug_visibility", _lib.lib().fa_bwd_debug_visibility(ctypes.byref(p), _vp(out), _stream()))
+    return out
+
+
+def debug_dropout_keep(p: _lib.FaBwdParams, device) -> torch.Tensor:
+    out = torch.empty((p.batch, p.num_heads, p.seq_q, p.seq_k), dtype=torch.uint8, device=device)
+    _lib.check("fa_bwd_debug_dropout_keep", _lib.lib().fa_bwd_debug_dropout_keep(ctypes.byref(p), _vp(out), _stream()))
+    return out

@@ -1,0 +1,185 @@
+// C ABI of libfa_bwd.so (declared in include/fa_bwd.h).
+//
+// Every check runs here, on the host, before any HIP call; the launchers
+// behind it assume validated arguments.  The library allocates nothing and
+// only enqueues work on the caller's stream.
+#include <math.h>
+
+#include "fa_bwd.h"
+#include "fa_internal.h"
+
+namespace {
+
+using fa::PrefillArgs;
+
+int elem_bytes(int dtype) { return dtype == FA_DTYPE_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxSeq = int64_t(1) << 30;
+
+fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
+  if (p == nullptr) return FA_ERR_NULL;
+  if (p->dtype != FA_DTYPE_F32 && p->dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (p->batch <= 0 || p->num_heads <= 0 || p->num_kv_heads <= 0 || p->seq_q <= 0 || p->seq_k <= 0 ||
+      p->head_dim <= 0)
+    return FA_ERR_SHAPE;
+  if (p->num_heads % p->num_kv_heads != 0) return FA_ERR_SHAPE;
+  if (p->head_dim != 64 && p->head_dim != 128) return FA_ERR_UNSUPPORTED;
+  if (p->seq_q > kMaxSeq || p->seq_k > kMaxSeq || p->causal_offset > kMaxSeq || p->window > kMaxSeq)
+    return FA_ERR_UNSUPPORTED;
+  if (p->causal != 0 && p->causal != 1) return FA_ERR_ARG;
+  if (p->causal_offset < 0 || p->window < 0) return FA_ERR_ARG;
+  if (!(p->dropout_p >= 0.0f && p->dropout_p < 1.0f)) return FA_ERR_ARG;  // also rejects NaN
+  const int64_t qs[3] = {p->q_stride_b, p->q_stride_s, p->q_stride_h};
+  const int64_t ks[3] = {p->kv_stride_b, p->kv_stride_s, p->kv_stride_h};
+  const int64_t per16 = 16 / elem_bytes(p->dtype);
+  for (int i = 0; i < 3; ++i) {
+    if (qs[i] < 0 || ks[i] < 0) return FA_ERR_ARG;
+    if (qs[i] % per16 != 0 || ks[i] % per16 != 0) return FA_ERR_ALIGN;
+  }
+  if (p->mask != nullptr) {
+    if (p->mask_stride_b < 0 || p->mask_stride_h < 0 || p->mask_stride_q < 0 || p->mask_stride_k < 0)
+      return FA_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(p->mask) & 3u) != 0) return FA_ERR_ALIGN;
+  }
+  // Grid sizes (the kernels index blocks with 32-bit integers).
+  const int64_t nq = (p->seq_q + fa::kDqRowsPerBlock - 1) / fa::kDqRowsPerBlock;
+  const int64_t nk = (p->seq_k + fa::kDkdvKeysPerBlock - 1) / fa::kDkdvKeysPerBlock;
+  if (nq * p->batch * p->num_heads >= (int64_t(1) << 31) || nk * p->batch * p->num_kv_heads >= (int64_t(1) << 31))
+    return FA_ERR_UNSUPPORTED;
+
+  a->B = p->batch;
+  a->Hq = p->num_heads;
+  a->Hkv = p->num_kv_heads;
+  a->Sq = p->seq_q;
+  a->Sk = p->seq_k;
+  a->group = p->num_heads / p->num_kv_heads;
+  a->qsb = p->q_stride_b;
+  a->qss = p->q_stride_s;
+  a->qsh = p->q_stride_h;
+  a->ksb = p->kv_stride_b;
+  a->kss = p->kv_stride_s;
+  a->ksh = p->kv_stride_h;
+  a->scale = p->scale;
+  a->scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  a->causal = p->causal;
+  a->offset = p->causal_offset;
+  a->window = p->window;
+  const double pf = (double)p->dropout_p;  // the fp32 value, exactly
+  a->drop = pf > 0.0 ? 1 : 0;
+  a->drop_thr = (uint32_t)floor(pf * 4294967296.0);  // exact: an fp32 times 2^32
+  a->drop_inv = (float)(1.0 / (1.0 - pf));
+  a->seed_mix = fa::fmix32(p->seed);
+  a->mask = p->mask;
+  a->msb = p->mask_stride_b;
+  a->msh = p->mask_stride_h;
+  a->msq = p->mask_stride_q;
+  a->msk = p->mask_stride_k;
+  return FA_OK;
+}
+
+fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+hipStream_t as_stream(fa_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_bwd_preprocess(const fa_bwd_params* p, const void* O, const void* dO, float* delta,
+                            fa_stream_t stream) {
+  PrefillArgs a;
+  if (p == nullptr || O == nullptr || dO == nullptr || delta == nullptr) return FA_ERR_NULL;
+  fa_status s = check_prefill(p, &a);
+  if (s != FA_OK) return s;
+  if (!aligned16(O) || !aligned16(dO) || (reinterpret_cast<uintptr_t>(delta) & 3u)) return FA_ERR_ALIGN;
+  return hip_status(fa::launch_preprocess(a, p->dtype, p->head_dim, O, dO, delta, as_stream(stream)));
+}
+
+fa_status fa_bwd_dkdv(const fa_bwd_params* p, const void* Q, const void* K, const void* V,
+                      const void* dO, const float* L, const float* delta, void* dK, void* dV,
+                      fa_stream_t stream) {
+  PrefillArgs a;
+  if (p == nullptr || Q == nullptr || K == nullptr || V == nullptr || dO == nullptr || L == nullptr ||
+      delta == nullptr || dK == nullptr || dV == nullptr)
+    return FA_ERR_NULL;
+  fa_status s = check_prefill(p, &a);
+  if (s != FA_OK) return s;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(dK) || !aligned16(dV) ||
+      (reinterpret_cast<uintptr_t>(L) & 3u) || (reinterpret_cast<uintptr_t>(delta) & 3u))
+    return FA_ERR_ALIGN;
+  return hip_status(fa::launch_dkdv(a, p->dtype, p->head_dim, Q, K, V, dO, L, delta, dK, dV, as_stream(stream)));
+}
+
+fa_status fa_bwd_dq(const fa_bwd_params* p, const void* Q, const void* K, const void* V,
+                    const void* dO, const float* L, const float* delta, void* dQ,
+                    fa_stream_t stream) {
+  PrefillArgs a;
+  if (p == nullptr || Q == nullptr || K == nullptr || V == nullptr || dO == nullptr || L == nullptr ||
+      delta == nullptr || dQ == nullptr)
+    return FA_ERR_NULL;
+  fa_status s = check_prefill(p, &a);
+  if (s != FA_OK) return s;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(dQ) ||
+      (reinterpret_cast<uintptr_t>(L) & 3u) || (reinterpret_cast<uintptr_t>(delta) & 3u))
+    return FA_ERR_ALIGN;
+  return hip_status(fa::launch_dq(a, p->dtype, p->head_dim, Q, K, V, dO, L, delta, dQ, as_stream(stream)));
+}
+
+int32_t fa_bwd_decode_max_history(const fa_decode_params* p) {
+  if (p == nullptr || p->n_kv_heads <= 0 || p->n_heads <= 0 || p->n_heads % p->n_kv_heads != 0) return 0;
+  return fa::decode_max_history(p->n_heads / p->n_kv_heads);
+}
+
+fa_status fa_bwd_decode(const fa_decode_params* p, const float* k_hist, const float* v_hist,
+                        const float* probs, const float* d_out, float* d_scores, float* d_q,
+                        fa_stream_t stream) {
+  if (p == nullptr || k_hist == nullptr || v_hist == nullptr || probs == nullptr || d_out == nullptr ||
+      d_scores == nullptr || d_q == nullptr)
+    return FA_ERR_NULL;
+  if (p->num_seqs <= 0 || p->n_heads <= 0 || p->n_kv_heads <= 0 || p->head_dim <= 0 || p->history_len <= 0)
+    return FA_ERR_SHAPE;
+  if (p->n_heads % p->n_kv_heads != 0) return FA_ERR_SHAPE;
+  const int g = p->n_heads / p->n_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return FA_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) return FA_ERR_UNSUPPORTED;
+  if (p->history_len > fa::decode_max_history(g)) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)p->num_seqs * p->n_kv_heads >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(k_hist) || !aligned16(v_hist) || !aligned16(d_out) || !aligned16(d_q) ||
+      (reinterpret_cast<uintptr_t>(probs) & 3u) || (reinterpret_cast<uintptr_t>(d_scores) & 3u))
+    return FA_ERR_ALIGN;
+  fa::DecodeArgs a{p->num_seqs, p->n_heads, p->n_kv_heads, p->head_dim, p->history_len, g};
+  return hip_status(fa::launch_decode(a, k_hist, v_hist, probs, d_out, d_scores, d_q, as_stream(stream)));
+}
+
+const char* fa_bwd_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: a size is <= 0 or num_heads is not a multiple of num_kv_heads";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head_dim, dtype, grouping or length outside the built kernels";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a base pointer or row stride is not 16-byte aligned";
+    case FA_ERR_ARG: return "FA_ERR_ARG: invalid scalar argument (dropout_p, causal, offset, window or stride)";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+  }
+  return "unknown fa_status";
+}
+
+fa_status fa_bwd_debug_visibility(const fa_bwd_params* p, uint8_t* out, fa_stream_t stream) {
+  PrefillArgs a;
+  if (p == nullptr || out == nullptr) return FA_ERR_NULL;
+  fa_status s = check_prefill(p, &a);
+  if (s != FA_OK) return s;
+  return hip_status(fa::launch_debug_visibility(a, out, as_stream(stream)));
+}
+
+fa_status fa_bwd_debug_dropout_keep(const fa_bwd_params* p, uint8_t* out, fa_stream_t stream) {
+  PrefillArgs a;
+  if (p == nullptr || out == nullptr) return FA_ERR_NULL;
+  fa_status s = check_prefill(p, &a);
+  if (s != FA_OK) return s;
+  return hip_status(fa::launch_debug_dropout(a, out, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,179 @@
+// Device-side building blocks shared by the gfx950 attention-backward kernels:
+// the launch-argument block, the element visibility / mask / dropout rules,
+// and the 32x32 MFMA operand helpers.  Internal to libfa_bwd.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kMaskedSentinel = -1.0e30f;  // an additive mask entry <= this excludes the element
+
+// Everything a prefill kernel needs, resolved on the host (passed by value).
+struct PrefillArgs {
+  int B, Hq, Hkv, Sq, Sk, group;  // group = Hq / Hkv
+  int64_t qsb, qss, qsh;          // element strides of Q, O, dO, dQ
+  int64_t ksb, kss, ksh;          // element strides of K, V, dK, dV
+  float scale;                    // softmax scale (applied to dQ and dK at the end)
+  float scale_log2;               // scale * log2(e): P = exp2(qk * scale_log2 + mask * log2e - L * log2e)
+  int causal, offset, window;
+  int drop;                       // dropout enabled (p > 0)
+  uint32_t drop_thr;              // keep iff draw >= drop_thr
+  float drop_inv;                 // 1 / (1 - p), rounded to fp32
+  uint32_t seed_mix;              // fmix32(seed)
+  const float* mask;
+  int64_t msb, msh, msq, msk;
+};
+
+// MurmurHash3 32-bit finaliser (Appleby, public domain).
+__host__ __device__ __forceinline__ uint32_t fmix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x85EBCA6Bu;
+  x ^= x >> 13;
+  x *= 0xC2B2AE35u;
+  x ^= x >> 16;
+  return x;
+}
+
+// Per-row part of the dropout draw: fmix32(((b*Hq + h)*Sq + i) + fmix32(seed)), mod 2^32.
+__device__ __forceinline__ uint32_t drop_row_key(const PrefillArgs& a, int b, int h, int i) {
+  uint32_t row = ((uint32_t)b * (uint32_t)a.Hq + (uint32_t)h) * (uint32_t)a.Sq + (uint32_t)i;
+  return fmix32(row + a.seed_mix);
+}
+
+// Keep bit of element (row key rk, key j): fmix32(rk ^ j*0x9E3779B9) >= threshold.
+__device__ __forceinline__ bool drop_keep(uint32_t rk, int j, uint32_t thr) {
+  return fmix32(rk ^ ((uint32_t)j * 0x9E3779B9u)) >= thr;
+}
+
+// Geometric visibility (ferrotensor-backend flash_attention_v2_backward.wgsl, fab2_visible).
+__device__ __forceinline__ bool visible(const PrefillArgs& a, int i, int j) {
+  if (i >= a.Sq || j >= a.Sk || i < 0 || j < 0) return false;
+  const int qa = i + a.offset;
+  if (a.causal && j > qa) return false;
+  if (a.window > 0) {
+    int d = j - qa;
+    d = d < 0 ? -d : d;
+    if (d >= a.window) return false;
+  }
+  return true;
+}
+
+__device__ __forceinline__ float mask_at(const PrefillArgs& a, int b, int h, int i, int j) {
+  return a.mask[(int64_t)b * a.msb + (int64_t)h * a.msh + (int64_t)i * a.msq + (int64_t)j * a.msk];
+}
+
+// Is every element of the rectangle rows [i0, i1] x keys [j0, j1] geometrically visible?
+__device__ __forceinline__ bool rect_all_visible(const PrefillArgs& a, int i0, int i1, int j0, int j1) {
+  if (i1 >= a.Sq || j1 >= a.Sk) return false;
+  if (a.causal && j1 > i0 + a.offset) return false;
+  if (a.window > 0) {
+    if ((i1 + a.offset) - j0 >= a.window) return false;
+    if (j1 - (i0 + a.offset) >= a.window) return false;
+  }
+  return true;
+}
+
+// Is no element of the rectangle visible (so the tile can be skipped)?
+__device__ __forceinline__ bool rect_none_visible(const PrefillArgs& a, int i0, int i1, int j0, int j1) {
+  if (i0 >= a.Sq || j0 >= a.Sk) return true;
+  if (a.causal && j0 > i1 + a.offset) return true;
+  if (a.window > 0) {
+    if (j0 - (i1 + a.offset) >= a.window) return true;   // every key right of every query's window
+    if ((i0 + a.offset) - j1 >= a.window) return true;   // every key left of every query's window
+  }
+  return false;
+}
+
+// Keys [begin, end) that any query in [q0, q1] can see (tile-range version of the predicate).
+__device__ __forceinline__ void key_range(const PrefillArgs& a, int q0, int q1, int& begin, int& end) {
+  long e = a.Sk;
+  long bg = 0;
+  if (a.causal) e = min(e, (long)q1 + a.offset + 1);
+  if (a.window > 0) {
+    bg = max(0L, (long)q0 + a.offset - a.window + 1);
+    if (!a.causal) e = min(e, (long)q1 + a.offset + a.window);
+  }
+  begin = (int)bg;
+  end = (int)max(e, bg);
+}
+
+// Queries [begin, end) that can see any key in [k0, k1].
+__device__ __forceinline__ void query_range(const PrefillArgs& a, int k0, int k1, int& begin, int& end) {
+  long bg = 0, e = a.Sq;
+  if (a.causal) bg = max(0L, (long)k0 - a.offset);
+  if (a.window > 0) {
+    e = min(e, max(0L, (long)k1 + a.window - a.offset));
+    if (!a.causal) bg = max(bg, (long)k0 - a.window - a.offset + 1);
+  }
+  begin = (int)min(bg, (long)a.Sq);
+  end = (int)max(e, (long)begin);
+}
+
+// ----------------------------------------------------------------------------
+// 32x32 MFMA operand chunks.  A "chunk" is the 16 bytes one lane supplies per
+// k-block: 8 bf16 (one v_mfma_f32_32x32x16_bf16) or 4 fp32 (four
+// v_mfma_f32_32x32x2_f32).  Lane l supplies row/column l%32 and the k-slice
+// selected by its half h = l/32; A and B use the same (h, element) -> k map,
+// so any consistent assignment of k indices to (h, element) is a valid
+// contraction.  C layout: lane l holds column l%32 and rows
+// 8*(r/4) + 4*h + (r%4) for r = 0..15.
+// ----------------------------------------------------------------------------
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<__bf16> {
+  static constexpr int CH = 8;  // elements per lane per chunk
+  using chunk = bf16x8;
+  static __device__ __forceinline__ void run(f32x16& c, const chunk& a, const chunk& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // Pack C registers [r0, r0+8) into a B-operand chunk (RNE to bf16).
+  static __device__ __forceinline__ chunk from_acc(const f32x16& c, int r0) {
+    chunk o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (__bf16)c[r0 + e];
+    return o;
+  }
+};
+
+template <>
+struct Mma<float> {
+  static constexpr int CH = 4;
+  using chunk = f32x4;
+  static __device__ __forceinline__ void run(f32x16& c, const chunk& a, const chunk& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1], b[1], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2], b[2], c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[3], b[3], c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ chunk from_acc(const f32x16& c, int r0) {
+    chunk o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = c[r0 + e];
+    return o;
+  }
+};
+
+// 16-byte global / LDS loads and stores.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::chunk ld16(const T* p) {
+  return *reinterpret_cast<const typename Mma<T>::chunk*>(p);
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x) { return (T)x; }
+
+}  // namespace fa

@@ -1,0 +1,250 @@
+// Key-block-outer pass: dK and dV without atomics (ferrotensor-backend
+// flash_attention_v2_backward.wgsl, flash_bwd_dk_dv; formulas from its header
+// comment).  For each key j of KV head kvh, summed over the query heads of the
+// GQA group and over every query i that sees it:
+//   dV_j = sum_i P_ij M_ij dO_i,     dK_j = scale * sum_i dS_ij Q_i,
+//   P_ij = exp(S_ij - L_i) on counted elements (0 elsewhere),
+//   dS_ij = P_ij (M_ij dO_i.V_j - Delta_i).
+//
+// gfx950 design: a 256-thread block owns 128 keys of one (b, kvh); each of its
+// four waves keeps its 32 keys' K and V rows in registers as MFMA B operands
+// and accumulates dK^T, dV^T (D x 32, fp32) in registers.  The block streams
+// BQ-row tiles of Q and dO through LDS, stored row-major (A operand of
+// S = Q K^T and dP = dO V^T) and transposed (A operand of dV^T += dO^T (P.M)
+// and dK^T += Q^T dS).  S and dP come out of the MFMA in the C layout whose
+// per-lane column is a key, which is exactly the B-operand layout the second
+// pair of contractions needs, so P and dS never leave registers.
+#include "fa_internal.h"
+
+namespace fa {
+
+template <typename T, int D, int BQ, bool MASK, bool DROP>
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __restrict__ Q,
+                                                      const T* __restrict__ K,
+                                                      const T* __restrict__ V,
+                                                      const T* __restrict__ dO,
+                                                      const float* __restrict__ L,
+                                                      const float* __restrict__ Dl,
+                                                      T* __restrict__ dK, T* __restrict__ dV) {
+  using M = Mma<T>;
+  using chunk = typename M::chunk;
+  constexpr int CH = M::CH;
+  constexpr int KS = D / (2 * CH);            // k-blocks of the head_dim contraction
+  constexpr int PR = D + 16 / (int)sizeof(T);  // row-major LDS pitch (elements): +16 B per row
+  constexpr int PT = BQ + 4;                   // transposed LDS pitch (elements)
+  constexpr int MB = BQ / 32;                  // 32-row blocks in a Q tile
+  constexpr int TC = 16 / CH;                  // B-operand chunks per 32-row C block
+  constexpr int DB = D / 32;                   // 32-row blocks of dK^T / dV^T
+
+  __shared__ __attribute__((aligned(16))) T sQ[BQ * PR];
+  __shared__ __attribute__((aligned(16))) T sdO[BQ * PR];
+  __shared__ __attribute__((aligned(16))) T sQT[D * PT];
+  __shared__ __attribute__((aligned(16))) T sdOT[D * PT];
+  __shared__ float sL[BQ];
+  __shared__ float sDel[BQ];
+  __shared__ uint32_t sRK[DROP ? BQ : 1];
+
+  const int nbh = a.B * a.Hkv;
+  const int kb = blockIdx.x / nbh;  // ascending key block: longest causal work first
+  const int bh = blockIdx.x % nbh;  // consecutive blocks cycle over (b, kvh) -> one XCD per KV head
+  const int b = bh / a.Hkv;
+  const int kvh = bh % a.Hkv;
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  const int h2 = lane / 32;
+  const int l32 = lane % 32;
+  const int k0 = kb * kDkdvKeysPerBlock;
+  const int kw0 = k0 + wave * kDkdvKeysPerWave;
+  const int jl = kw0 + l32;  // this lane's key (its C-layout column)
+
+  chunk kr[KS], vr[KS];
+  const int64_t koff = (int64_t)b * a.ksb + (int64_t)jl * a.kss + (int64_t)kvh * a.ksh;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (jl < a.Sk) {
+      kr[s] = ld16<T>(K + koff + 2 * CH * s + CH * h2);
+      vr[s] = ld16<T>(V + koff + 2 * CH * s + CH * h2);
+    } else {
+      kr[s] = chunk{};
+      vr[s] = chunk{};
+    }
+  }
+
+  f32x16 acck[DB], accv[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) {
+    acck[d] = f32x16{};
+    accv[d] = f32x16{};
+  }
+
+  int qb, qe;
+  query_range(a, k0, min(k0 + kDkdvKeysPerBlock, a.Sk) - 1, qb, qe);
+
+  for (int g = 0; g < a.group; ++g) {
+    const int h = kvh * a.group + g;
+    const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq;
+    for (int qt = qb; qt < qe; qt += BQ) {
+      __syncthreads();  // the previous tile has been consumed
+      for (int c = tid; c < BQ * (D / CH); c += 256) {
+        const int r = c / (D / CH);
+        const int cc = c % (D / CH);
+        const int i = qt + r;
+        chunk qv{}, gv{};
+        if (i < a.Sq) {
+          const int64_t off = (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh + cc * CH;
+          qv = ld16<T>(Q + off);
+          gv = ld16<T>(dO + off);
+        }
+        *reinterpret_cast<chunk*>(&sQ[r * PR + cc * CH]) = qv;
+        *reinterpret_cast<chunk*>(&sdO[r * PR + cc * CH]) = gv;
+#pragma unroll
+        for (int e = 0; e < CH; ++e) {
+          sQT[(cc * CH + e) * PT + r] = qv[e];
+          sdOT[(cc * CH + e) * PT + r] = gv[e];
+        }
+      }
+      for (int r = tid; r < BQ; r += 256) {
+        const int i = qt + r;
+        const bool in = i < a.Sq;
+        sL[r] = in ? L[lrow + i] * kLog2e : __builtin_inff();
+        sDel[r] = in ? Dl[lrow + i] : 0.f;
+        if constexpr (DROP) sRK[r] = drop_row_key(a, b, h, i);
+      }
+      __syncthreads();
+
+      if (rect_none_visible(a, qt, qt + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1)) continue;
+      const bool full = !MASK && !DROP && rect_all_visible(a, qt, qt + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1);
+
+      // S = Q K^T and dP = dO V^T for this wave's 32 keys (C column = key).
+      f32x16 s[MB], dp[MB];
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        s[m] = f32x16{};
+        dp[m] = f32x16{};
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          const int base = (32 * m + l32) * PR + 2 * CH * ks + CH * h2;
+          M::run(s[m], *reinterpret_cast<const chunk*>(&sQ[base]), kr[ks]);
+          M::run(dp[m], *reinterpret_cast<const chunk*>(&sdO[base]), vr[ks]);
+        }
+      }
+
+      // Elementwise: P, dropout, dS.  s <- P*M, dp <- dS.
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * m + 8 * (r / 4) + 4 * h2 + (r % 4);
+          const int i = qt + row;
+          const float l2 = sL[row];
+          float p;
+          if (full) {
+            p = __builtin_amdgcn_exp2f(s[m][r] * a.scale_log2 - l2);
+          } else {
+            bool ok = visible(a, i, jl);
+            float madd = 0.f;
+            if constexpr (MASK) {
+              if (ok) {
+                const float mv = mask_at(a, b, h, i, jl);
+                ok = !(mv <= kMaskedSentinel);
+                madd = mv * kLog2e;
+              }
+            }
+            p = ok ? __builtin_amdgcn_exp2f(s[m][r] * a.scale_log2 + madd - l2) : 0.f;
+          }
+          float dpv = dp[m][r];
+          float pm = p;
+          if constexpr (DROP) {
+            const float mm = drop_keep(sRK[row], jl, a.drop_thr) ? a.drop_inv : 0.f;
+            dpv *= mm;
+            pm = p * mm;
+          }
+          dp[m][r] = p * (dpv - sDel[row]);
+          s[m][r] = pm;
+        }
+      }
+
+      // dV^T += dO^T (P.M),  dK^T += Q^T dS  (contraction over the tile's queries).
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+#pragma unroll
+        for (int t = 0; t < TC; ++t) {
+          const chunk pmc = M::from_acc(s[m], t * CH);
+          const chunk dsc = M::from_acc(dp[m], t * CH);
+#pragma unroll
+          for (int d = 0; d < DB; ++d) {
+            const int trow = (32 * d + l32) * PT;
+            chunk ao, aq;
+#pragma unroll
+            for (int sg = 0; sg < CH / 4; ++sg) {
+              const int q = 32 * m + 8 * ((CH / 4) * t + sg) + 4 * h2;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                ao[4 * sg + e] = sdOT[trow + q + e];
+                aq[4 * sg + e] = sQT[trow + q + e];
+              }
+            }
+            M::run(accv[d], ao, pmc);
+            M::run(acck[d], aq, dsc);
+          }
+        }
+      }
+    }
+  }
+
+  if (jl < a.Sk) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dd = 32 * d + 8 * r4 + 4 * h2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dK[koff + dd + e] = from_f32<T>(acck[d][4 * r4 + e] * a.scale);
+          dV[koff + dd + e] = from_f32<T>(accv[d][4 * r4 + e]);
+        }
+      }
+    }
+  }
+}
+
+template <typename T, int D, bool MASK, bool DROP>
+static hipError_t launch_t(const PrefillArgs& a, const void* Q, const void* K, const void* V,
+                           const void* dO, const float* L, const float* delta, void* dK, void* dV,
+                           hipStream_t st) {
+  constexpr int BQ = 64;
+  const int nkb = (a.Sk + kDkdvKeysPerBlock - 1) / kDkdvKeysPerBlock;
+  const unsigned grid = (unsigned)(nkb * a.B * a.Hkv);
+  hipLaunchKernelGGL((dkdv_kernel<T, D, BQ, MASK, DROP>), dim3(grid), dim3(256), 0, st, a,
+                     static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
+                     static_cast<const T*>(dO), L, delta, static_cast<T*>(dK), static_cast<T*>(dV));
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, const void* V,
+                           const void* dO, const float* L, const float* delta, void* dK, void* dV,
+                           hipStream_t st) {
+  const bool mask = a.mask != nullptr;
+  const bool drop = a.drop != 0;
+  if (mask && drop) return launch_t<T, D, true, true>(a, Q, K, V, dO, L, delta, dK, dV, st);
+  if (mask) return launch_t<T, D, true, false>(a, Q, K, V, dO, L, delta, dK, dV, st);
+  if (drop) return launch_t<T, D, false, true>(a, Q, K, V, dO, L, delta, dK, dV, st);
+  return launch_t<T, D, false, false>(a, Q, K, V, dO, L, delta, dK, dV, st);
+}
+
+hipError_t launch_dkdv(const PrefillArgs& a, int dtype, int D, const void* Q, const void* K,
+                       const void* V, const void* dO, const float* L, const float* delta, void* dK,
+                       void* dV, hipStream_t st) {
+  if (dtype == kBF16)
+    return D == 64 ? launch_d<__bf16, 64>(a, Q, K, V, dO, L, delta, dK, dV, st)
+                   : launch_d<__bf16, 128>(a, Q, K, V, dO, L, delta, dK, dV, st);
+  return D == 64 ? launch_d<float, 64>(a, Q, K, V, dO, L, delta, dK, dV, st)
+                 : launch_d<float, 128>(a, Q, K, V, dO, L, delta, dK, dV, st);
+}
+
+}  // namespace fa

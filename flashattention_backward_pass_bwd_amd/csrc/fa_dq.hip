@@ -1,0 +1,221 @@
+// Query-block-outer pass: dQ without atomics (rustytorch
+// flash_attention_backward_dq.metal kernel; ferrotensor-backend
+// flash_attention_v2_backward.wgsl, flash_bwd_dq second sweep, with L given):
+//   dQ_i = scale * sum_j dS_ij K_j,  dS_ij = P_ij (M_ij dO_i.V_j - Delta_i),
+//   P_ij = exp(S_ij - L_i) on counted elements, 0 elsewhere.
+//
+// gfx950 design: a 256-thread block owns 128 query rows of one (b, h); each
+// wave keeps its 32 rows of Q and dO in registers as MFMA B operands and
+// accumulates dQ^T (D x 32, fp32).  The block streams BK-key tiles of K and V
+// through LDS (row-major: A operand of S^T = K Q^T and dP^T = V dO^T; K also
+// transposed: A operand of dQ^T += K^T dS^T).  S^T comes out of the MFMA with
+// one query per lane column, so dS^T is already the B operand of the last
+// contraction and L_i, Delta_i are per-lane scalars.
+#include "fa_internal.h"
+
+namespace fa {
+
+template <typename T, int D, int BK, bool MASK, bool DROP>
+__global__ __launch_bounds__(256, 1) void dq_kernel(PrefillArgs a, const T* __restrict__ Q,
+                                                    const T* __restrict__ K,
+                                                    const T* __restrict__ V,
+                                                    const T* __restrict__ dO,
+                                                    const float* __restrict__ L,
+                                                    const float* __restrict__ Dl,
+                                                    T* __restrict__ dQ) {
+  using M = Mma<T>;
+  using chunk = typename M::chunk;
+  constexpr int CH = M::CH;
+  constexpr int KS = D / (2 * CH);
+  constexpr int PR = D + 16 / (int)sizeof(T);
+  constexpr int PT = BK + 4;
+  constexpr int MB = BK / 32;
+  constexpr int TC = 16 / CH;
+  constexpr int DB = D / 32;
+
+  __shared__ __attribute__((aligned(16))) T sK[BK * PR];
+  __shared__ __attribute__((aligned(16))) T sV[BK * PR];
+  __shared__ __attribute__((aligned(16))) T sKT[D * PT];
+
+  const int nbh = a.B * a.Hq;
+  const int nqb = (a.Sq + kDqRowsPerBlock - 1) / kDqRowsPerBlock;
+  const int qbi = nqb - 1 - (int)(blockIdx.x / nbh);  // last query block first: longest causal work
+  // Consecutive blocks cycle over KV heads first, so the query heads of one
+  // KV head land on the same XCD (blocks are dealt round-robin over XCDs).
+  const int bhi = blockIdx.x % nbh;
+  const int kvh = bhi % a.Hkv;
+  const int rest = bhi / a.Hkv;
+  const int gi = rest % a.group;
+  const int b = rest / a.group;
+  const int h = kvh * a.group + gi;
+
+  const int tid = threadIdx.x;
+  const int wave = tid / 64;
+  const int lane = tid % 64;
+  const int h2 = lane / 32;
+  const int l32 = lane % 32;
+  const int q0 = qbi * kDqRowsPerBlock;
+  const int qw0 = q0 + wave * kDqRowsPerWave;
+  const int il = qw0 + l32;  // this lane's query row (its C-layout column)
+
+  chunk qr[KS], gr[KS];
+  const int64_t qoff = (int64_t)b * a.qsb + (int64_t)il * a.qss + (int64_t)h * a.qsh;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (il < a.Sq) {
+      qr[s] = ld16<T>(Q + qoff + 2 * CH * s + CH * h2);
+      gr[s] = ld16<T>(dO + qoff + 2 * CH * s + CH * h2);
+    } else {
+      qr[s] = chunk{};
+      gr[s] = chunk{};
+    }
+  }
+  const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq + il;
+  const float l2 = il < a.Sq ? L[lrow] * kLog2e : __builtin_inff();
+  const float del = il < a.Sq ? Dl[lrow] : 0.f;
+  uint32_t rk = 0;
+  if constexpr (DROP) rk = drop_row_key(a, b, h, il);
+
+  f32x16 accq[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) accq[d] = f32x16{};
+
+  int kb, ke;
+  key_range(a, q0, min(q0 + kDqRowsPerBlock, a.Sq) - 1, kb, ke);
+
+  for (int kt = kb; kt < ke; kt += BK) {
+    __syncthreads();
+    for (int c = tid; c < BK * (D / CH); c += 256) {
+      const int r = c / (D / CH);
+      const int cc = c % (D / CH);
+      const int j = kt + r;
+      chunk kv{}, vv{};
+      if (j < a.Sk) {
+        const int64_t off = (int64_t)b * a.ksb + (int64_t)j * a.kss + (int64_t)kvh * a.ksh + cc * CH;
+        kv = ld16<T>(K + off);
+        vv = ld16<T>(V + off);
+      }
+      *reinterpret_cast<chunk*>(&sK[r * PR + cc * CH]) = kv;
+      *reinterpret_cast<chunk*>(&sV[r * PR + cc * CH]) = vv;
+#pragma unroll
+      for (int e = 0; e < CH; ++e) sKT[(cc * CH + e) * PT + r] = kv[e];
+    }
+    __syncthreads();
+
+    if (rect_none_visible(a, qw0, qw0 + kDqRowsPerWave - 1, kt, kt + BK - 1)) continue;
+    const bool full = !MASK && !DROP && rect_all_visible(a, qw0, qw0 + kDqRowsPerWave - 1, kt, kt + BK - 1);
+
+    // S^T = K Q^T, dP^T = V dO^T (C column = query).
+    f32x16 st[MB], dpt[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      st[m] = f32x16{};
+      dpt[m] = f32x16{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const int base = (32 * m + l32) * PR + 2 * CH * ks + CH * h2;
+        M::run(st[m], *reinterpret_cast<const chunk*>(&sK[base]), qr[ks]);
+        M::run(dpt[m], *reinterpret_cast<const chunk*>(&sV[base]), gr[ks]);
+      }
+    }
+
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = kt + 32 * m + 8 * (r / 4) + 4 * h2 + (r % 4);
+        float p;
+        if (full) {
+          p = __builtin_amdgcn_exp2f(st[m][r] * a.scale_log2 - l2);
+        } else {
+          bool ok = visible(a, il, j);
+          float madd = 0.f;
+          if constexpr (MASK) {
+            if (ok) {
+              const float mv = mask_at(a, b, h, il, j);
+              ok = !(mv <= kMaskedSentinel);
+              madd = mv * kLog2e;
+            }
+          }
+          p = ok ? __builtin_amdgcn_exp2f(st[m][r] * a.scale_log2 + madd - l2) : 0.f;
+        }
+        float dpv = dpt[m][r];
+        if constexpr (DROP) dpv *= drop_keep(rk, j, a.drop_thr) ? a.drop_inv : 0.f;
+        dpt[m][r] = p * (dpv - del);
+      }
+    }
+
+    // dQ^T += K^T dS^T (contraction over the tile's keys).
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+#pragma unroll
+      for (int t = 0; t < TC; ++t) {
+        const chunk dsc = M::from_acc(dpt[m], t * CH);
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          const int trow = (32 * d + l32) * PT;
+          chunk ak;
+#pragma unroll
+          for (int sg = 0; sg < CH / 4; ++sg) {
+            const int kk = 32 * m + 8 * ((CH / 4) * t + sg) + 4 * h2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ak[4 * sg + e] = sKT[trow + kk + e];
+          }
+          M::run(accq[d], ak, dsc);
+        }
+      }
+    }
+  }
+
+  if (il < a.Sq) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int dd = 32 * d + 8 * r4 + 4 * h2;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dQ[qoff + dd + e] = from_f32<T>(accq[d][4 * r4 + e] * a.scale);
+      }
+    }
+  }
+}
+
+template <typename T, int D, bool MASK, bool DROP>
+static hipError_t launch_t(const PrefillArgs& a, const void* Q, const void* K, const void* V,
+                           const void* dO, const float* L, const float* delta, void* dQ,
+                           hipStream_t st) {
+  constexpr int BK = 64;
+  const int nqb = (a.Sq + kDqRowsPerBlock - 1) / kDqRowsPerBlock;
+  const unsigned grid = (unsigned)(nqb * a.B * a.Hq);
+  hipLaunchKernelGGL((dq_kernel<T, D, BK, MASK, DROP>), dim3(grid), dim3(256), 0, st, a,
+                     static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
+                     static_cast<const T*>(dO), L, delta, static_cast<T*>(dQ));
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, const void* V,
+                           const void* dO, const float* L, const float* delta, void* dQ,
+                           hipStream_t st) {
+  const bool mask = a.mask != nullptr;
+  const bool drop = a.drop != 0;
+  if (mask && drop) return launch_t<T, D, true, true>(a, Q, K, V, dO, L, delta, dQ, st);
+  if (mask) return launch_t<T, D, true, false>(a, Q, K, V, dO, L, delta, dQ, st);
+  if (drop) return launch_t<T, D, false, true>(a, Q, K, V, dO, L, delta, dQ, st);
+  return launch_t<T, D, false, false>(a, Q, K, V, dO, L, delta, dQ, st);
+}
+
+hipError_t launch_dq(const PrefillArgs& a, int dtype, int D, const void* Q, const void* K,
+                     const void* V, const void* dO, const float* L, const float* delta, void* dQ,
+                     hipStream_t st) {
+  if (dtype == kBF16)
+    return D == 64 ? launch_d<__bf16, 64>(a, Q, K, V, dO, L, delta, dQ, st)
+                   : launch_d<__bf16, 128>(a, Q, K, V, dO, L, delta, dQ, st);
+  return D == 64 ? launch_d<float, 64>(a, Q, K, V, dO, L, delta, dQ, st)
+                 : launch_d<float, 128>(a, Q, K, V, dO, L, delta, dQ, st);
+}
+
+}  // namespace fa

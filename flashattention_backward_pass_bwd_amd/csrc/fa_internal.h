@@ -1,0 +1,38 @@
+// Launchers shared between the kernel translation units and the C ABI layer.
+// Every launcher assumes its arguments were validated by fa_api.cpp.
+#pragma once
+
+#include "fa_common.h"
+
+namespace fa {
+
+enum { kF32 = 0, kBF16 = 1 };
+
+// Launch geometry of the prefill kernels (also used by the host for checks).
+constexpr int kDkdvKeysPerWave = 32;
+constexpr int kDkdvWaves = 4;
+constexpr int kDkdvKeysPerBlock = kDkdvKeysPerWave * kDkdvWaves;
+constexpr int kDqRowsPerWave = 32;
+constexpr int kDqWaves = 4;
+constexpr int kDqRowsPerBlock = kDqRowsPerWave * kDqWaves;
+
+struct DecodeArgs {
+  int N, H, Hkv, D, len, g;
+};
+
+hipError_t launch_preprocess(const PrefillArgs& a, int dtype, int D, const void* O, const void* dO,
+                             float* delta, hipStream_t st);
+hipError_t launch_dkdv(const PrefillArgs& a, int dtype, int D, const void* Q, const void* K,
+                       const void* V, const void* dO, const float* L, const float* delta, void* dK,
+                       void* dV, hipStream_t st);
+hipError_t launch_dq(const PrefillArgs& a, int dtype, int D, const void* Q, const void* K,
+                     const void* V, const void* dO, const float* L, const float* delta, void* dQ,
+                     hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, const float* k_hist, const float* v_hist,
+                         const float* probs, const float* d_out, float* d_scores, float* d_q,
+                         hipStream_t st);
+int decode_max_history(int g);
+hipError_t launch_debug_visibility(const PrefillArgs& a, uint8_t* out, hipStream_t st);
+hipError_t launch_debug_dropout(const PrefillArgs& a, uint8_t* out, hipStream_t st);
+
+}  // namespace fa

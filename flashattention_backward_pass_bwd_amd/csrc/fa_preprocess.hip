@@ -1,0 +1,55 @@
+// Delta_i = sum_d dO_id * O_id for every (b, h, i) row (rustytorch
+// flash_attention_backward_dq.metal, header: D = rowsum(dO * O);
+// ferrotensor-backend flash_attention_v2_backward.wgsl, pass-1 Delta).
+//
+// HBM-bound: each row is read once as 16-byte chunks by a group of lanes,
+// multiplied in fp32 and reduced across the group with butterfly shuffles.
+#include "fa_internal.h"
+
+namespace fa {
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void preprocess_kernel(PrefillArgs a, const T* __restrict__ O,
+                                                         const T* __restrict__ dO,
+                                                         float* __restrict__ delta) {
+  constexpr int CH = Mma<T>::CH;          // elements per 16-byte chunk
+  constexpr int LPR = D / CH;             // lanes per row
+  constexpr int RPB = 256 / LPR;          // rows per block
+  const int lane_in_row = threadIdx.x % LPR;
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const int i = (int)(row % a.Sq);
+    const int64_t bh = row / a.Sq;
+    const int h = (int)(bh % a.Hq);
+    const int b = (int)(bh / a.Hq);
+    const int64_t off = (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh + lane_in_row * CH;
+    const auto o = ld16<T>(O + off);
+    const auto g = ld16<T>(dO + off);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) acc += to_f32(g[e]) * to_f32(o[e]);
+  }
+#pragma unroll
+  for (int s = LPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s, LPR);
+  if (row < rows && lane_in_row == 0) delta[row] = acc;
+}
+
+template <typename T, int D>
+static hipError_t launch(const PrefillArgs& a, const void* O, const void* dO, float* delta, hipStream_t st) {
+  constexpr int LPR = D / Mma<T>::CH;
+  constexpr int RPB = 256 / LPR;
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+  const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
+  hipLaunchKernelGGL((preprocess_kernel<T, D>), dim3(grid), dim3(256), 0, st, a,
+                     static_cast<const T*>(O), static_cast<const T*>(dO), delta);
+  return hipGetLastError();
+}
+
+hipError_t launch_preprocess(const PrefillArgs& a, int dtype, int D, const void* O, const void* dO,
+                             float* delta, hipStream_t st) {
+  if (dtype == kBF16) return D == 64 ? launch<__bf16, 64>(a, O, dO, delta, st) : launch<__bf16, 128>(a, O, dO, delta, st);
+  return D == 64 ? launch<float, 64>(a, O, dO, delta, st) : launch<float, 128>(a, O, dO, delta, st);
+}
+
+}  // namespace fa

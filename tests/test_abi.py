@@ -1,0 +1,162 @@
+"""C ABI checks that need no GPU (CPU only).
+
+* libfa_bwd.so loads and exports every function include/fa_bwd.h declares;
+* the ctypes mirrors of the parameter structs match the C layout (gcc probe);
+* every invalid argument is rejected with its status code before any HIP call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from flashattention_backward_pass_bwd_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_bwd.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libfa_bwd.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:fa_status|int32_t|const char\*)\s+(fa_bwd_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_surface():
+    assert _declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    for name in _declared_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_struct_layouts_match_c():
+    src = r"""
+    #include <stdio.h>
+    #include <stddef.h>
+    #include "fa_bwd.h"
+    #define F(s, m) printf(#m " %zu\n", offsetof(s, m));
+    int main(void) {
+      printf("size_bwd %zu\nsize_dec %zu\n", sizeof(fa_bwd_params), sizeof(fa_decode_params));
+      F(fa_bwd_params, q_stride_b) F(fa_bwd_params, kv_stride_h) F(fa_bwd_params, scale)
+      F(fa_bwd_params, dropout_p) F(fa_bwd_params, seed) F(fa_bwd_params, mask) F(fa_bwd_params, mask_stride_k)
+      F(fa_decode_params, history_len)
+      return 0;
+    }
+    """
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "probe.c")
+        exe = os.path.join(d, "probe")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+        lines = dict(l.split() for l in subprocess.run([exe], capture_output=True, text=True).stdout.splitlines())
+    assert int(lines["size_bwd"]) == ctypes.sizeof(_lib.FaBwdParams)
+    assert int(lines["size_dec"]) == ctypes.sizeof(_lib.FaDecodeParams)
+    for name in ("q_stride_b", "kv_stride_h", "scale", "dropout_p", "seed", "mask", "mask_stride_k"):
+        assert int(lines[name]) == getattr(_lib.FaBwdParams, name).offset, name
+    assert int(lines["history_len"]) == _lib.FaDecodeParams.history_len.offset
+
+
+def _valid():
+    p = _lib.FaBwdParams()
+    p.dtype = _lib.FA_DTYPE_BF16
+    p.batch, p.num_heads, p.num_kv_heads, p.seq_q, p.seq_k, p.head_dim = 2, 8, 2, 100, 120, 128
+    p.q_stride_b, p.q_stride_s, p.q_stride_h = 100 * 8 * 128, 8 * 128, 128
+    p.kv_stride_b, p.kv_stride_s, p.kv_stride_h = 120 * 2 * 128, 2 * 128, 128
+    p.scale = 0.088
+    return p
+
+
+FAKE = ctypes.c_void_p(4096)  # never dereferenced: every case below fails validation first
+
+BAD = [
+    ("head_dim", 96, _lib.FA_ERR_UNSUPPORTED),
+    ("head_dim", 0, _lib.FA_ERR_SHAPE),
+    ("dtype", 7, _lib.FA_ERR_UNSUPPORTED),
+    ("batch", 0, _lib.FA_ERR_SHAPE),
+    ("seq_q", -1, _lib.FA_ERR_SHAPE),
+    ("seq_k", 0, _lib.FA_ERR_SHAPE),
+    ("num_kv_heads", 3, _lib.FA_ERR_SHAPE),
+    ("dropout_p", 1.0, _lib.FA_ERR_ARG),
+    ("dropout_p", -0.1, _lib.FA_ERR_ARG),
+    ("dropout_p", float("nan"), _lib.FA_ERR_ARG),
+    ("causal_offset", -1, _lib.FA_ERR_ARG),
+    ("window", -5, _lib.FA_ERR_ARG),
+    ("causal", 2, _lib.FA_ERR_ARG),
+    ("q_stride_s", 8 * 128 + 4, _lib.FA_ERR_ALIGN),
+    ("kv_stride_h", 130, _lib.FA_ERR_ALIGN),
+    ("q_stride_b", -1, _lib.FA_ERR_ARG),
+]
+
+
+@pytest.mark.parametrize("field,value,code", BAD)
+def test_invalid_prefill_arguments(field, value, code):
+    L = _lib.lib()
+    p = _valid()
+    setattr(p, field, value)
+    P = ctypes.byref(p)
+    assert L.fa_bwd_preprocess(P, FAKE, FAKE, FAKE, None) == code
+    assert L.fa_bwd_dkdv(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
+    assert L.fa_bwd_dq(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
+    assert L.fa_bwd_debug_visibility(P, FAKE, None) == code
+    assert L.fa_bwd_debug_dropout_keep(P, FAKE, None) == code
+
+
+def test_null_and_misaligned_pointers():
+    L = _lib.lib()
+    p = _valid()
+    P = ctypes.byref(p)
+    assert L.fa_bwd_preprocess(None, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_NULL
+    assert L.fa_bwd_preprocess(P, None, FAKE, FAKE, None) == _lib.FA_ERR_NULL
+    assert L.fa_bwd_dkdv(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == _lib.FA_ERR_NULL
+    assert L.fa_bwd_dq(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.FA_ERR_NULL
+    odd = ctypes.c_void_p(4096 + 8)
+    assert L.fa_bwd_preprocess(P, odd, FAKE, FAKE, None) == _lib.FA_ERR_ALIGN
+    assert L.fa_bwd_dkdv(P, FAKE, odd, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_ALIGN
+    assert L.fa_bwd_dq(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, odd, None) == _lib.FA_ERR_ALIGN
+    p.mask = 4096 + 2
+    assert L.fa_bwd_dq(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_ALIGN
+    p.mask = 4096
+    p.mask_stride_q = -2
+    assert L.fa_bwd_dq(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_ARG
+
+
+def test_invalid_decode_arguments():
+    L = _lib.lib()
+
+    def dp(**kw):
+        p = _lib.FaDecodeParams()
+        p.num_seqs, p.n_heads, p.n_kv_heads, p.head_dim, p.history_len = 4, 32, 8, 256, 4096
+        for k, v in kw.items():
+            setattr(p, k, v)
+        return p
+
+    def call(p, *ptrs):
+        ptrs = ptrs or (FAKE,) * 6
+        return L.fa_bwd_decode(ctypes.byref(p), *ptrs, None)
+
+    assert call(dp(n_kv_heads=5)) == _lib.FA_ERR_SHAPE
+    assert call(dp(num_seqs=0)) == _lib.FA_ERR_SHAPE
+    assert call(dp(n_heads=48, n_kv_heads=4)) == _lib.FA_ERR_UNSUPPORTED  # 12 heads per KV head
+    assert call(dp(head_dim=96)) == _lib.FA_ERR_UNSUPPORTED
+    maxlen = L.fa_bwd_decode_max_history(ctypes.byref(dp()))
+    assert maxlen >= 8192
+    assert call(dp(history_len=maxlen + 1)) == _lib.FA_ERR_UNSUPPORTED
+    assert call(dp(), None, FAKE, FAKE, FAKE, FAKE, FAKE) == _lib.FA_ERR_NULL
+    assert call(dp(), FAKE, ctypes.c_void_p(4100), FAKE, FAKE, FAKE, FAKE) == _lib.FA_ERR_ALIGN
+    assert L.fa_bwd_decode_max_history(ctypes.byref(dp(n_heads=30))) == 0
+
+
+def test_status_strings():
+    for code in range(-6, 1):
+        s = _lib.status_string(code)
+        assert s.startswith("FA_")
+    assert "unknown" in _lib.status_string(-99)
