@@ -32,6 +32,10 @@ PEAK_F32_TFLOPS = 157.3     # fp32 matrix peak
 PEAK_HBM_GBS = 8000.0       # HBM3E
 
 
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,9 +156,11 @@ def bench_prefill(args, w):
     p = api.make_params(q, k, scale=w.scale, causal=w.causal, causal_offset=w.causal_offset, window=w.window,
                         dropout_p=w.dropout_p, seed=w.dropout_seed, mask=mask)
     keep = api.debug_dropout_keep(p, dev) if w.dropout_p > 0 else None
+    _log(f"inputs of {w.name} on device; reference forward for O, L")
     o, lse = _torch_reference_forward(q, k, v, w, mask, keep)
     del keep
     torch.cuda.synchronize()
+    _log("O, L ready; timing")
 
     delta = torch.empty((w.batch, w.num_heads, w.seq_q), dtype=torch.float32, device=dev)
     dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=dev)
@@ -225,8 +231,11 @@ def bench_prefill(args, w):
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
                      "per_unit": "8*D FLOP per visible (b,h,i,j) pair", "units": pairs},
     }
+    _log(f"timed {args.steps} steps: {ms:.3f} ms/step")
     if not args.no_cpu_baseline:
+        _log("cpu baseline: oracle on one head")
         out["cpu_baseline"] = _cpu_baseline(w, q, k, v, o, do, lse)
+        _log(f"cpu baseline took {out['cpu_baseline']['seconds']:.1f} s")
     return out
 
 
