@@ -5,7 +5,7 @@ Hkv=8, S=16384, D=128, scale 1/sqrt(128)), seeded synthetic inputs.  One
 step = the whole backward path: Delta preprocess + dK/dV pass + dQ pass, all
 inputs resident in HBM.  Prints ONE JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|extras|causal_f32|decode]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|extras|causal_f32|decode|copy]
                   [--no-cpu-baseline]
 
 O and L (inputs of the backward) are produced once, before timing, by a plain
@@ -41,7 +41,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="long", choices=["long", "extras", "causal_f32", "decode"])
+    ap.add_argument("--workload", default="long", choices=["long", "extras", "causal_f32", "decode", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -293,6 +293,30 @@ def bench_decode(args):
     }
 
 
+def bench_copy(args):
+    """A plain device copy of known size: calibrates the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = 1 << 28  # 2^28 fp32 = 1 GiB read + 1 GiB written per launch
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    nbytes = 2 * 4 * n
+    return {"metric": "device copy GB/s (counter calibration)", "value": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic", "config": {"workload": "copy_1GiB", "bytes_read": 4 * n, "bytes_written": 4 * n}}
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -309,6 +333,8 @@ def main():
 
     if args.workload == "decode":
         out = bench_decode(args)
+    elif args.workload == "copy":
+        out = bench_copy(args)
     else:
         w = {"long": synth.LONG_BF16, "extras": synth.EXTRAS_BF16, "causal_f32": synth.CAUSAL_F32}[args.workload]
         out = bench_prefill(args, w)

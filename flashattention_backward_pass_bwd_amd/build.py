@@ -23,7 +23,9 @@ LIB_PATH = os.path.join(HERE, "libfa_bwd.so")
 SOURCES = [
     "fa_preprocess.hip",
     "fa_dkdv.hip",
+    "fa_dkdv_bf16.hip",
     "fa_dq.hip",
+    "fa_dq_bf16.hip",
     "fa_decode.hip",
     "fa_debug.hip",
     "fa_api.cpp",

@@ -1,4 +1,4 @@
-// Key-block-outer pass: dK and dV without atomics (ferrotensor-backend
+// Key-block-outer pass, fp32 path (the bf16 path is fa_dkdv_bf16.hip): dK and dV without atomics (ferrotensor-backend
 // flash_attention_v2_backward.wgsl, flash_bwd_dk_dv; formulas from its header
 // comment).  For each key j of KV head kvh, summed over the query heads of the
 // GQA group and over every query i that sees it:
@@ -240,9 +240,7 @@ static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, c
 hipError_t launch_dkdv(const PrefillArgs& a, int dtype, int D, const void* Q, const void* K,
                        const void* V, const void* dO, const float* L, const float* delta, void* dK,
                        void* dV, hipStream_t st) {
-  if (dtype == kBF16)
-    return D == 64 ? launch_d<__bf16, 64>(a, Q, K, V, dO, L, delta, dK, dV, st)
-                   : launch_d<__bf16, 128>(a, Q, K, V, dO, L, delta, dK, dV, st);
+  if (dtype == kBF16) return launch_dkdv_bf16(a, D, Q, K, V, dO, L, delta, dK, dV, st);
   return D == 64 ? launch_d<float, 64>(a, Q, K, V, dO, L, delta, dK, dV, st)
                  : launch_d<float, 128>(a, Q, K, V, dO, L, delta, dK, dV, st);
 }

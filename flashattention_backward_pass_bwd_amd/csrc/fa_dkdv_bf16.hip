@@ -1,0 +1,286 @@
+// Key-block-outer dK/dV pass, bf16 storage, bf16 MFMA with fp32 accumulation
+// (ferrotensor-backend flash_attention_v2_backward.wgsl, flash_bwd_dk_dv and
+// its header formulas):
+//   dV_j = sum_h sum_i P_ij M_ij dO_i,  dK_j = scale * sum_h sum_i dS_ij Q_i,
+//   P_ij = exp(S_ij - L_i) on counted elements, dS_ij = P_ij (M_ij dO_i.V_j - Delta_i).
+//
+// Block: 4 waves own 128 consecutive keys of one (b, kvh); wave w owns keys
+// k0 + 32w .. +31 and keeps their K and V rows in registers as MFMA B operands
+// (v_mfma_f32_32x32x16_bf16), accumulating dK^T and dV^T (D x 32 fp32) in
+// registers.  The block walks every (query head of the group, 64-row query
+// tile) pair; Q and dO tiles are double-buffered in LDS (swizzled, see
+// fa_tiles.h): the next tile's global loads are issued before the current
+// tile's MFMAs and land in the other buffer afterwards, so one barrier per
+// tile suffices.  S = Q K^T and dP = dO V^T read row-major operands; the
+// transposed operands of dV^T += dO^T (P.M) and dK^T += Q^T dS come from the
+// same tiles through ds_read_b64_tr_b16.  P and dS stay in registers: the C
+// layout of S (one key per lane column) is the B layout of the second pair of
+// contractions.  For causal attention without a window, block i also takes
+// key block nkb-1-i, so every block carries the same amount of work.
+#include "fa_internal.h"
+#include "fa_tiles.h"
+
+namespace fa {
+
+template <int D, bool MASK, bool DROP>
+__global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const __bf16* __restrict__ Q,
+                                                           const __bf16* __restrict__ K,
+                                                           const __bf16* __restrict__ V,
+                                                           const __bf16* __restrict__ dO,
+                                                           const float* __restrict__ L,
+                                                           const float* __restrict__ Dl,
+                                                           __bf16* __restrict__ dK, __bf16* __restrict__ dV,
+                                                           int nkb, int paired) {
+  using M = Mma<__bf16>;
+  constexpr int BQ = 64;
+  constexpr int NCH = D / 8;                // 16-byte chunks per row
+  constexpr int KS = D / 16;                // k-blocks of the head_dim contraction
+  constexpr int DB = D / 32;                // 32-row blocks of dK^T / dV^T
+  constexpr int RPU = 256 / NCH;            // tile rows loaded per thread-sweep
+  constexpr int LPT = BQ / RPU;             // chunks per thread per tile per tensor
+  constexpr int TILE = BQ * D;
+
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 sdO[2][TILE];
+  __shared__ __attribute__((aligned(16))) float sL[2][BQ];
+  __shared__ __attribute__((aligned(16))) float sDel[2][BQ];
+  __shared__ uint32_t sRK[2][DROP ? BQ : 1];
+
+  const int nbh = a.B * a.Hkv;
+  const int wi = blockIdx.x / nbh;
+  const int bh = blockIdx.x % nbh;  // consecutive blocks cycle over (b, kvh): one XCD per KV head
+  const int b = bh / a.Hkv;
+  const int kvh = bh % a.Hkv;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int h2 = lane >> 5;
+  const int l32 = lane & 31;
+
+  // Tile-load assignment: thread -> (row lr + RPU*u, chunk lc).
+  const int lr = tid / NCH;
+  const int lc = tid % NCH;
+  const int st_off = tile_off<D>(lr, lc);  // + u*RPU*D for sweep u (swizzle depends on row%8 only)
+  // Per-lane LDS offsets of the row-major operand chunks and the transposed reads.
+  int rd_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) rd_off[ks] = tile_off<D>(l32, 2 * ks + h2);
+  int tr_off[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) tr_off[d] = tr_lane_off<D>(lane, d);
+
+  const int npass = paired ? 2 : 1;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int kb = pass == 0 ? wi : nkb - 1 - wi;
+    if (pass == 1 && kb <= wi) break;
+    const int k0 = kb * kDkdvKeysPerBlock;
+    const int kw0 = k0 + wave * kDkdvKeysPerWave;
+    const int jl = kw0 + l32;
+
+    bf16x8 kr[KS], vr[KS];
+    const int64_t koff = (int64_t)b * a.ksb + (int64_t)jl * a.kss + (int64_t)kvh * a.ksh;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      kr[s] = bf16x8{};
+      vr[s] = bf16x8{};
+      if (jl < a.Sk) {
+        kr[s] = *reinterpret_cast<const bf16x8*>(K + koff + 16 * s + 8 * h2);
+        vr[s] = *reinterpret_cast<const bf16x8*>(V + koff + 16 * s + 8 * h2);
+      }
+    }
+    f32x16 acck[DB], accv[DB];
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+      acck[d] = f32x16{};
+      accv[d] = f32x16{};
+    }
+
+    int qb, qe;
+    query_range(a, k0, min(k0 + kDkdvKeysPerBlock, a.Sk) - 1, qb, qe);
+    const int ntq = (qe - qb + BQ - 1) / BQ;
+    const int ntiles = ntq * a.group;
+
+    // Prefetch registers for the next tile.
+    bf16x8 pq[LPT], pg[LPT];
+    float pl = 0.f, pd = 0.f;
+    uint32_t prk = 0;
+    auto load_tile = [&](int it) {
+      const int g = it / ntq;
+      const int qt = qb + (it - g * ntq) * BQ;
+      const int h = kvh * a.group + g;
+#pragma unroll
+      for (int u = 0; u < LPT; ++u) {
+        const int i = qt + lr + RPU * u;
+        pq[u] = bf16x8{};
+        pg[u] = bf16x8{};
+        if (i < a.Sq) {
+          const int64_t off = (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh + 8 * lc;
+          pq[u] = *reinterpret_cast<const bf16x8*>(Q + off);
+          pg[u] = *reinterpret_cast<const bf16x8*>(dO + off);
+        }
+      }
+      if (tid < BQ) {
+        const int i = qt + tid;
+        const int64_t row = ((int64_t)b * a.Hq + h) * a.Sq + i;
+        const bool in = i < a.Sq;
+        pl = in ? L[row] * kLog2e : __builtin_inff();
+        pd = in ? Dl[row] : 0.f;
+        if constexpr (DROP) prk = drop_row_key(a, b, h, i);
+      }
+    };
+    auto store_tile = [&](int stage) {
+#pragma unroll
+      for (int u = 0; u < LPT; ++u) {
+        *reinterpret_cast<bf16x8*>(&sQ[stage][st_off + u * RPU * D]) = pq[u];
+        *reinterpret_cast<bf16x8*>(&sdO[stage][st_off + u * RPU * D]) = pg[u];
+      }
+      if (tid < BQ) {
+        sL[stage][tid] = pl;
+        sDel[stage][tid] = pd;
+        if constexpr (DROP) sRK[stage][tid] = prk;
+      }
+    };
+
+    if (ntiles > 0) {
+      load_tile(0);
+      store_tile(0);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < ntiles; ++it) {
+      const int stage = it & 1;
+      const bool has_next = it + 1 < ntiles;
+      if (has_next) load_tile(it + 1);
+
+      const int g = it / ntq;
+      const int qt = qb + (it - g * ntq) * BQ;
+      const int h = kvh * a.group + g;
+      if (!rect_none_visible(a, qt, qt + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1)) {
+        const bool full = !MASK && !DROP && rect_all_visible(a, qt, qt + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1);
+        const __bf16* tq = sQ[stage];
+        const __bf16* tg = sdO[stage];
+
+        f32x16 s[2], dp[2];
+        s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            M::run(s[m], lds_read_b128(tq + rd_off[ks] + 32 * m * D), kr[ks]);
+            M::run(dp[m], lds_read_b128(tg + rd_off[ks] + 32 * m * D), vr[ks]);
+          }
+        }
+
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int row0 = 32 * m + 8 * r4 + 4 * h2;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[stage][row0]);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[stage][row0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * r4 + e;
+              float p, dpv = dp[m][r];
+              if (full) {
+                p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[m][r], a.scale_log2, -l4[e]));
+              } else {
+                const int i = qt + row0 + e;
+                bool ok = visible(a, i, jl);
+                float x = __builtin_fmaf(s[m][r], a.scale_log2, -l4[e]);
+                if constexpr (MASK) {
+                  if (ok) {
+                    const float mv = mask_at(a, b, h, i, jl);
+                    ok = !(mv <= kMaskedSentinel);
+                    x = __builtin_fmaf(mv, kLog2e, x);
+                  }
+                }
+                p = ok ? __builtin_amdgcn_exp2f(x) : 0.f;
+              }
+              float pm = p;
+              if constexpr (DROP) {
+                const float mm = drop_keep(sRK[stage][row0 + e], jl, a.drop_thr) ? a.drop_inv : 0.f;
+                dpv *= mm;
+                pm = p * mm;
+              }
+              dp[m][r] = p * (dpv - d4[e]);
+              s[m][r] = pm;
+            }
+          }
+        }
+
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const bf16x8 pmc = M::from_acc(s[m], 8 * t);
+            const bf16x8 dsc = M::from_acc(dp[m], 8 * t);
+            const int rb = (32 * m + 16 * t) * D;
+#pragma unroll
+            for (int d = 0; d < DB; ++d) {
+              const bf16x8 ao = concat(lds_read_tr(tg + tr_off[d] + rb), lds_read_tr(tg + tr_off[d] + rb + 8 * D));
+              M::run(accv[d], ao, pmc);
+              const bf16x8 aq = concat(lds_read_tr(tq + tr_off[d] + rb), lds_read_tr(tq + tr_off[d] + rb + 8 * D));
+              M::run(acck[d], aq, dsc);
+            }
+          }
+        }
+      }
+
+      if (has_next) store_tile(stage ^ 1);
+      __syncthreads();
+    }
+
+    if (jl < a.Sk) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int dd = 32 * d + 8 * r4 + 4 * h2;
+          bf16x4 ok4, ov4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ok4[e] = (__bf16)(acck[d][4 * r4 + e] * a.scale);
+            ov4[e] = (__bf16)accv[d][4 * r4 + e];
+          }
+          *reinterpret_cast<bf16x4*>(dK + koff + dd) = ok4;
+          *reinterpret_cast<bf16x4*>(dV + koff + dd) = ov4;
+        }
+      }
+    }
+  }
+}
+
+template <int D, bool MASK, bool DROP>
+static hipError_t launch_t(const PrefillArgs& a, const void* Q, const void* K, const void* V, const void* dO,
+                           const float* L, const float* delta, void* dK, void* dV, hipStream_t st) {
+  const int nkb = (a.Sk + kDkdvKeysPerBlock - 1) / kDkdvKeysPerBlock;
+  const int paired = (a.causal && a.window == 0 && nkb > 1) ? 1 : 0;
+  const int nwi = paired ? (nkb + 1) / 2 : nkb;
+  const unsigned grid = (unsigned)(nwi * a.B * a.Hkv);
+  hipLaunchKernelGGL((dkdv_bf16_kernel<D, MASK, DROP>), dim3(grid), dim3(256), 0, st, a,
+                     static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
+                     static_cast<const __bf16*>(dO), L, delta, static_cast<__bf16*>(dK), static_cast<__bf16*>(dV),
+                     nkb, paired);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, const void* V, const void* dO,
+                           const float* L, const float* delta, void* dK, void* dV, hipStream_t st) {
+  const bool mask = a.mask != nullptr;
+  const bool drop = a.drop != 0;
+  if (mask && drop) return launch_t<D, true, true>(a, Q, K, V, dO, L, delta, dK, dV, st);
+  if (mask) return launch_t<D, true, false>(a, Q, K, V, dO, L, delta, dK, dV, st);
+  if (drop) return launch_t<D, false, true>(a, Q, K, V, dO, L, delta, dK, dV, st);
+  return launch_t<D, false, false>(a, Q, K, V, dO, L, delta, dK, dV, st);
+}
+
+hipError_t launch_dkdv_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V,
+                            const void* dO, const float* L, const float* delta, void* dK, void* dV,
+                            hipStream_t st) {
+  return D == 64 ? launch_d<64>(a, Q, K, V, dO, L, delta, dK, dV, st)
+                 : launch_d<128>(a, Q, K, V, dO, L, delta, dK, dV, st);
+}
+
+}  // namespace fa

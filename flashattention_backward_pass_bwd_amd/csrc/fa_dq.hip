@@ -1,4 +1,4 @@
-// Query-block-outer pass: dQ without atomics (rustytorch
+// Query-block-outer pass, fp32 path (the bf16 path is fa_dq_bf16.hip): dQ without atomics (rustytorch
 // flash_attention_backward_dq.metal kernel; ferrotensor-backend
 // flash_attention_v2_backward.wgsl, flash_bwd_dq second sweep, with L given):
 //   dQ_i = scale * sum_j dS_ij K_j,  dS_ij = P_ij (M_ij dO_i.V_j - Delta_i),
@@ -211,9 +211,7 @@ static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, c
 hipError_t launch_dq(const PrefillArgs& a, int dtype, int D, const void* Q, const void* K,
                      const void* V, const void* dO, const float* L, const float* delta, void* dQ,
                      hipStream_t st) {
-  if (dtype == kBF16)
-    return D == 64 ? launch_d<__bf16, 64>(a, Q, K, V, dO, L, delta, dQ, st)
-                   : launch_d<__bf16, 128>(a, Q, K, V, dO, L, delta, dQ, st);
+  if (dtype == kBF16) return launch_dq_bf16(a, D, Q, K, V, dO, L, delta, dQ, st);
   return D == 64 ? launch_d<float, 64>(a, Q, K, V, dO, L, delta, dQ, st)
                  : launch_d<float, 128>(a, Q, K, V, dO, L, delta, dQ, st);
 }

@@ -1,0 +1,235 @@
+// Query-block-outer dQ pass, bf16 storage, bf16 MFMA with fp32 accumulation
+// (rustytorch flash_attention_backward_dq.metal kernel; ferrotensor-backend
+// flash_attention_v2_backward.wgsl, flash_bwd_dq second sweep, L supplied):
+//   dQ_i = scale * sum_j dS_ij K_j,  dS_ij = P_ij (M_ij dO_i.V_j - Delta_i).
+//
+// Block: 4 waves own 128 consecutive query rows of one (b, h); wave w keeps
+// its 32 rows of Q and dO in registers as MFMA B operands and accumulates
+// dQ^T (D x 32 fp32).  K and V tiles of 64 keys are double-buffered in LDS
+// (swizzled, see fa_tiles.h) with the next tile's loads in flight during the
+// current tile's MFMAs.  S^T = K Q^T and dP^T = V dO^T read row-major
+// operands; dQ^T += K^T dS^T reads K transposed through ds_read_b64_tr_b16.
+// S^T has one query per lane column, so L_i and Delta_i are per-lane scalars
+// and dS^T is already the B operand of the last contraction.  Blocks of the
+// query heads sharing a KV head are dealt to one XCD; for causal attention
+// without a window, block i also takes query block nqb-1-i.
+#include "fa_internal.h"
+#include "fa_tiles.h"
+
+namespace fa {
+
+template <int D, bool MASK, bool DROP>
+__global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __bf16* __restrict__ Q,
+                                                         const __bf16* __restrict__ K,
+                                                         const __bf16* __restrict__ V,
+                                                         const __bf16* __restrict__ dO,
+                                                         const float* __restrict__ L,
+                                                         const float* __restrict__ Dl,
+                                                         __bf16* __restrict__ dQ, int nqb, int paired) {
+  using M = Mma<__bf16>;
+  constexpr int BK = 64;
+  constexpr int NCH = D / 8;
+  constexpr int KS = D / 16;
+  constexpr int DB = D / 32;
+  constexpr int RPU = 256 / NCH;
+  constexpr int LPT = BK / RPU;
+  constexpr int TILE = BK * D;
+
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2][TILE];
+
+  const int nbh = a.B * a.Hq;
+  const int wi = blockIdx.x / nbh;
+  const int bhi = blockIdx.x % nbh;
+  const int kvh = bhi % a.Hkv;  // KV head varies fastest: its query heads share an XCD
+  const int rest = bhi / a.Hkv;
+  const int gi = rest % a.group;
+  const int b = rest / a.group;
+  const int h = kvh * a.group + gi;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int h2 = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int lr = tid / NCH;
+  const int lc = tid % NCH;
+  const int st_off = tile_off<D>(lr, lc);
+  int rd_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) rd_off[ks] = tile_off<D>(l32, 2 * ks + h2);
+  int tr_off[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) tr_off[d] = tr_lane_off<D>(lane, d);
+
+  const int npass = paired ? 2 : 1;
+  for (int pass = 0; pass < npass; ++pass) {
+    // Without pairing, later blocks take earlier query blocks (longest causal work first).
+    const int qbi = paired ? (pass == 0 ? wi : nqb - 1 - wi) : nqb - 1 - wi;
+    if (pass == 1 && qbi <= wi) break;
+    const int q0 = qbi * kDqRowsPerBlock;
+    const int qw0 = q0 + wave * kDqRowsPerWave;
+    const int il = qw0 + l32;
+
+    bf16x8 qr[KS], gr[KS];
+    const int64_t qoff = (int64_t)b * a.qsb + (int64_t)il * a.qss + (int64_t)h * a.qsh;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qr[s] = bf16x8{};
+      gr[s] = bf16x8{};
+      if (il < a.Sq) {
+        qr[s] = *reinterpret_cast<const bf16x8*>(Q + qoff + 16 * s + 8 * h2);
+        gr[s] = *reinterpret_cast<const bf16x8*>(dO + qoff + 16 * s + 8 * h2);
+      }
+    }
+    const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq + il;
+    const float l2 = il < a.Sq ? L[lrow] * kLog2e : __builtin_inff();
+    const float del = il < a.Sq ? Dl[lrow] : 0.f;
+    uint32_t rk = 0;
+    if constexpr (DROP) rk = drop_row_key(a, b, h, il);
+
+    f32x16 accq[DB];
+#pragma unroll
+    for (int d = 0; d < DB; ++d) accq[d] = f32x16{};
+
+    int kb, ke;
+    key_range(a, q0, min(q0 + kDqRowsPerBlock, a.Sq) - 1, kb, ke);
+    const int ntiles = (ke - kb + BK - 1) / BK;
+
+    bf16x8 pk[LPT], pv[LPT];
+    auto load_tile = [&](int it) {
+      const int kt = kb + it * BK;
+#pragma unroll
+      for (int u = 0; u < LPT; ++u) {
+        const int j = kt + lr + RPU * u;
+        pk[u] = bf16x8{};
+        pv[u] = bf16x8{};
+        if (j < a.Sk) {
+          const int64_t off = (int64_t)b * a.ksb + (int64_t)j * a.kss + (int64_t)kvh * a.ksh + 8 * lc;
+          pk[u] = *reinterpret_cast<const bf16x8*>(K + off);
+          pv[u] = *reinterpret_cast<const bf16x8*>(V + off);
+        }
+      }
+    };
+    auto store_tile = [&](int stage) {
+#pragma unroll
+      for (int u = 0; u < LPT; ++u) {
+        *reinterpret_cast<bf16x8*>(&sK[stage][st_off + u * RPU * D]) = pk[u];
+        *reinterpret_cast<bf16x8*>(&sV[stage][st_off + u * RPU * D]) = pv[u];
+      }
+    };
+
+    if (ntiles > 0) {
+      load_tile(0);
+      store_tile(0);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < ntiles; ++it) {
+      const int stage = it & 1;
+      const bool has_next = it + 1 < ntiles;
+      if (has_next) load_tile(it + 1);
+      const int kt = kb + it * BK;
+      if (!rect_none_visible(a, qw0, qw0 + kDqRowsPerWave - 1, kt, kt + BK - 1)) {
+        const bool full = !MASK && !DROP && rect_all_visible(a, qw0, qw0 + kDqRowsPerWave - 1, kt, kt + BK - 1);
+        const __bf16* tk = sK[stage];
+        const __bf16* tv = sV[stage];
+        f32x16 st[2], dpt[2];
+        st[0] = st[1] = dpt[0] = dpt[1] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            M::run(st[m], lds_read_b128(tk + rd_off[ks] + 32 * m * D), qr[ks]);
+            M::run(dpt[m], lds_read_b128(tv + rd_off[ks] + 32 * m * D), gr[ks]);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float p, dpv = dpt[m][r];
+            if (full) {
+              p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[m][r], a.scale_log2, -l2));
+            } else {
+              const int j = kt + 32 * m + 8 * (r / 4) + 4 * h2 + (r % 4);
+              bool ok = visible(a, il, j);
+              float x = __builtin_fmaf(st[m][r], a.scale_log2, -l2);
+              if constexpr (MASK) {
+                if (ok) {
+                  const float mv = mask_at(a, b, h, il, j);
+                  ok = !(mv <= kMaskedSentinel);
+                  x = __builtin_fmaf(mv, kLog2e, x);
+                }
+              }
+              p = ok ? __builtin_amdgcn_exp2f(x) : 0.f;
+              if constexpr (DROP) dpv *= drop_keep(rk, j, a.drop_thr) ? a.drop_inv : 0.f;
+            }
+            dpt[m][r] = p * (dpv - del);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const bf16x8 dsc = M::from_acc(dpt[m], 8 * t);
+            const int rb = (32 * m + 16 * t) * D;
+#pragma unroll
+            for (int d = 0; d < DB; ++d) {
+              const bf16x8 ak = concat(lds_read_tr(tk + tr_off[d] + rb), lds_read_tr(tk + tr_off[d] + rb + 8 * D));
+              M::run(accq[d], ak, dsc);
+            }
+          }
+        }
+      }
+      if (has_next) store_tile(stage ^ 1);
+      __syncthreads();
+    }
+
+    if (il < a.Sq) {
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int dd = 32 * d + 8 * r4 + 4 * h2;
+          bf16x4 o4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(accq[d][4 * r4 + e] * a.scale);
+          *reinterpret_cast<bf16x4*>(dQ + qoff + dd) = o4;
+        }
+      }
+    }
+  }
+}
+
+template <int D, bool MASK, bool DROP>
+static hipError_t launch_t(const PrefillArgs& a, const void* Q, const void* K, const void* V, const void* dO,
+                           const float* L, const float* delta, void* dQ, hipStream_t st) {
+  const int nqb = (a.Sq + kDqRowsPerBlock - 1) / kDqRowsPerBlock;
+  const int paired = (a.causal && a.window == 0 && nqb > 1) ? 1 : 0;
+  const int nwi = paired ? (nqb + 1) / 2 : nqb;
+  const unsigned grid = (unsigned)(nwi * a.B * a.Hq);
+  hipLaunchKernelGGL((dq_bf16_kernel<D, MASK, DROP>), dim3(grid), dim3(256), 0, st, a,
+                     static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
+                     static_cast<const __bf16*>(dO), L, delta, static_cast<__bf16*>(dQ), nqb, paired);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, const void* V, const void* dO,
+                           const float* L, const float* delta, void* dQ, hipStream_t st) {
+  const bool mask = a.mask != nullptr;
+  const bool drop = a.drop != 0;
+  if (mask && drop) return launch_t<D, true, true>(a, Q, K, V, dO, L, delta, dQ, st);
+  if (mask) return launch_t<D, true, false>(a, Q, K, V, dO, L, delta, dQ, st);
+  if (drop) return launch_t<D, false, true>(a, Q, K, V, dO, L, delta, dQ, st);
+  return launch_t<D, false, false>(a, Q, K, V, dO, L, delta, dQ, st);
+}
+
+hipError_t launch_dq_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V,
+                          const void* dO, const float* L, const float* delta, void* dQ, hipStream_t st) {
+  return D == 64 ? launch_d<64>(a, Q, K, V, dO, L, delta, dQ, st) : launch_d<128>(a, Q, K, V, dO, L, delta, dQ, st);
+}
+
+}  // namespace fa

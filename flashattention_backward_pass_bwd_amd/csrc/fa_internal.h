@@ -25,6 +25,11 @@ hipError_t launch_preprocess(const PrefillArgs& a, int dtype, int D, const void*
 hipError_t launch_dkdv(const PrefillArgs& a, int dtype, int D, const void* Q, const void* K,
                        const void* V, const void* dO, const float* L, const float* delta, void* dK,
                        void* dV, hipStream_t st);
+hipError_t launch_dkdv_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V,
+                            const void* dO, const float* L, const float* delta, void* dK, void* dV,
+                            hipStream_t st);
+hipError_t launch_dq_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V,
+                          const void* dO, const float* L, const float* delta, void* dQ, hipStream_t st);
 hipError_t launch_dq(const PrefillArgs& a, int dtype, int D, const void* Q, const void* K,
                      const void* V, const void* dO, const float* L, const float* delta, void* dQ,
                      hipStream_t st);
