@@ -33,6 +33,14 @@ SOURCES = [
 
 ARCH = "gfx950"
 
+# The MFMA tile kernels: schedule for instruction-level parallelism (LDS reads
+# issued ahead of their MFMAs, VALU interleaved with MFMAs) rather than for
+# minimum register pressure -- they run one wave per SIMD by design.
+EXTRA_FLAGS = {
+    "fa_dkdv_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "fa_dq_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
 COMMON_FLAGS = [
     "-O3",
     "-std=c++17",
@@ -56,7 +64,7 @@ def _hipcc() -> str:
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [_hipcc(), *COMMON_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -67,6 +67,28 @@ __device__ __forceinline__ bool visible(const PrefillArgs& a, int i, int j) {
   return true;
 }
 
+// The same geometric rule as two uniform bounds on d = j - i: an in-range
+// element is visible iff dlo < d < dhi (causal: d <= offset; window:
+// |d - offset| < window).  Lets tile kernels test visibility branch-free.
+struct DiagBounds {
+  int dlo, dhi;
+};
+
+__device__ __forceinline__ DiagBounds diag_bounds(const PrefillArgs& a) {
+  DiagBounds db{-(1 << 30) - 1, (1 << 30) + 1};
+  if (a.causal) db.dhi = a.offset + 1;
+  if (a.window > 0) {
+    db.dlo = a.offset - a.window;
+    if (!a.causal) db.dhi = a.offset + a.window;
+  }
+  return db;
+}
+
+// Declares AGPR use so the compiler selects the AGPR form of MFMA (accumulators
+// and long-lived operands in the accumulation registers) instead of spilling
+// VGPR-form accumulators into AGPRs.
+__device__ __forceinline__ void use_agpr_form() { asm volatile("" ::: "a255"); }
+
 __device__ __forceinline__ float mask_at(const PrefillArgs& a, int b, int h, int i, int j) {
   return a.mask[(int64_t)b * a.msb + (int64_t)h * a.msh + (int64_t)i * a.msq + (int64_t)j * a.msk];
 }

@@ -7,16 +7,20 @@
 // Block: 4 waves own 128 consecutive keys of one (b, kvh); wave w owns keys
 // k0 + 32w .. +31 and keeps their K and V rows in registers as MFMA B operands
 // (v_mfma_f32_32x32x16_bf16), accumulating dK^T and dV^T (D x 32 fp32) in
-// registers.  The block walks every (query head of the group, 64-row query
-// tile) pair; Q and dO tiles are double-buffered in LDS (swizzled, see
-// fa_tiles.h): the next tile's global loads are issued before the current
-// tile's MFMAs and land in the other buffer afterwards, so one barrier per
-// tile suffices.  S = Q K^T and dP = dO V^T read row-major operands; the
-// transposed operands of dV^T += dO^T (P.M) and dK^T += Q^T dS come from the
-// same tiles through ds_read_b64_tr_b16.  P and dS stay in registers: the C
-// layout of S (one key per lane column) is the B layout of the second pair of
-// contractions.  For causal attention without a window, block i also takes
-// key block nkb-1-i, so every block carries the same amount of work.
+// accumulation registers.  The block walks every (query head of the group,
+// 64-row query tile) pair; Q and dO tiles are double-buffered in LDS
+// (swizzled, see fa_tiles.h): the next tile's global loads are issued before
+// the current tile's MFMAs and land in the other buffer afterwards, so one
+// barrier per tile suffices.  S = Q K^T and dP = dO V^T read row-major
+// operands; the transposed operands of dV^T += dO^T (P.M) and dK^T += Q^T dS
+// come from the same tiles through ds_read_b64_tr_b16.  P and dS never leave
+// registers: the C layout of S (one key per lane column) is the B layout of
+// the second pair of contractions.  A tile is processed as two 32-row halves
+// so that the exp/dS arithmetic of one half can overlap the MFMAs of the
+// other.  For causal attention without a window, block i also takes key block
+// nkb-1-i, so every block carries the same amount of work.
+#include <type_traits>
+
 #include "fa_internal.h"
 #include "fa_tiles.h"
 
@@ -52,10 +56,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
   const int b = bh / a.Hkv;
   const int kvh = bh % a.Hkv;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int h2 = lane >> 5;
   const int l32 = lane & 31;
+  use_agpr_form();
+  const DiagBounds vb = diag_bounds(a);
 
   // Tile-load assignment: thread -> (row lr + RPU*u, chunk lc).
   const int lr = tid / NCH;
@@ -147,88 +153,134 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     }
     __syncthreads();
 
-    for (int it = 0; it < ntiles; ++it) {
+    // One step: stage tile it+1 while computing tile it.  KIND 0 = no element
+    // of the tile is visible to this wave, 1 = boundary tile (per-element
+    // predicate), 2 = interior tile (every element counted).  Each kind runs
+    // in a loop of its own, so no loop body branches around the MFMAs.
+    auto step = [&](auto kind_c, int it) {
+      constexpr int KIND = decltype(kind_c)::value;
       const int stage = it & 1;
       const bool has_next = it + 1 < ntiles;
       if (has_next) load_tile(it + 1);
-
+      if constexpr (KIND != 0) {
       const int g = it / ntq;
       const int qt = qb + (it - g * ntq) * BQ;
       const int h = kvh * a.group + g;
-      if (!rect_none_visible(a, qt, qt + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1)) {
-        const bool full = !MASK && !DROP && rect_all_visible(a, qt, qt + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1);
-        const __bf16* tq = sQ[stage];
-        const __bf16* tg = sdO[stage];
+      const __bf16* tq = sQ[stage];
+      const __bf16* tg = sdO[stage];
+      const float* tl = sL[stage];
+      const float* td = sDel[stage];
 
-        f32x16 s[2], dp[2];
-        s[0] = s[1] = dp[0] = dp[1] = f32x16{};
+      // S (m-th 32-row half) = Q K^T and dP = dO V^T.
+      auto mma_sdp = [&](int m, f32x16& s, f32x16& dp) {
+        s = f32x16{};
+        dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            M::run(s[m], lds_read_b128(tq + rd_off[ks] + 32 * m * D), kr[ks]);
-            M::run(dp[m], lds_read_b128(tg + rd_off[ks] + 32 * m * D), vr[ks]);
-          }
+          M::run(s, lds_read_b128(tq + rd_off[ks] + 32 * m * D), kr[ks]);
+          M::run(dp, lds_read_b128(tg + rd_off[ks] + 32 * m * D), vr[ks]);
         }
-
+      };
+      // P, dropout and dS for one half, packed into the bf16 B operands of the next contractions.
+      auto elementwise = [&](auto full_c, int m, const f32x16& s, const f32x16& dp, bf16x8 (&pmc)[2],
+                             bf16x8 (&dsc)[2]) {
+        constexpr bool FULL = decltype(full_c)::value;
+        const int dl0 = jl - qt;  // d = j - i = dl0 - row
+        const int rlim = a.Sq - qt;
+        const bool jin = jl < a.Sk;
+        const int jc = min(jl, a.Sk - 1);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int row0 = 32 * m + 8 * r4 + 4 * h2;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(tl + row0);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(td + row0);
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int row0 = 32 * m + 8 * r4 + 4 * h2;
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[stage][row0]);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[stage][row0]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * r4 + e;
-              float p, dpv = dp[m][r];
-              if (full) {
-                p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[m][r], a.scale_log2, -l4[e]));
-              } else {
-                const int i = qt + row0 + e;
-                bool ok = visible(a, i, jl);
-                float x = __builtin_fmaf(s[m][r], a.scale_log2, -l4[e]);
-                if constexpr (MASK) {
-                  if (ok) {
-                    const float mv = mask_at(a, b, h, i, jl);
-                    ok = !(mv <= kMaskedSentinel);
-                    x = __builtin_fmaf(mv, kLog2e, x);
-                  }
-                }
-                p = ok ? __builtin_amdgcn_exp2f(x) : 0.f;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            float x = __builtin_fmaf(s[r], a.scale_log2, -l4[e]);
+            if constexpr (!FULL) {
+              const int row = row0 + e;
+              const int dd = dl0 - row;
+              bool ok = jin && row < rlim && dd > vb.dlo && dd < vb.dhi;
+              if constexpr (MASK) {
+                // clamped indices keep the load in bounds; ok discards out-of-range elements
+                const float mv = mask_at(a, b, h, min(qt + row, a.Sq - 1), jc);
+                ok = ok && !(mv <= kMaskedSentinel);
+                x = __builtin_fmaf(mv, kLog2e, x);
               }
-              float pm = p;
-              if constexpr (DROP) {
-                const float mm = drop_keep(sRK[stage][row0 + e], jl, a.drop_thr) ? a.drop_inv : 0.f;
-                dpv *= mm;
-                pm = p * mm;
-              }
-              dp[m][r] = p * (dpv - d4[e]);
-              s[m][r] = pm;
+              x = ok ? x : -__builtin_inff();
             }
+            const float p = __builtin_amdgcn_exp2f(x);
+            float dpv = dp[r];
+            float pm = p;
+            if constexpr (DROP) {
+              const float mm = drop_keep(sRK[stage][row0 + e], jl, a.drop_thr) ? a.drop_inv : 0.f;
+              dpv *= mm;
+              pm = p * mm;
+            }
+            pmc[r >> 3][r & 7] = (__bf16)pm;
+            dsc[r >> 3][r & 7] = (__bf16)(p * (dpv - d4[e]));
           }
         }
+      };
+      // dV^T += dO^T (P.M) and dK^T += Q^T dS over the m-th half's 32 queries.
+      auto mma_dkdv = [&](int m, const bf16x8 (&pmc)[2], const bf16x8 (&dsc)[2]) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int rb = (32 * m + 16 * t) * D;
+#pragma unroll
+          for (int d = 0; d < DB; ++d) {
+            const bf16x8 ao = concat(lds_read_tr(tg + tr_off[d] + rb), lds_read_tr(tg + tr_off[d] + rb + 8 * D));
+            M::run(accv[d], ao, pmc[t]);
+            const bf16x8 aq = concat(lds_read_tr(tq + tr_off[d] + rb), lds_read_tr(tq + tr_off[d] + rb + 8 * D));
+            M::run(acck[d], aq, dsc[t]);
+          }
+        }
+      };
+      auto tile = [&](auto full_c) {
+        f32x16 s0, dp0, s1, dp1;
+        bf16x8 pm0[2], ds0[2], pm1[2], ds1[2];
+        mma_sdp(0, s0, dp0);
+        mma_sdp(1, s1, dp1);
+        elementwise(full_c, 0, s0, dp0, pm0, ds0);
+        mma_dkdv(0, pm0, ds0);
+        elementwise(full_c, 1, s1, dp1, pm1, ds1);
+        mma_dkdv(1, pm1, ds1);
+      };
 
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const bf16x8 pmc = M::from_acc(s[m], 8 * t);
-            const bf16x8 dsc = M::from_acc(dp[m], 8 * t);
-            const int rb = (32 * m + 16 * t) * D;
-#pragma unroll
-            for (int d = 0; d < DB; ++d) {
-              const bf16x8 ao = concat(lds_read_tr(tg + tr_off[d] + rb), lds_read_tr(tg + tr_off[d] + rb + 8 * D));
-              M::run(accv[d], ao, pmc);
-              const bf16x8 aq = concat(lds_read_tr(tq + tr_off[d] + rb), lds_read_tr(tq + tr_off[d] + rb + 8 * D));
-              M::run(acck[d], aq, dsc);
-            }
-          }
-        }
+      tile(std::integral_constant<bool, KIND == 2>{});
       }
-
       if (has_next) store_tile(stage ^ 1);
       __syncthreads();
+    };
+
+    const std::integral_constant<int, 0> kSkip;
+    const std::integral_constant<int, 1> kEdge;
+    const std::integral_constant<int, 2> kInner;
+    for (int g = 0; g < a.group; ++g) {
+      // This wave's tiles of head g, in order: [0,v0) invisible, [v0,f0) boundary,
+      // [f0,f1) interior, [f1,v1) boundary, [v1,ntq) invisible (the visible key
+      // interval moves monotonically with the query row, so the classes are contiguous).
+      auto none = [&](int t) { return rect_none_visible(a, qb + t * BQ, qb + t * BQ + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1); };
+      auto all = [&](int t) { return rect_all_visible(a, qb + t * BQ, qb + t * BQ + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1); };
+      int v0 = 0;
+      while (v0 < ntq && none(v0)) ++v0;
+      int v1 = v0;
+      while (v1 < ntq && !none(v1)) ++v1;
+      int f0 = v1, f1 = v1;
+      if constexpr (!MASK && !DROP) {
+        f0 = v0;
+        while (f0 < v1 && !all(f0)) ++f0;
+        f1 = f0;
+        while (f1 < v1 && all(f1)) ++f1;
+      }
+      const int base = g * ntq;
+      int t = 0;
+      for (; t < v0; ++t) step(kSkip, base + t);
+      for (; t < f0; ++t) step(kEdge, base + t);
+      for (; t < f1; ++t) step(kInner, base + t);
+      for (; t < v1; ++t) step(kEdge, base + t);
+      for (; t < ntq; ++t) step(kSkip, base + t);
     }
 
     if (jl < a.Sk) {

@@ -13,6 +13,8 @@
 // and dS^T is already the B operand of the last contraction.  Blocks of the
 // query heads sharing a KV head are dealt to one XCD; for causal attention
 // without a window, block i also takes query block nqb-1-i.
+#include <type_traits>
+
 #include "fa_internal.h"
 #include "fa_tiles.h"
 
@@ -48,10 +50,12 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
   const int h = kvh * a.group + gi;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int h2 = lane >> 5;
   const int l32 = lane & 31;
+  use_agpr_form();
+  const DiagBounds vb = diag_bounds(a);
 
   const int lr = tid / NCH;
   const int lc = tid % NCH;
@@ -126,66 +130,103 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
     }
     __syncthreads();
 
-    for (int it = 0; it < ntiles; ++it) {
+    // One step: stage tile it+1 while computing tile it.  KIND 0 = no element
+    // visible to this wave, 1 = boundary tile (per-element predicate),
+    // 2 = interior tile; each kind runs in a loop of its own.
+    auto step = [&](auto kind_c, int it) {
+      constexpr int KIND = decltype(kind_c)::value;
       const int stage = it & 1;
       const bool has_next = it + 1 < ntiles;
       if (has_next) load_tile(it + 1);
-      const int kt = kb + it * BK;
-      if (!rect_none_visible(a, qw0, qw0 + kDqRowsPerWave - 1, kt, kt + BK - 1)) {
-        const bool full = !MASK && !DROP && rect_all_visible(a, qw0, qw0 + kDqRowsPerWave - 1, kt, kt + BK - 1);
+      if constexpr (KIND != 0) {
+        const int kt = kb + it * BK;
         const __bf16* tk = sK[stage];
         const __bf16* tv = sV[stage];
-        f32x16 st[2], dpt[2];
-        st[0] = st[1] = dpt[0] = dpt[1] = f32x16{};
+        // S^T (m-th 32-key half) = K Q^T and dP^T = V dO^T.
+        auto mma_sdp = [&](int m, f32x16& s, f32x16& dp) {
+          s = f32x16{};
+          dp = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            M::run(st[m], lds_read_b128(tk + rd_off[ks] + 32 * m * D), qr[ks]);
-            M::run(dpt[m], lds_read_b128(tv + rd_off[ks] + 32 * m * D), gr[ks]);
+          for (int ks = 0; ks < KS; ++ks) {
+            M::run(s, lds_read_b128(tk + rd_off[ks] + 32 * m * D), qr[ks]);
+            M::run(dp, lds_read_b128(tv + rd_off[ks] + 32 * m * D), gr[ks]);
           }
-        }
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        };
+        // P, dropout and dS for one half, packed into the bf16 B operands of dQ^T += K^T dS^T.
+        auto elementwise = [&](int m, const f32x16& s, const f32x16& dp, bf16x8 (&dsc)[2]) {
+          const int dl0 = kt - il;  // d = j - i = dl0 + row
+          const int rlim = a.Sk - kt;
+          const bool iin = il < a.Sq;
+          const int ic = min(il, a.Sq - 1);
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            float p, dpv = dpt[m][r];
-            if (full) {
-              p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[m][r], a.scale_log2, -l2));
-            } else {
-              const int j = kt + 32 * m + 8 * (r / 4) + 4 * h2 + (r % 4);
-              bool ok = visible(a, il, j);
-              float x = __builtin_fmaf(st[m][r], a.scale_log2, -l2);
+            float x = __builtin_fmaf(s[r], a.scale_log2, -l2);
+            float dpv = dp[r];
+            if constexpr (KIND == 1) {
+              const int row = 32 * m + 8 * (r / 4) + 4 * h2 + (r % 4);
+              const int dd = dl0 + row;
+              bool ok = iin && row < rlim && dd > vb.dlo && dd < vb.dhi;
               if constexpr (MASK) {
-                if (ok) {
-                  const float mv = mask_at(a, b, h, il, j);
-                  ok = !(mv <= kMaskedSentinel);
-                  x = __builtin_fmaf(mv, kLog2e, x);
-                }
+                // clamped indices keep the load in bounds; ok discards out-of-range elements
+                const float mv = mask_at(a, b, h, ic, min(kt + row, a.Sk - 1));
+                ok = ok && !(mv <= kMaskedSentinel);
+                x = __builtin_fmaf(mv, kLog2e, x);
               }
-              p = ok ? __builtin_amdgcn_exp2f(x) : 0.f;
-              if constexpr (DROP) dpv *= drop_keep(rk, j, a.drop_thr) ? a.drop_inv : 0.f;
+              x = ok ? x : -__builtin_inff();
+              if constexpr (DROP) dpv *= drop_keep(rk, kt + row, a.drop_thr) ? a.drop_inv : 0.f;
             }
-            dpt[m][r] = p * (dpv - del);
+            const float p = __builtin_amdgcn_exp2f(x);
+            dsc[r >> 3][r & 7] = (__bf16)(p * (dpv - del));
           }
-        }
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        };
+        auto mma_dq = [&](int m, const bf16x8 (&dsc)[2]) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
-            const bf16x8 dsc = M::from_acc(dpt[m], 8 * t);
             const int rb = (32 * m + 16 * t) * D;
 #pragma unroll
             for (int d = 0; d < DB; ++d) {
               const bf16x8 ak = concat(lds_read_tr(tk + tr_off[d] + rb), lds_read_tr(tk + tr_off[d] + rb + 8 * D));
-              M::run(accq[d], ak, dsc);
+              M::run(accq[d], ak, dsc[t]);
             }
           }
-        }
+        };
+        f32x16 s0, dp0, s1, dp1;
+        bf16x8 ds0[2], ds1[2];
+        mma_sdp(0, s0, dp0);
+        mma_sdp(1, s1, dp1);
+        elementwise(0, s0, dp0, ds0);
+        mma_dq(0, ds0);
+        elementwise(1, s1, dp1, ds1);
+        mma_dq(1, ds1);
       }
       if (has_next) store_tile(stage ^ 1);
       __syncthreads();
+    };
+
+    // This wave's key tiles in order: [0,v0) invisible, [v0,f0) boundary, [f0,f1)
+    // interior, [f1,v1) boundary, [v1,ntiles) invisible.
+    auto none = [&](int t) { return rect_none_visible(a, qw0, qw0 + kDqRowsPerWave - 1, kb + t * BK, kb + t * BK + BK - 1); };
+    auto all = [&](int t) { return rect_all_visible(a, qw0, qw0 + kDqRowsPerWave - 1, kb + t * BK, kb + t * BK + BK - 1); };
+    int v0 = 0;
+    while (v0 < ntiles && none(v0)) ++v0;
+    int v1 = v0;
+    while (v1 < ntiles && !none(v1)) ++v1;
+    int f0 = v1, f1 = v1;
+    if constexpr (!MASK && !DROP) {
+      f0 = v0;
+      while (f0 < v1 && !all(f0)) ++f0;
+      f1 = f0;
+      while (f1 < v1 && all(f1)) ++f1;
     }
+    const std::integral_constant<int, 0> kSkip;
+    const std::integral_constant<int, 1> kEdge;
+    const std::integral_constant<int, 2> kInner;
+    int t = 0;
+    for (; t < v0; ++t) step(kSkip, t);
+    for (; t < f0; ++t) step(kEdge, t);
+    for (; t < f1; ++t) step(kInner, t);
+    for (; t < v1; ++t) step(kEdge, t);
+    for (; t < ntiles; ++t) step(kSkip, t);
 
     if (il < a.Sq) {
 #pragma unroll
