@@ -8,10 +8,11 @@
 // k0 + 32w .. +31 and keeps their K and V rows in registers as MFMA B operands
 // (v_mfma_f32_32x32x16_bf16), accumulating dK^T and dV^T (D x 32 fp32) in
 // accumulation registers.  The block walks every (query head of the group,
-// 64-row query tile) pair; Q and dO tiles are double-buffered in LDS
-// (swizzled, see fa_tiles.h): the next tile's global loads are issued before
-// the current tile's MFMAs and land in the other buffer afterwards, so one
-// barrier per tile suffices.  S = Q K^T and dP = dO V^T read row-major
+// 64-row query tile) pair.  Q and dO tiles live in a 3-stage LDS ring
+// (swizzled, see fa_tiles.h) filled by direct global->LDS copies issued two
+// tiles ahead, so their latency hides behind two tiles of MFMA work and the
+// copies need no registers; L and Delta (64 floats each per tile) take the
+// register path.  One fence-free barrier per tile.  S = Q K^T and dP = dO V^T read row-major
 // operands; the transposed operands of dV^T += dO^T (P.M) and dK^T += Q^T dS
 // come from the same tiles through ds_read_b64_tr_b16.  P and dS never leave
 // registers: the C layout of S (one key per lane column) is the B layout of
@@ -40,15 +41,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
   constexpr int NCH = D / 8;                // 16-byte chunks per row
   constexpr int KS = D / 16;                // k-blocks of the head_dim contraction
   constexpr int DB = D / 32;                // 32-row blocks of dK^T / dV^T
-  constexpr int RPU = 256 / NCH;            // tile rows loaded per thread-sweep
-  constexpr int LPT = BQ / RPU;             // chunks per thread per tile per tensor
+  constexpr int NST = 3;                    // LDS ring stages
+  constexpr int RPI = 1024 / (2 * D);       // tile rows per 1 KB global->LDS copy (64 lanes x 16 B)
+  constexpr int NIW = BQ / RPI / 4;         // copies per wave per tile per tensor
   constexpr int TILE = BQ * D;
 
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[2][TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 sdO[2][TILE];
-  __shared__ __attribute__((aligned(16))) float sL[2][BQ];
-  __shared__ __attribute__((aligned(16))) float sDel[2][BQ];
-  __shared__ uint32_t sRK[2][DROP ? BQ : 1];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[NST][TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 sdO[NST][TILE];
+  __shared__ __attribute__((aligned(16))) float sL[NST][BQ];
+  __shared__ __attribute__((aligned(16))) float sDel[NST][BQ];
+  __shared__ uint32_t sRK[NST][DROP ? BQ : 1];
 
   const int nbh = a.B * a.Hkv;
   const int wi = blockIdx.x / nbh;
@@ -63,17 +65,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
   use_agpr_form();
   const DiagBounds vb = diag_bounds(a);
 
-  // Tile-load assignment: thread -> (row lr + RPU*u, chunk lc).
-  const int lr = tid / NCH;
-  const int lc = tid % NCH;
-  const int st_off = tile_off<D>(lr, lc);  // + u*RPU*D for sweep u (swizzle depends on row%8 only)
+  // Copy u of this wave fills rows (wave*NIW + u)*RPI + lane/NCH; lane l lands in
+  // physical chunk l%NCH, so it fetches the logical chunk stored there.
+  const int cp_row = lane / NCH;
+  const int cp_pc = lane % NCH;
   // Per-lane LDS offsets of the row-major operand chunks and the transposed reads.
   int rd_off[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) rd_off[ks] = tile_off<D>(l32, 2 * ks + h2);
-  int tr_off[DB];
+  int tr_lo[DB], tr_hi[DB];  // first and second 8-row halves of a transposed operand
 #pragma unroll
-  for (int d = 0; d < DB; ++d) tr_off[d] = tr_lane_off<D>(lane, d);
+  for (int d = 0; d < DB; ++d) {
+    tr_lo[d] = tr_lane_off<D>(lane, d, 0);
+    tr_hi[d] = tr_lane_off<D>(lane, d, 8);
+  }
 
   const int npass = paired ? 2 : 1;
   for (int pass = 0; pass < npass; ++pass) {
@@ -106,62 +111,71 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     const int ntq = (qe - qb + BQ - 1) / BQ;
     const int ntiles = ntq * a.group;
 
-    // Prefetch registers for the next tile.
-    bf16x8 pq[LPT], pg[LPT];
+    // L and Delta of a tile travel through registers (wave 0), Q and dO by direct copies.
     float pl = 0.f, pd = 0.f;
     uint32_t prk = 0;
-    auto load_tile = [&](int it) {
-      const int g = it / ntq;
-      const int qt = qb + (it - g * ntq) * BQ;
-      const int h = kvh * a.group + g;
-#pragma unroll
-      for (int u = 0; u < LPT; ++u) {
-        const int i = qt + lr + RPU * u;
-        pq[u] = bf16x8{};
-        pg[u] = bf16x8{};
-        if (i < a.Sq) {
-          const int64_t off = (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh + 8 * lc;
-          pq[u] = *reinterpret_cast<const bf16x8*>(Q + off);
-          pg[u] = *reinterpret_cast<const bf16x8*>(dO + off);
-        }
-      }
-      if (tid < BQ) {
-        const int i = qt + tid;
-        const int64_t row = ((int64_t)b * a.Hq + h) * a.Sq + i;
+    auto load_ld = [&](int it) {
+      if (wave == 0) {
+        const int g = it / ntq;
+        const int i = qb + (it - g * ntq) * BQ + lane;
+        const int h = kvh * a.group + g;
+        const int64_t row = ((int64_t)b * a.Hq + h) * a.Sq + min(i, a.Sq - 1);
         const bool in = i < a.Sq;
         pl = in ? L[row] * kLog2e : __builtin_inff();
         pd = in ? Dl[row] : 0.f;
         if constexpr (DROP) prk = drop_row_key(a, b, h, i);
       }
     };
-    auto store_tile = [&](int stage) {
-#pragma unroll
-      for (int u = 0; u < LPT; ++u) {
-        *reinterpret_cast<bf16x8*>(&sQ[stage][st_off + u * RPU * D]) = pq[u];
-        *reinterpret_cast<bf16x8*>(&sdO[stage][st_off + u * RPU * D]) = pg[u];
+    auto store_ld = [&](int stage) {
+      if (wave == 0) {
+        sL[stage][lane] = pl;
+        sDel[stage][lane] = pd;
+        if constexpr (DROP) sRK[stage][lane] = prk;
       }
-      if (tid < BQ) {
-        sL[stage][tid] = pl;
-        sDel[stage][tid] = pd;
-        if constexpr (DROP) sRK[stage][tid] = prk;
+    };
+    auto issue_tile = [&](int it, int stage) {
+      const int g = it / ntq;
+      const int qt = qb + (it - g * ntq) * BQ;
+      const int h = kvh * a.group + g;
+#pragma unroll
+      for (int u = 0; u < NIW; ++u) {
+        const int blk = wave * NIW + u;
+        const int r = blk * RPI + cp_row;
+        const int i = min(qt + r, a.Sq - 1);  // rows past the end repeat the last row; they are never counted
+        const int64_t off = (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh + 8 * (cp_pc ^ swz<D>(r));
+        dma16(Q + off, &sQ[stage][blk * RPI * D]);
+        dma16(dO + off, &sdO[stage][blk * RPI * D]);
       }
     };
 
     if (ntiles > 0) {
-      load_tile(0);
-      store_tile(0);
+      load_ld(0);
+      issue_tile(0, 0);
+      store_ld(0);
     }
-    __syncthreads();
+    if (ntiles > 1) {
+      load_ld(1);
+      issue_tile(1, 1);
+      store_ld(1);
+      wait_vmcnt<2 * NIW>();  // tile 0 landed; tile 1 may still be in flight
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_lds();
 
-    // One step: stage tile it+1 while computing tile it.  KIND 0 = no element
-    // of the tile is visible to this wave, 1 = boundary tile (per-element
-    // predicate), 2 = interior tile (every element counted).  Each kind runs
-    // in a loop of its own, so no loop body branches around the MFMAs.
+    // One step: start the copies of tile it+2 while computing tile it.  KIND
+    // 0 = no element of the tile is visible to this wave, 1 = boundary tile
+    // (per-element predicate), 2 = interior tile (every element counted).
+    // Each kind runs in a loop of its own, so no loop body branches around the MFMAs.
     auto step = [&](auto kind_c, int it) {
       constexpr int KIND = decltype(kind_c)::value;
-      const int stage = it & 1;
-      const bool has_next = it + 1 < ntiles;
-      if (has_next) load_tile(it + 1);
+      const int stage = it % NST;
+      const int stage2 = (it + 2) % NST;
+      const bool has2 = it + 2 < ntiles;
+      if (has2) {
+        load_ld(it + 2);
+        issue_tile(it + 2, stage2);
+      }
       if constexpr (KIND != 0) {
       const int g = it / ntq;
       const int qt = qb + (it - g * ntq) * BQ;
@@ -230,9 +244,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           const int rb = (32 * m + 16 * t) * D;
 #pragma unroll
           for (int d = 0; d < DB; ++d) {
-            const bf16x8 ao = concat(lds_read_tr(tg + tr_off[d] + rb), lds_read_tr(tg + tr_off[d] + rb + 8 * D));
+            const bf16x8 ao = concat(lds_read_tr(tg + tr_lo[d] + rb), lds_read_tr(tg + tr_hi[d] + rb));
             M::run(accv[d], ao, pmc[t]);
-            const bf16x8 aq = concat(lds_read_tr(tq + tr_off[d] + rb), lds_read_tr(tq + tr_off[d] + rb + 8 * D));
+            const bf16x8 aq = concat(lds_read_tr(tq + tr_lo[d] + rb), lds_read_tr(tq + tr_hi[d] + rb));
             M::run(acck[d], aq, dsc[t]);
           }
         }
@@ -250,8 +264,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
 
       tile(std::integral_constant<bool, KIND == 2>{});
       }
-      if (has_next) store_tile(stage ^ 1);
-      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      if (has2) {
+        store_ld(stage2);
+        wait_vmcnt<2 * NIW>();  // tile it+1 landed; tile it+2 may still be in flight
+      } else {
+        wait_vmcnt<0>();
+      }
+      barrier_lds();
     };
 
     const std::integral_constant<int, 0> kSkip;

@@ -5,9 +5,9 @@
 //
 // Block: 4 waves own 128 consecutive query rows of one (b, h); wave w keeps
 // its 32 rows of Q and dO in registers as MFMA B operands and accumulates
-// dQ^T (D x 32 fp32).  K and V tiles of 64 keys are double-buffered in LDS
-// (swizzled, see fa_tiles.h) with the next tile's loads in flight during the
-// current tile's MFMAs.  S^T = K Q^T and dP^T = V dO^T read row-major
+// dQ^T (D x 32 fp32).  K and V tiles of 64 keys live in a 3-stage LDS ring
+// (swizzled, see fa_tiles.h) filled by direct global->LDS copies issued two
+// tiles ahead; one fence-free barrier per tile.  S^T = K Q^T and dP^T = V dO^T read row-major
 // operands; dQ^T += K^T dS^T reads K transposed through ds_read_b64_tr_b16.
 // S^T has one query per lane column, so L_i and Delta_i are per-lane scalars
 // and dS^T is already the B operand of the last contraction.  Blocks of the
@@ -33,12 +33,13 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
   constexpr int NCH = D / 8;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int RPU = 256 / NCH;
-  constexpr int LPT = BK / RPU;
+  constexpr int NST = 3;                    // LDS ring stages
+  constexpr int RPI = 1024 / (2 * D);       // tile rows per 1 KB global->LDS copy
+  constexpr int NIW = BK / RPI / 4;         // copies per wave per tile per tensor
   constexpr int TILE = BK * D;
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[NST][TILE];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[NST][TILE];
 
   const int nbh = a.B * a.Hq;
   const int wi = blockIdx.x / nbh;
@@ -57,15 +58,19 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
   use_agpr_form();
   const DiagBounds vb = diag_bounds(a);
 
-  const int lr = tid / NCH;
-  const int lc = tid % NCH;
-  const int st_off = tile_off<D>(lr, lc);
+  // Copy u of this wave fills rows (wave*NIW + u)*RPI + lane/NCH; lane l lands in
+  // physical chunk l%NCH, so it fetches the logical chunk stored there.
+  const int cp_row = lane / NCH;
+  const int cp_pc = lane % NCH;
   int rd_off[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) rd_off[ks] = tile_off<D>(l32, 2 * ks + h2);
-  int tr_off[DB];
+  int tr_lo[DB], tr_hi[DB];  // first and second 8-row halves of a transposed operand
 #pragma unroll
-  for (int d = 0; d < DB; ++d) tr_off[d] = tr_lane_off<D>(lane, d);
+  for (int d = 0; d < DB; ++d) {
+    tr_lo[d] = tr_lane_off<D>(lane, d, 0);
+    tr_hi[d] = tr_lane_off<D>(lane, d, 8);
+  }
 
   const int npass = paired ? 2 : 1;
   for (int pass = 0; pass < npass; ++pass) {
@@ -101,43 +106,36 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
     key_range(a, q0, min(q0 + kDqRowsPerBlock, a.Sq) - 1, kb, ke);
     const int ntiles = (ke - kb + BK - 1) / BK;
 
-    bf16x8 pk[LPT], pv[LPT];
-    auto load_tile = [&](int it) {
+    auto issue_tile = [&](int it, int stage) {
       const int kt = kb + it * BK;
 #pragma unroll
-      for (int u = 0; u < LPT; ++u) {
-        const int j = kt + lr + RPU * u;
-        pk[u] = bf16x8{};
-        pv[u] = bf16x8{};
-        if (j < a.Sk) {
-          const int64_t off = (int64_t)b * a.ksb + (int64_t)j * a.kss + (int64_t)kvh * a.ksh + 8 * lc;
-          pk[u] = *reinterpret_cast<const bf16x8*>(K + off);
-          pv[u] = *reinterpret_cast<const bf16x8*>(V + off);
-        }
-      }
-    };
-    auto store_tile = [&](int stage) {
-#pragma unroll
-      for (int u = 0; u < LPT; ++u) {
-        *reinterpret_cast<bf16x8*>(&sK[stage][st_off + u * RPU * D]) = pk[u];
-        *reinterpret_cast<bf16x8*>(&sV[stage][st_off + u * RPU * D]) = pv[u];
+      for (int u = 0; u < NIW; ++u) {
+        const int blk = wave * NIW + u;
+        const int r = blk * RPI + cp_row;
+        const int j = min(kt + r, a.Sk - 1);  // rows past the end repeat the last key; they are never counted
+        const int64_t off = (int64_t)b * a.ksb + (int64_t)j * a.kss + (int64_t)kvh * a.ksh + 8 * (cp_pc ^ swz<D>(r));
+        dma16(K + off, &sK[stage][blk * RPI * D]);
+        dma16(V + off, &sV[stage][blk * RPI * D]);
       }
     };
 
-    if (ntiles > 0) {
-      load_tile(0);
-      store_tile(0);
+    if (ntiles > 0) issue_tile(0, 0);
+    if (ntiles > 1) {
+      issue_tile(1, 1);
+      wait_vmcnt<2 * NIW>();  // tile 0 landed; tile 1 may still be in flight
+    } else {
+      wait_vmcnt<0>();
     }
-    __syncthreads();
+    barrier_lds();
 
-    // One step: stage tile it+1 while computing tile it.  KIND 0 = no element
-    // visible to this wave, 1 = boundary tile (per-element predicate),
-    // 2 = interior tile; each kind runs in a loop of its own.
+    // One step: start the copies of tile it+2 while computing tile it.  KIND 0
+    // = no element visible to this wave, 1 = boundary tile (per-element
+    // predicate), 2 = interior tile; each kind runs in a loop of its own.
     auto step = [&](auto kind_c, int it) {
       constexpr int KIND = decltype(kind_c)::value;
-      const int stage = it & 1;
-      const bool has_next = it + 1 < ntiles;
-      if (has_next) load_tile(it + 1);
+      const int stage = it % NST;
+      const bool has2 = it + 2 < ntiles;
+      if (has2) issue_tile(it + 2, (it + 2) % NST);
       if constexpr (KIND != 0) {
         const int kt = kb + it * BK;
         const __bf16* tk = sK[stage];
@@ -185,7 +183,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
             const int rb = (32 * m + 16 * t) * D;
 #pragma unroll
             for (int d = 0; d < DB; ++d) {
-              const bf16x8 ak = concat(lds_read_tr(tk + tr_off[d] + rb), lds_read_tr(tk + tr_off[d] + rb + 8 * D));
+              const bf16x8 ak = concat(lds_read_tr(tk + tr_lo[d] + rb), lds_read_tr(tk + tr_hi[d] + rb));
               M::run(accq[d], ak, dsc[t]);
             }
           }
@@ -199,8 +197,12 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         elementwise(1, s1, dp1, ds1);
         mma_dq(1, ds1);
       }
-      if (has_next) store_tile(stage ^ 1);
-      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      if (has2)
+        wait_vmcnt<2 * NIW>();  // tile it+1 landed; tile it+2 may still be in flight
+      else
+        wait_vmcnt<0>();
+      barrier_lds();
     };
 
     // This wave's key tiles in order: [0,v0) invisible, [v0,f0) boundary, [f0,f1)

@@ -1,6 +1,6 @@
 // bf16 LDS tiles for the gfx950 MFMA kernels.
 //
-// A tile holds ROWS rows of D bf16 values, row-major, 2*D bytes per row with no
+// A tile holds rows of D bf16 values, row-major, 2*D bytes per row with no
 // padding; the 16-byte chunk c of row r is stored at chunk position
 // c ^ swz(r).  Two read patterns hit the tile:
 //   * row reads (ds_read_b128): lane l reads chunk c of row r0 + l%32 -- the
@@ -8,9 +8,12 @@
 //   * transposed reads (ds_read_b64_tr_b16): each 16-lane group reads a
 //     4-row x 16-column block and every lane receives one column of 4 rows --
 //     the MFMA operand whose k index runs down the rows.
-// swz(r) = 2*(r%4) + (r/4)%2 makes both conflict-free: eight consecutive rows
-// see eight distinct 16-byte bank groups, and four consecutive rows see four
-// distinct 32-byte bank groups.
+// gfx950's LDS serves 256 bytes per clock (64 four-byte banks).  The swizzle
+// spreads sixteen consecutive rows over sixteen distinct 16-byte bank groups
+// (row reads) and four consecutive rows over four distinct 64-byte bank groups
+// (transposed reads of a 32-lane half), so neither pattern has bank conflicts:
+//   D = 128 (16 chunks per row): swz(r) = 4*(r%4) + (r/4)%4
+//   D = 64  (8 chunks, two rows per 256 bytes): swz(r) = 4*((r/2)%2) + (r/4)%4
 #pragma once
 
 #include "fa_common.h"
@@ -19,12 +22,16 @@ namespace fa {
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 // Element offset of chunk c of row r in a swizzled tile with D columns.
 template <int D>
 __device__ __forceinline__ int tile_off(int r, int c) {
-  return r * D + ((c ^ swz(r)) << 3);
+  return r * D + ((c ^ swz<D>(r)) << 3);
 }
 
 __device__ __forceinline__ bf16x8 lds_read_b128(const __bf16* p) {
@@ -39,16 +46,34 @@ __device__ __forceinline__ bf16x8 concat(const bf16x4& a, const bf16x4& b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// Per-lane element offset (excluding the 16-row block base qb*D) of the
-// transposed read that gives lane l column 32*db + l%32 and rows
-// qb + 4*(l/32) + 0..3 (the second half of the operand is 8 rows further on).
+// Direct global->LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
+// l's bytes land at lds_base + 16*l; lds_base must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// Block barrier without a memory fence: LDS writes of this wave are complete
+// (lgkmcnt(0)) but outstanding global->LDS copies are not waited for, so the
+// copies of later tiles stay in flight across it.  Callers wait for the copies
+// they need with wait_vmcnt first.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Per-lane element offset, relative to a 16-row block, of the transposed read
+// that gives lane l column 32*db + l%32 and rows rb + 4*(l/32) + 0..3 of the
+// block (rb = 0 for the first half of an MFMA operand, 8 for the second).
 template <int D>
-__device__ __forceinline__ int tr_lane_off(int lane, int db) {
+__device__ __forceinline__ int tr_lane_off(int lane, int db, int rb) {
   const int g = lane >> 4;        // 16-lane group
   const int s = lane & 15;        // source slot within the group
-  const int r = 4 * (g >> 1) + (s >> 2);            // row within the 16-row block
+  const int r = rb + 4 * (g >> 1) + (s >> 2);       // row within the 16-row block
   const int col = 32 * db + 16 * (g & 1) + 4 * (s & 3);
-  return r * D + (((col >> 3) ^ swz(r)) << 3) + (col & 7);
+  return r * D + (((col >> 3) ^ swz<D>(r)) << 3) + (col & 7);
 }
 
 }  // namespace fa
