@@ -104,8 +104,30 @@ def _torch_reference_forward(q, k, v, w, mask=None, keep=None):
     return o, lse
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dkdv_bf16_long_traffic.txt")
+TRAFFIC_SOURCES = ["fa_dkdv_bf16.hip", "fa_tiles.h", "fa_common.h", "fa_internal.h"]
+
+
+def _dkdv_traffic_bytes():
+    """HBM bytes per dK/dV launch from the committed FETCH_SIZE/WRITE_SIZE counters, scaled by the
+    copy-kernel calibration; None when the kernel sources changed since the counters were taken."""
+    import hashlib
+
+    try:
+        vals = dict(l.strip().split("=", 1) for l in open(TRAFFIC_FILE) if "=" in l and not l.startswith("#"))
+        h = hashlib.sha256()
+        for f in TRAFFIC_SOURCES:
+            h.update(open(os.path.join(ROOT, "flashattention_backward_pass_bwd_amd", "csrc", f), "rb").read())
+        if h.hexdigest()[:16] != vals["kernel_source_hash"]:
+            return None
+        return 1024.0 * (float(vals["fetch_kib"]) * float(vals["fetch_scale"]) +
+                         float(vals["write_kib"]) * float(vals["write_scale"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def _cpu_baseline(w, q, k, v, o, do, lse):
-    """Time the fp64 oracle backward on one query head (its KV head) of the workload."""
+    """Time the fp64 oracle backward on one GQA group (batch 0, KV head 0 and its query heads)."""
     import numpy as np
 
     import oracle
@@ -117,21 +139,21 @@ def _cpu_baseline(w, q, k, v, o, do, lse):
         threads = os.cpu_count() or 1
     g = w.num_heads // w.num_kv_heads
 
-    def head(x, h):  # [B,S,H,D] device -> logical [1,1,S,D] float64 host
-        return x[0:1, :, h:h + 1, :].float().cpu().numpy().transpose(0, 2, 1, 3).astype(np.float64)
+    def heads(x, h0, n):  # [B,S,H,D] device -> logical [1,n,S,D] float64 host
+        return x[0:1, :, h0:h0 + n, :].float().cpu().numpy().transpose(0, 2, 1, 3).astype(np.float64)
 
-    qs, dos, os_ = head(q, 0), head(do, 0), head(o, 0)
-    ks, vs = head(k, 0), head(v, 0)
-    ls = lse[0:1, 0:1, :].cpu().numpy().astype(np.float64)
+    qs, dos, os_ = heads(q, 0, g), heads(do, 0, g), heads(o, 0, g)
+    ks, vs = heads(k, 0, 1), heads(v, 0, 1)
+    ls = lse[0:1, 0:g, :].cpu().numpy().astype(np.float64)
     spec = oracle.Spec(scale=w.scale, causal=w.causal, causal_offset=w.causal_offset, window=w.window)
     t0 = time.perf_counter()
     oracle.backward(qs, ks, vs, os_, dos, ls, spec, None, chunk=2048)
     dt = time.perf_counter() - t0
-    flops = 10.0 * w.seq_q * w.seq_k * w.head_dim * (0.5 if w.causal else 1.0)
+    flops = 10.0 * g * w.seq_q * w.seq_k * w.head_dim * (0.5 if w.causal else 1.0)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"numpy fp64 oracle backward of one query head (b=0, h=0, its KV head, all "
-                      f"{w.seq_q} rows) of the same workload: {dt:.1f} s for {flops / 1e9:.1f} nominal GFLOP; "
-                      f"group size {g} not included (one head)", "seconds": dt}
+            "sample": f"numpy fp64 oracle backward of one GQA group of the same workload (batch 0, KV head 0 "
+                      f"and its {g} query heads, all {w.seq_q} rows; {g}/{w.batch * w.num_heads} of the job): "
+                      f"{dt:.1f} s for {flops / 1e9:.1f} nominal GFLOP", "seconds": dt}
 
 
 def bench_prefill(args, w):
@@ -228,7 +250,9 @@ def bench_prefill(args, w):
                    "window_aware_gflop": round(10.0 * w.head_dim * pairs / 1e9, 3)},
         "kernels_ms": {"preprocess": round(t_pre, 4), "dkdv": round(t_dkdv, 4), "dq": round(t_dq, 4)},
         "roofline": {"kernel": "dkdv_kernel", "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": _dkdv_traffic_bytes() if w.name == synth.LONG_BF16.name else None,
+                     "traffic_unit": "bytes per launch (HBM, FETCH_SIZE+WRITE_SIZE scaled by the copy calibration)",
                      "per_unit": "8*D FLOP per visible (b,h,i,j) pair", "units": pairs},
     }
     _log(f"timed {args.steps} steps: {ms:.3f} ms/step")
@@ -294,19 +318,20 @@ def bench_decode(args):
 
 
 def bench_copy(args):
-    """A plain device copy of known size: calibrates the FETCH_SIZE / WRITE_SIZE counters."""
+    """A plain elementwise copy kernel of known size (dst = -src, 1 GiB each way): calibrates the
+    FETCH_SIZE / WRITE_SIZE counters.  (A same-dtype copy_ would be a DMA memcpy, not a kernel.)"""
     import torch
 
     n = 1 << 28  # 2^28 fp32 = 1 GiB read + 1 GiB written per launch
     src = torch.ones(n, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
     for _ in range(args.warmup):
-        dst.copy_(src)
+        torch.neg(src, out=dst)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(args.steps):
-        dst.copy_(src)
+        torch.neg(src, out=dst)
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
