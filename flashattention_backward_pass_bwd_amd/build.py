@@ -33,12 +33,16 @@ SOURCES = [
 
 ARCH = "gfx950"
 
-# The MFMA tile kernels: schedule for instruction-level parallelism (LDS reads
-# issued ahead of their MFMAs, VALU interleaved with MFMAs) rather than for
-# minimum register pressure -- they run one wave per SIMD by design.
+# The MFMA tile kernels run one wave per SIMD by design, so they are scheduled
+# for instruction-level parallelism (LDS reads issued ahead of their MFMAs,
+# VALU interleaved with MFMAs) rather than for minimum register pressure.  The
+# dQ kernel also asks for the VGPR form of MFMA: S and dP then come out in the
+# registers the exp/dS arithmetic reads, and the compiler moves only the dQ
+# accumulators into accumulation registers.
+ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
 EXTRA_FLAGS = {
-    "fa_dkdv_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
-    "fa_dq_bf16.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "fa_dkdv_bf16.hip": ILP,
+    "fa_dq_bf16.hip": ILP + ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 COMMON_FLAGS = [

@@ -17,6 +17,7 @@ int elem_bytes(int dtype) { return dtype == FA_DTYPE_BF16 ? 2 : 4; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int64_t kMaxSeq = int64_t(1) << 30;
+constexpr int64_t kMaxRowStride = int64_t(1) << 24;  // elements between consecutive rows
 
 fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
   if (p == nullptr) return FA_ERR_NULL;
@@ -38,6 +39,8 @@ fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
     if (qs[i] < 0 || ks[i] < 0) return FA_ERR_ARG;
     if (qs[i] % per16 != 0 || ks[i] % per16 != 0) return FA_ERR_ALIGN;
   }
+  // Tile copies address rows by 32-bit byte offsets from a tile's first row.
+  if (p->q_stride_s > kMaxRowStride || p->kv_stride_s > kMaxRowStride) return FA_ERR_UNSUPPORTED;
   if (p->mask != nullptr) {
     if (p->mask_stride_b < 0 || p->mask_stride_h < 0 || p->mask_stride_q < 0 || p->mask_stride_k < 0)
       return FA_ERR_ARG;

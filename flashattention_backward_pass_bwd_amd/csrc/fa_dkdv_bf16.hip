@@ -105,86 +105,100 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       acck[d] = f32x16{};
       accv[d] = f32x16{};
     }
+    wait_all_vmem();  // K and V rows are in registers before the copy ring starts
 
     int qb, qe;
     query_range(a, k0, min(k0 + kDkdvKeysPerBlock, a.Sk) - 1, qb, qe);
     const int ntq = (qe - qb + BQ - 1) / BQ;
     const int ntiles = ntq * a.group;
 
-    // L and Delta of a tile travel through registers (wave 0), Q and dO by direct copies.
-    float pl = 0.f, pd = 0.f;
-    uint32_t prk = 0;
-    auto load_ld = [&](int it) {
-      if (wave == 0) {
-        const int g = it / ntq;
-        const int i = qb + (it - g * ntq) * BQ + lane;
-        const int h = kvh * a.group + g;
-        const int64_t row = ((int64_t)b * a.Hq + h) * a.Sq + min(i, a.Sq - 1);
-        const bool in = i < a.Sq;
-        pl = in ? L[row] * kLog2e : __builtin_inff();
-        pd = in ? Dl[row] : 0.f;
-        if constexpr (DROP) prk = drop_row_key(a, b, h, i);
-      }
+    // Tiles are numbered it = g*ntq + t (query head g of the group, query tile t).
+    // A scalar cursor (cg, ct) names the tile whose copies are issued next; past
+    // the last tile it stays there, so the last copies repeat into a stage that
+    // is no longer read and every step runs the same straight-line code.
+    int cg = 0, ct = 0;
+    auto advance = [&]() {
+      const int tn = ct + 1;
+      const bool wrap = tn == ntq;
+      const int gn = cg + (wrap ? 1 : 0);
+      const bool end = gn == a.group;
+      ct = end ? ct : (wrap ? 0 : tn);
+      cg = end ? cg : gn;
     };
-    auto store_ld = [&](int stage) {
-      if (wave == 0) {
-        sL[stage][lane] = pl;
-        sDel[stage][lane] = pd;
-        if constexpr (DROP) sRK[stage][lane] = prk;
+    // Copies of the cursor's tile into a stage.  L (natural log) and Delta
+    // (64 floats each) go first, by waves 0 and 1; then the Q and dO rows:
+    // copy u of this wave fills rows (wave*NIW + u)*RPI + lane/NCH.  Rows past
+    // the end repeat the last row; they are never counted.  Per-lane offsets
+    // are 32-bit, relative to the tile's first row (the host bounds the row
+    // stride).  Because L and Delta are issued before the 2*NIW row copies,
+    // waiting until at most 2*NIW copies are in flight covers them.
+    auto issue_tile = [&](int stage) {
+      const int h = kvh * a.group + cg;
+      const int qt = qb + ct * BQ;
+      const int lim = a.Sq - 1 - qt;
+      if (wave < 2) {
+        const float* src = (wave == 0 ? L : Dl) + (((int64_t)b * a.Hq + h) * a.Sq + qt);
+        dma4(src, 4u * (uint32_t)min(lane, lim), lds_addr(wave == 0 ? sL[stage] : sDel[stage]));
       }
-    };
-    auto issue_tile = [&](int it, int stage) {
-      const int g = it / ntq;
-      const int qt = qb + (it - g * ntq) * BQ;
-      const int h = kvh * a.group + g;
+      const int64_t base = (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)qt * a.qss;
+      const __bf16* tq = Q + base;
+      const __bf16* tg = dO + base;
 #pragma unroll
       for (int u = 0; u < NIW; ++u) {
         const int blk = wave * NIW + u;
         const int r = blk * RPI + cp_row;
-        const int i = min(qt + r, a.Sq - 1);  // rows past the end repeat the last row; they are never counted
-        const int64_t off = (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh + 8 * (cp_pc ^ swz<D>(r));
-        dma16(Q + off, &sQ[stage][blk * RPI * D]);
-        dma16(dO + off, &sdO[stage][blk * RPI * D]);
+        const uint32_t off = 2u * ((uint32_t)min(r, lim) * (uint32_t)a.qss + 8u * (uint32_t)(cp_pc ^ swz<D>(r)));
+        dma16(tq, off, lds_addr(&sQ[stage][blk * RPI * D]));
+        dma16(tg, off, lds_addr(&sdO[stage][blk * RPI * D]));
       }
+    };
+    // Dropout row keys of the cursor's tile (lanes 0-15 of each wave, 16 rows per wave).
+    auto store_rk = [&](int stage) {
+      if constexpr (DROP) {
+        if (lane < 16) {
+          const int h = kvh * a.group + cg;
+          sRK[stage][16 * wave + lane] = drop_row_key(a, b, h, qb + ct * BQ + 16 * wave + lane);
+        }
+      }
+    };
+    // Wave 0 turns a landed tile's L into L*log2(e) in place (one value per lane).
+    auto scale_l = [&](int stage) {
+      if (wave == 0) sL[stage][lane] *= kLog2e;
     };
 
     if (ntiles > 0) {
-      load_ld(0);
-      issue_tile(0, 0);
-      store_ld(0);
+      issue_tile(0);
+      store_rk(0);
+      advance();
+      issue_tile(1);
+      store_rk(1);
+      advance();
+      wait_vmcnt<2 * NIW>();  // tile 0 and the L/Delta of tile 1 landed
+      scale_l(0);             // the first step scales tile 1's
+      barrier_lds();
     }
-    if (ntiles > 1) {
-      load_ld(1);
-      issue_tile(1, 1);
-      store_ld(1);
-      wait_vmcnt<2 * NIW>();  // tile 0 landed; tile 1 may still be in flight
-    } else {
-      wait_vmcnt<0>();
-    }
-    barrier_lds();
 
-    // One step: start the copies of tile it+2 while computing tile it.  KIND
-    // 0 = no element of the tile is visible to this wave, 1 = boundary tile
-    // (per-element predicate), 2 = interior tile (every element counted).
-    // Each kind runs in a loop of its own, so no loop body branches around the MFMAs.
-    auto step = [&](auto kind_c, int it) {
+    // One step: issue the copies of tile it+2 (the cursor) while computing tile
+    // it = (g, t) from stage st.  KIND 0 = no element of the tile is visible to
+    // this wave, 1 = boundary tile (per-element predicate), 2 = interior tile
+    // (every element counted).  Each kind runs in a loop of its own, so no loop
+    // body branches.
+    int st = 0;
+    auto step = [&](auto kind_c, int g, int t) {
       constexpr int KIND = decltype(kind_c)::value;
-      const int stage = it % NST;
-      const int stage2 = (it + 2) % NST;
-      const bool has2 = it + 2 < ntiles;
-      if (has2) {
-        load_ld(it + 2);
-        issue_tile(it + 2, stage2);
-      }
+      const int stage = st;
+      const int stage1 = st == NST - 1 ? 0 : st + 1;  // (st + 1) % NST
+      const int stage2 = st == 0 ? 2 : st - 1;        // (st + 2) % NST
+      issue_tile(stage2);
+      // L of tile it+1 landed with the wait at the end of the previous step.
+      scale_l(stage1);
       if constexpr (KIND != 0) {
-      const int g = it / ntq;
-      const int qt = qb + (it - g * ntq) * BQ;
+      const int qt = qb + t * BQ;
       const int h = kvh * a.group + g;
       const __bf16* tq = sQ[stage];
       const __bf16* tg = sdO[stage];
       const float* tl = sL[stage];
       const float* td = sDel[stage];
-
       // S (m-th 32-row half) = Q K^T and dP = dO V^T.
       auto mma_sdp = [&](int m, f32x16& s, f32x16& dp) {
         s = f32x16{};
@@ -265,12 +279,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       tile(std::integral_constant<bool, KIND == 2>{});
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (has2) {
-        store_ld(stage2);
-        wait_vmcnt<2 * NIW>();  // tile it+1 landed; tile it+2 may still be in flight
-      } else {
-        wait_vmcnt<0>();
-      }
+      store_rk(stage2);
+      advance();
+      st = stage1;
+      wait_vmcnt<2 * NIW>();  // tile it+1 and the L/Delta of tile it+2 landed; its rows may still be in flight
       barrier_lds();
     };
 
@@ -294,14 +306,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         f1 = f0;
         while (f1 < v1 && all(f1)) ++f1;
       }
-      const int base = g * ntq;
       int t = 0;
-      for (; t < v0; ++t) step(kSkip, base + t);
-      for (; t < f0; ++t) step(kEdge, base + t);
-      for (; t < f1; ++t) step(kInner, base + t);
-      for (; t < v1; ++t) step(kEdge, base + t);
-      for (; t < ntq; ++t) step(kSkip, base + t);
+      for (; t < v0; ++t) step(kSkip, g, t);
+      for (; t < f0; ++t) step(kEdge, g, t);
+      for (; t < f1; ++t) step(kInner, g, t);
+      for (; t < v1; ++t) step(kEdge, g, t);
+      for (; t < ntq; ++t) step(kSkip, g, t);
     }
+    wait_vmcnt<0>();  // the repeated copies of the last steps have landed
 
     if (jl < a.Sk) {
 #pragma unroll

@@ -10,7 +10,8 @@
 // tiles ahead; one fence-free barrier per tile.  S^T = K Q^T and dP^T = V dO^T read row-major
 // operands; dQ^T += K^T dS^T reads K transposed through ds_read_b64_tr_b16.
 // S^T has one query per lane column, so L_i and Delta_i are per-lane scalars
-// and dS^T is already the B operand of the last contraction.  Blocks of the
+// (without dropout the dP^T chain starts from -Delta_i, so dP - Delta comes
+// out of the MFMAs) and dS^T is already the B operand of the last contraction.  Blocks of the
 // query heads sharing a KV head are dealt to one XCD; for causal attention
 // without a window, block i also takes query block nqb-1-i.
 #include <type_traits>
@@ -55,7 +56,6 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
   const int lane = tid & 63;
   const int h2 = lane >> 5;
   const int l32 = lane & 31;
-  use_agpr_form();
   const DiagBounds vb = diag_bounds(a);
 
   // Copy u of this wave fills rows (wave*NIW + u)*RPI + lane/NCH; lane l lands in
@@ -97,7 +97,12 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
     const float del = il < a.Sq ? Dl[lrow] : 0.f;
     uint32_t rk = 0;
     if constexpr (DROP) rk = drop_row_key(a, b, h, il);
+    wait_all_vmem();  // Q, dO rows, L and Delta are in registers before the copy ring starts
 
+    // Without dropout dP - Delta comes straight out of the MFMA chain: it starts from -Delta.
+    f32x16 dp_init;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dp_init[r] = DROP ? 0.f : -del;
     f32x16 accq[DB];
 #pragma unroll
     for (int d = 0; d < DB; ++d) accq[d] = f32x16{};
@@ -106,16 +111,21 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
     key_range(a, q0, min(q0 + kDqRowsPerBlock, a.Sq) - 1, kb, ke);
     const int ntiles = (ke - kb + BK - 1) / BK;
 
+    // Copy u of this wave fills key rows (wave*NIW + u)*RPI + lane/NCH of a tile.
+    // Rows past the end repeat the last key; they are never counted.  Per-lane
+    // offsets are 32-bit, relative to the tile's first key (the host bounds the
+    // row stride).
     auto issue_tile = [&](int it, int stage) {
       const int kt = kb + it * BK;
+      const int lim = a.Sk - 1 - kt;
+      const int64_t base = (int64_t)b * a.ksb + (int64_t)kt * a.kss + (int64_t)kvh * a.ksh;
 #pragma unroll
       for (int u = 0; u < NIW; ++u) {
         const int blk = wave * NIW + u;
         const int r = blk * RPI + cp_row;
-        const int j = min(kt + r, a.Sk - 1);  // rows past the end repeat the last key; they are never counted
-        const int64_t off = (int64_t)b * a.ksb + (int64_t)j * a.kss + (int64_t)kvh * a.ksh + 8 * (cp_pc ^ swz<D>(r));
-        dma16(K + off, &sK[stage][blk * RPI * D]);
-        dma16(V + off, &sV[stage][blk * RPI * D]);
+        const uint32_t off = 2u * ((uint32_t)min(r, lim) * (uint32_t)a.kss + 8u * (uint32_t)(cp_pc ^ swz<D>(r)));
+        dma16(K + base, off, lds_addr(&sK[stage][blk * RPI * D]));
+        dma16(V + base, off, lds_addr(&sV[stage][blk * RPI * D]));
       }
     };
 
@@ -143,7 +153,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         // S^T (m-th 32-key half) = K Q^T and dP^T = V dO^T.
         auto mma_sdp = [&](int m, f32x16& s, f32x16& dp) {
           s = f32x16{};
-          dp = f32x16{};
+          dp = dp_init;
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             M::run(s, lds_read_b128(tk + rd_off[ks] + 32 * m * D), qr[ks]);
@@ -174,7 +184,8 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
               if constexpr (DROP) dpv *= drop_keep(rk, kt + row, a.drop_thr) ? a.drop_inv : 0.f;
             }
             const float p = __builtin_amdgcn_exp2f(x);
-            dsc[r >> 3][r & 7] = (__bf16)(p * (dpv - del));
+            if constexpr (DROP) dsc[r >> 3][r & 7] = (__bf16)(p * (dpv - del));
+            else dsc[r >> 3][r & 7] = (__bf16)(p * dpv);
           }
         };
         auto mma_dq = [&](int m, const bf16x8 (&dsc)[2]) {

@@ -46,11 +46,33 @@ __device__ __forceinline__ bf16x8 concat(const bf16x4& a, const bf16x4& b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-// Direct global->LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane
-// l's bytes land at lds_base + 16*l; lds_base must be wave-uniform.
-__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+// LDS byte address of a __shared__ object: a generic pointer to LDS carries
+// the LDS offset in its low 32 bits.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// Direct global->LDS copies (global_load_lds_dword / _dwordx4, scalar base +
+// 32-bit per-lane byte offset): lane l's 4 or 16 bytes at sbase + voff land
+// at LDS byte address lds + 4*l or 16*l; lds must be wave-uniform.  They are
+// issued as inline assembly on purpose: the compiler then does not treat them
+// as LDS writes and does not wait for every copy in flight before each later
+// LDS read, which would serialise the copy ring.  Callers order them with
+// wait_vmcnt (every wave waits for its own copies) and a block barrier.
+// M0 holds the LDS address for the copy; it is saved and restored around it,
+// with the one wait state an M0 write needs before an LDS DMA.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t sv;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(sv)
+      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)));
+}
+
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  uint32_t sv;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(sv)
+      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)));
 }
 
 // Block barrier without a memory fence: LDS writes of this wave are complete
@@ -58,6 +80,13 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
 // copies of later tiles stay in flight across it.  Callers wait for the copies
 // they need with wait_vmcnt first.
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Waits for every vector memory access of this wave, as an instruction the
+// compiler sees: loads the compiler issued (register operands loaded before a
+// copy ring starts) are then known complete, and it places no wait of its own
+// for them inside the ring's loop, where such a wait would also stall on the
+// copies in flight.
+__device__ __forceinline__ void wait_all_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

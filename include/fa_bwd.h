@@ -42,7 +42,7 @@ typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = -1,        /* a required pointer is NULL */
   FA_ERR_SHAPE = -2,       /* a size <= 0, or num_heads % num_kv_heads != 0 */
-  FA_ERR_UNSUPPORTED = -3, /* head_dim / dtype / history length outside the built kernels */
+  FA_ERR_UNSUPPORTED = -3, /* head_dim / dtype / history length / row stride outside the built kernels */
   FA_ERR_ALIGN = -4,       /* base or row stride not a multiple of 16 bytes, or D not unit-stride */
   FA_ERR_ARG = -5,         /* dropout_p not in [0,1), causal_offset < 0, window < 0, bad stride */
   FA_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
@@ -67,6 +67,8 @@ typedef void* fa_stream_t;
  * key-side tensors), so both [B,S,H,D] and [B,H,S,D] storage are expressed
  * by choosing the strides.  head_dim is unit-stride.  The four query-side
  * tensors share one stride set; the four key-side tensors share the other.
+ * The sequence strides q_stride_s and kv_stride_s may not exceed 2^24
+ * elements (FA_ERR_UNSUPPORTED): tile copies use 32-bit row offsets.
  * L (natural-log log-sum-exp from the forward) and Delta are fp32,
  * contiguous [batch, num_heads, seq_q].
  *
