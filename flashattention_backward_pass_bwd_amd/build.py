@@ -40,9 +40,10 @@ ARCH = "gfx950"
 # registers the exp/dS arithmetic reads, and the compiler moves only the dQ
 # accumulators into accumulation registers.
 ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 EXTRA_FLAGS = {
-    "fa_dkdv_bf16.hip": ILP,
-    "fa_dq_bf16.hip": ILP + ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "fa_dkdv_bf16.hip": VGPR_FORM,
+    "fa_dq_bf16.hip": ILP + VGPR_FORM,
 }
 
 COMMON_FLAGS = [

@@ -8,18 +8,29 @@
 // k0 + 32w .. +31 and keeps their K and V rows in registers as MFMA B operands
 // (v_mfma_f32_32x32x16_bf16), accumulating dK^T and dV^T (D x 32 fp32) in
 // accumulation registers.  The block walks every (query head of the group,
-// 64-row query tile) pair.  Q and dO tiles live in a 3-stage LDS ring
-// (swizzled, see fa_tiles.h) filled by direct global->LDS copies issued two
-// tiles ahead, so their latency hides behind two tiles of MFMA work and the
-// copies need no registers; L and Delta (64 floats each per tile) take the
-// register path.  One fence-free barrier per tile.  S = Q K^T and dP = dO V^T read row-major
-// operands; the transposed operands of dV^T += dO^T (P.M) and dK^T += Q^T dS
-// come from the same tiles through ds_read_b64_tr_b16.  P and dS never leave
-// registers: the C layout of S (one key per lane column) is the B layout of
-// the second pair of contractions.  A tile is processed as two 32-row halves
-// so that the exp/dS arithmetic of one half can overlap the MFMAs of the
-// other.  For causal attention without a window, block i also takes key block
-// nkb-1-i, so every block carries the same amount of work.
+// 64-row query tile) pair.  Per tile and wave: S = Q K^T and dP = dO V^T
+// (row-major A operands from LDS), P and dS in registers, then dV^T += dO^T (P.M)
+// and dK^T += Q^T dS (transposed A operands through ds_read_b64_tr_b16).  The
+// C layout of S (one key per lane column) is the B layout of the second pair
+// of contractions, so P and dS never leave registers.
+//
+// Software pipeline.  A tile is two 32-row halves; the step of tile it runs
+//   A: S/dP of half 1 (MFMA)      with  exp/dS of half 0 (VALU)
+//      -- wait for tile it+1's copies, block barrier --
+//   B: copies of tile it+3 (and L/Delta of tile it+4) issued; dV/dK of half 0
+//   C: S/dP of half 0 of tile it+1 with exp/dS of half 1
+//   D: dV/dK of half 1
+// so the exp/dS arithmetic of one half always overlaps the MFMAs of another,
+// and the next tile's first MFMAs follow the current tile's last without a
+// barrier in between.  Q and dO tiles live in a 4-stage LDS ring (swizzled,
+// see fa_tiles.h) filled by direct global->LDS copies three tiles ahead; one
+// barrier per tile separates the last reads of a stage from its refill.  L and
+// Delta (64 floats per tile) travel through an 8-stage ring four tiles ahead;
+// two tiles before use, wave 0 turns L into -L*log2(e) and wave 1 turns Delta
+// into -Delta in place, so P = exp2(S*scale*log2(e) - L*log2(e)) is one FMA
+// and one exp2, and (without dropout) the dP chain starts from -Delta and
+// yields dP - Delta directly.  For causal attention without a window, block i
+// also takes key block nkb-1-i, so every block carries the same work.
 #include <type_traits>
 
 #include "fa_internal.h"
@@ -36,21 +47,31 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
                                                            const float* __restrict__ Dl,
                                                            __bf16* __restrict__ dK, __bf16* __restrict__ dV,
                                                            int nkb, int paired) {
-  using M = Mma<__bf16>;
   constexpr int BQ = 64;
   constexpr int NCH = D / 8;                // 16-byte chunks per row
   constexpr int KS = D / 16;                // k-blocks of the head_dim contraction
   constexpr int DB = D / 32;                // 32-row blocks of dK^T / dV^T
-  constexpr int NST = 3;                    // LDS ring stages
+  constexpr int NST = 4;                    // Q/dO ring stages
+  constexpr int NSL = 8;                    // L/Delta/row-key ring stages
   constexpr int RPI = 1024 / (2 * D);       // tile rows per 1 KB global->LDS copy (64 lanes x 16 B)
   constexpr int NIW = BQ / RPI / 4;         // copies per wave per tile per tensor
   constexpr int TILE = BQ * D;
+  constexpr bool FOLD = !DROP;              // dP chain seeded with -Delta
+  constexpr int NSD = 2 * KS;               // S/dP MFMAs per 32-row half
+  constexpr int NDK = 4 * DB;               // dV/dK MFMAs per 32-row half
+#ifndef FA_DKDV_NP
+#define FA_DKDV_NP 3
+#endif
+  constexpr int NP = FA_DKDV_NP;            // dV/dK MFMAs whose operands the preceding section reads
+  static_assert(NSD == NDK, "the S/dP section carries one transposed read per MFMA");
+  static_assert(NSD % (NIW / 2) == 0, "a section carries a quarter of a tile's copies evenly");
 
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[NST][TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 sdO[NST][TILE];
-  __shared__ __attribute__((aligned(16))) float sL[NST][BQ];
-  __shared__ __attribute__((aligned(16))) float sDel[NST][BQ];
-  __shared__ uint32_t sRK[NST][DROP ? BQ : 1];
+  // Ring stage s holds the Q tile (sT[s][0]) and the dO tile (sT[s][1]) side by
+  // side, so one per-lane address per stage serves both through immediate offsets.
+  __shared__ __attribute__((aligned(16))) __bf16 sT[NST][2][TILE];
+  __shared__ __attribute__((aligned(16))) float sL[NSL][BQ];
+  __shared__ __attribute__((aligned(16))) float sDel[NSL][BQ];
+  __shared__ __attribute__((aligned(16))) uint32_t sRK[DROP ? NSL : 1][DROP ? BQ : 1];
 
   const int nbh = a.B * a.Hkv;
   const int wi = blockIdx.x / nbh;
@@ -62,7 +83,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
   const int lane = tid & 63;
   const int h2 = lane >> 5;
   const int l32 = lane & 31;
-  use_agpr_form();
+
   const DiagBounds vb = diag_bounds(a);
 
   // Copy u of this wave fills rows (wave*NIW + u)*RPI + lane/NCH; lane l lands in
@@ -88,16 +109,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     const int kw0 = k0 + wave * kDkdvKeysPerWave;
     const int jl = kw0 + l32;
 
+    // K and V rows of this wave's keys, straight into accumulation registers
+    // (keys past the end repeat the last key; no element of theirs is counted).
     bf16x8 kr[KS], vr[KS];
     const int64_t koff = (int64_t)b * a.ksb + (int64_t)jl * a.kss + (int64_t)kvh * a.ksh;
+    const int64_t kclamp = (int64_t)b * a.ksb + (int64_t)min(jl, a.Sk - 1) * a.kss + (int64_t)kvh * a.ksh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      kr[s] = bf16x8{};
-      vr[s] = bf16x8{};
-      if (jl < a.Sk) {
-        kr[s] = *reinterpret_cast<const bf16x8*>(K + koff + 16 * s + 8 * h2);
-        vr[s] = *reinterpret_cast<const bf16x8*>(V + koff + 16 * s + 8 * h2);
-      }
+      kr[s] = ld16_agpr(K + kclamp + 16 * s + 8 * h2);
+      vr[s] = ld16_agpr(V + kclamp + 16 * s + 8 * h2);
     }
     f32x16 acck[DB], accv[DB];
 #pragma unroll
@@ -105,215 +125,358 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       acck[d] = f32x16{};
       accv[d] = f32x16{};
     }
-    wait_all_vmem();  // K and V rows are in registers before the copy ring starts
+    wait_vmcnt<0>();  // K and V rows landed before the copy ring starts
 
     int qb, qe;
     query_range(a, k0, min(k0 + kDkdvKeysPerBlock, a.Sk) - 1, qb, qe);
     const int ntq = (qe - qb + BQ - 1) / BQ;
     const int ntiles = ntq * a.group;
 
-    // Tiles are numbered it = g*ntq + t (query head g of the group, query tile t).
-    // A scalar cursor (cg, ct) names the tile whose copies are issued next; past
-    // the last tile it stays there, so the last copies repeat into a stage that
-    // is no longer read and every step runs the same straight-line code.
-    int cg = 0, ct = 0;
-    auto advance = [&]() {
-      const int tn = ct + 1;
-      const bool wrap = tn == ntq;
-      const int gn = cg + (wrap ? 1 : 0);
-      const bool end = gn == a.group;
-      ct = end ? ct : (wrap ? 0 : tn);
-      cg = end ? cg : gn;
-    };
-    // Copies of the cursor's tile into a stage.  L (natural log) and Delta
-    // (64 floats each) go first, by waves 0 and 1; then the Q and dO rows:
-    // copy u of this wave fills rows (wave*NIW + u)*RPI + lane/NCH.  Rows past
-    // the end repeat the last row; they are never counted.  Per-lane offsets
-    // are 32-bit, relative to the tile's first row (the host bounds the row
-    // stride).  Because L and Delta are issued before the 2*NIW row copies,
-    // waiting until at most 2*NIW copies are in flight covers them.
-    auto issue_tile = [&](int stage) {
-      const int h = kvh * a.group + cg;
-      const int qt = qb + ct * BQ;
-      const int lim = a.Sq - 1 - qt;
-      if (wave < 2) {
-        const float* src = (wave == 0 ? L : Dl) + (((int64_t)b * a.Hq + h) * a.Sq + qt);
-        dma4(src, 4u * (uint32_t)min(lane, lim), lds_addr(wave == 0 ? sL[stage] : sDel[stage]));
-      }
-      const int64_t base = (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)qt * a.qss;
-      const __bf16* tq = Q + base;
-      const __bf16* tg = dO + base;
-#pragma unroll
-      for (int u = 0; u < NIW; ++u) {
-        const int blk = wave * NIW + u;
+    if (ntiles > 0) {
+      // Tiles are numbered it = g*ntq + t (query head g of the group, query
+      // tile t).  A cursor names the tile whose copies are issued next; past
+      // the last tile it stays there, so the last copies repeat into stages
+      // that are never read and every step runs the same straight-line code.
+      struct Cursor {
+        int g, t;
+      };
+      auto advance = [&](Cursor& c) {
+        const int tn = c.t + 1;
+        const bool wrap = tn == ntq;
+        const int gn = c.g + (wrap ? 1 : 0);
+        const bool end = gn == a.group;
+        c.t = end ? c.t : (wrap ? 0 : tn);
+        c.g = end ? c.g : gn;
+      };
+      // Q and dO rows of a tile into a ring stage: copy u of this wave fills rows
+      // (wave*NIW + u)*RPI + lane/NCH.  Rows past the end repeat the last row;
+      // they are never counted.  Per-lane offsets are 32-bit, relative to the
+      // tile's first row (the host bounds the row stride).
+      auto qdo_base = [&](const Cursor& c) {
+        const int h = kvh * a.group + c.g;
+        const int qt = qb + c.t * BQ;
+        return (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)qt * a.qss;
+      };
+      // Copy u (0 .. 2*NIW-1; even: Q, odd: dO) of the cursor's tile into a stage.
+      auto issue_copy = [&](const Cursor& c, int64_t base, int stage, int u) {
+        const int lim = a.Sq - 1 - (qb + c.t * BQ);
+        const int blk = wave * NIW + (u >> 1);
         const int r = blk * RPI + cp_row;
         const uint32_t off = 2u * ((uint32_t)min(r, lim) * (uint32_t)a.qss + 8u * (uint32_t)(cp_pc ^ swz<D>(r)));
-        dma16(tq, off, lds_addr(&sQ[stage][blk * RPI * D]));
-        dma16(tg, off, lds_addr(&sdO[stage][blk * RPI * D]));
-      }
-    };
-    // Dropout row keys of the cursor's tile (lanes 0-15 of each wave, 16 rows per wave).
-    auto store_rk = [&](int stage) {
-      if constexpr (DROP) {
-        if (lane < 16) {
-          const int h = kvh * a.group + cg;
-          sRK[stage][16 * wave + lane] = drop_row_key(a, b, h, qb + ct * BQ + 16 * wave + lane);
-        }
-      }
-    };
-    // Wave 0 turns a landed tile's L into L*log2(e) in place (one value per lane).
-    auto scale_l = [&](int stage) {
-      if (wave == 0) sL[stage][lane] *= kLog2e;
-    };
-
-    if (ntiles > 0) {
-      issue_tile(0);
-      store_rk(0);
-      advance();
-      issue_tile(1);
-      store_rk(1);
-      advance();
-      wait_vmcnt<2 * NIW>();  // tile 0 and the L/Delta of tile 1 landed
-      scale_l(0);             // the first step scales tile 1's
-      barrier_lds();
-    }
-
-    // One step: issue the copies of tile it+2 (the cursor) while computing tile
-    // it = (g, t) from stage st.  KIND 0 = no element of the tile is visible to
-    // this wave, 1 = boundary tile (per-element predicate), 2 = interior tile
-    // (every element counted).  Each kind runs in a loop of its own, so no loop
-    // body branches.
-    int st = 0;
-    auto step = [&](auto kind_c, int g, int t) {
-      constexpr int KIND = decltype(kind_c)::value;
-      const int stage = st;
-      const int stage1 = st == NST - 1 ? 0 : st + 1;  // (st + 1) % NST
-      const int stage2 = st == 0 ? 2 : st - 1;        // (st + 2) % NST
-      issue_tile(stage2);
-      // L of tile it+1 landed with the wait at the end of the previous step.
-      scale_l(stage1);
-      if constexpr (KIND != 0) {
-      const int qt = qb + t * BQ;
-      const int h = kvh * a.group + g;
-      const __bf16* tq = sQ[stage];
-      const __bf16* tg = sdO[stage];
-      const float* tl = sL[stage];
-      const float* td = sDel[stage];
-      // S (m-th 32-row half) = Q K^T and dP = dO V^T.
-      auto mma_sdp = [&](int m, f32x16& s, f32x16& dp) {
-        s = f32x16{};
-        dp = f32x16{};
+        if (u & 1)
+          dma16(dO + base, off, lds_addr(&sT[stage][1][blk * RPI * D]));
+        else
+          dma16(Q + base, off, lds_addr(&sT[stage][0][blk * RPI * D]));
+      };
+      // A pending set of copies: the tile, its row base and its ring stage.
+      struct Job {
+        Cursor c;
+        int64_t base;
+        int stage;
+      };
+      constexpr int NC = 2 * NIW;  // copies per tile per wave
+      constexpr int PER = NC / 4;  // copies per section
+      static_assert(NC % 4 == 0, "a tile's copies spread over four sections");
+      auto job_of = [&](const Cursor& c, int stage) { return Job{c, qdo_base(c), stage}; };
+      auto issue_job = [&](const Job& j, int u) { issue_copy(j.c, j.base, j.stage, u); };
+      // Slot hook: copies u0 .. u0+PER-1 of job j, one every nslots/PER slots.
+      auto copies_at = [&](const Job& j, int u0, int k, int nslots) {
+        if (k % (nslots / PER) == 0) issue_job(j, u0 + k / (nslots / PER));
+      };
+      auto issue_qdo = [&](const Cursor& c, int stage) {
+        const int64_t base = qdo_base(c);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          M::run(s, lds_read_b128(tq + rd_off[ks] + 32 * m * D), kr[ks]);
-          M::run(dp, lds_read_b128(tg + rd_off[ks] + 32 * m * D), vr[ks]);
+        for (int u = 0; u < 2 * NIW; ++u) issue_copy(c, base, stage, u);
+      };
+      // L (wave 0) and Delta (wave 1) of a tile into an L ring stage (rows past
+      // the end repeat the last row), and the tile's dropout row keys (lanes
+      // 0-15 of each wave, 16 rows per wave).
+      auto issue_ld = [&](const Cursor& c, int lst) {
+        const int h = kvh * a.group + c.g;
+        const int qt = qb + c.t * BQ;
+        if (wave < 2) {
+          const float* src = (wave == 0 ? L : Dl) + (((int64_t)b * a.Hq + h) * a.Sq + qt);
+          dma4(src, 4u * (uint32_t)min(lane, a.Sq - 1 - qt), lds_addr(wave == 0 ? sL[lst] : sDel[lst]));
+        }
+        if constexpr (DROP) {
+          if (lane < 16) sRK[lst][16 * wave + lane] = drop_row_key(a, b, h, qt + 16 * wave + lane);
         }
       };
-      // P, dropout and dS for one half, packed into the bf16 B operands of the next contractions.
-      auto elementwise = [&](auto full_c, int m, const f32x16& s, const f32x16& dp, bf16x8 (&pmc)[2],
-                             bf16x8 (&dsc)[2]) {
+      // Once a stage's L/Delta landed: L -> -L*log2(e) (wave 0), Delta -> -Delta
+      // (wave 1, when the dP chain is seeded with it).
+      auto fix_ld = [&](int lst) {
+        if (wave == 0) sL[lst][lane] *= -kLog2e;
+        if constexpr (FOLD) {
+          if (wave == 1) sDel[lst][lane] = -sDel[lst][lane];
+        }
+      };
+      // Waits until this wave's copies issued before the previous step's have
+      // landed (waves 0 and 1 issue one more copy per step: L or Delta).
+      auto wait_prev = [&]() {
+        if (wave < 2)
+          wait_vmcnt<2 * NIW + 1>();
+        else
+          wait_vmcnt<2 * NIW>();
+      };
+
+      // Instruction order inside a step is fixed by hand: one wave per SIMD means
+      // the MFMAs overlap only the VALU and LDS work placed between them, so every
+      // slot below (an MFMA, the LDS reads a few MFMAs ahead, a slice of the
+      // exp/dS arithmetic) is fenced off with sched_barrier.
+      auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
+      // Row-major A operand of S/dP MFMA k (even: Q chunk k/2 for S, odd: dO chunk for dP).
+      auto rd_op = [&](int m, int stq, int k) {
+        return lds_read_b128(sT[stq][0] + rd_off[k >> 1] + (k & 1) * TILE + 32 * m * D);
+      };
+      // Transposed A operand half j (0 .. 2*NDK-1) of dV/dK MFMA j/2 of half m:
+      // MFMA n = 2*DB*t + 2d + w takes dO^T (w = 0, for dV) or Q^T (w = 1, for dK)
+      // rows 32m + 16t .. +15 of column block d; j even = first 8 rows, odd = last 8.
+      auto rd_tr = [&](int m, int stq, int j) {
+        const int n = j >> 1, t = n / (2 * DB), d = (n % (2 * DB)) >> 1, w = n & 1;
+        const __bf16* base = sT[stq][0] + (w ? 0 : TILE) + (32 * m + 16 * t) * D;
+        return lds_read_tr(base + ((j & 1) ? tr_hi[d] : tr_lo[d]));
+      };
+      auto mma_dkv = [&](int n, const bf16x4& lo, const bf16x4& hi, const bf16x8 (&pmc)[2], const bf16x8 (&dsc)[2]) {
+        const int t = n / (2 * DB), d = (n % (2 * DB)) >> 1;
+        if (n & 1)
+          mfma_acc(acck[d], concat(lo, hi), dsc[t]);
+        else
+          mfma_acc(accv[d], concat(lo, hi), pmc[t]);
+      };
+
+      // Section "S/dP + exp/dS": S/dP of half ms from stage sts (with FOLD the dP
+      // chain starts from the rows' -Delta, L ring stage lsts), overlapped with the
+      // exp/dS of half me of tile (qt, h) (values se, dpe; L ring stage lste) and
+      // with the transposed reads of the first NP MFMAs of that half's dV/dK (stage ste).
+      // Operand reads run PF MFMAs ahead; the 16 exp/dS elements are spread over
+      // the slots after the first (which wait for the L/Delta reads).
+      auto sec_sdp_ew = [&](auto full_c, int ms, int sts, int lsts, f32x16& s, f32x16& dp, int me, int ste,
+                            int lste, int qt, int h, const f32x16& se, const f32x16& dpe, bf16x8 (&pmc)[2],
+                            bf16x8 (&dsc)[2], bf16x4 (&trp)[2 * NP], auto&& slot_extra) {
         constexpr bool FULL = decltype(full_c)::value;
+        constexpr int PF = 6;
+        bf16x8 op[8];
+        f32x4 nl[4], dl[4];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          nl[r4] = *reinterpret_cast<const f32x4*>(&sL[lste][32 * me + 8 * r4 + 4 * h2]);
+          if constexpr (!FOLD) dl[r4] = *reinterpret_cast<const f32x4*>(&sDel[lste][32 * me + 8 * r4 + 4 * h2]);
+        }
+        op[0] = rd_op(ms, sts, 0);
+        op[1] = rd_op(ms, sts, 1);
+        if constexpr (FOLD) {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[lsts][32 * ms + 8 * r4 + 4 * h2]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = d4[e];
+          }
+        }
+#pragma unroll
+        for (int k = 2; k < PF; ++k) op[k] = rd_op(ms, sts, k);
         const int dl0 = jl - qt;  // d = j - i = dl0 - row
         const int rlim = a.Sq - qt;
         const bool jin = jl < a.Sk;
         const int jc = min(jl, a.Sk - 1);
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int row0 = 32 * m + 8 * r4 + 4 * h2;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(tl + row0);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(td + row0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * r4 + e;
-            float x = __builtin_fmaf(s[r], a.scale_log2, -l4[e]);
-            if constexpr (!FULL) {
-              const int row = row0 + e;
-              const int dd = dl0 - row;
-              bool ok = jin && row < rlim && dd > vb.dlo && dd < vb.dhi;
-              if constexpr (MASK) {
-                // clamped indices keep the load in bounds; ok discards out-of-range elements
-                const float mv = mask_at(a, b, h, min(qt + row, a.Sq - 1), jc);
-                ok = ok && !(mv <= kMaskedSentinel);
-                x = __builtin_fmaf(mv, kLog2e, x);
-              }
-              x = ok ? x : -__builtin_inff();
+        float pv[16], dv[16];
+        // exp/dS of element r (C-layout register r of half me); odd r packs the pair.
+        auto ew_elem = [&](int r) {
+          const int row = 32 * me + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          float x = __builtin_fmaf(se[r], a.scale_log2, nl[r >> 2][r & 3]);
+          if constexpr (!FULL) {
+            const int dd = dl0 - row;
+            bool ok = jin && row < rlim && dd > vb.dlo && dd < vb.dhi;
+            if constexpr (MASK) {
+              // clamped indices keep the load in bounds; ok discards out-of-range elements
+              const float mv = mask_at(a, b, h, min(qt + row, a.Sq - 1), jc);
+              ok = ok && !(mv <= kMaskedSentinel);
+              x = __builtin_fmaf(mv, kLog2e, x);
             }
-            const float p = __builtin_amdgcn_exp2f(x);
-            float dpv = dp[r];
-            float pm = p;
-            if constexpr (DROP) {
-              const float mm = drop_keep(sRK[stage][row0 + e], jl, a.drop_thr) ? a.drop_inv : 0.f;
-              dpv *= mm;
-              pm = p * mm;
-            }
-            pmc[r >> 3][r & 7] = (__bf16)pm;
-            dsc[r >> 3][r & 7] = (__bf16)(p * (dpv - d4[e]));
+            x = ok ? x : -__builtin_inff();
           }
-        }
-      };
-      // dV^T += dO^T (P.M) and dK^T += Q^T dS over the m-th half's 32 queries.
-      auto mma_dkdv = [&](int m, const bf16x8 (&pmc)[2], const bf16x8 (&dsc)[2]) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int rb = (32 * m + 16 * t) * D;
-#pragma unroll
-          for (int d = 0; d < DB; ++d) {
-            const bf16x8 ao = concat(lds_read_tr(tg + tr_lo[d] + rb), lds_read_tr(tg + tr_hi[d] + rb));
-            M::run(accv[d], ao, pmc[t]);
-            const bf16x8 aq = concat(lds_read_tr(tq + tr_lo[d] + rb), lds_read_tr(tq + tr_hi[d] + rb));
-            M::run(acck[d], aq, dsc[t]);
+          const float pr = __builtin_amdgcn_exp2f(x);
+          if constexpr (DROP) {
+            const float mm = drop_keep(sRK[lste][row], jl, a.drop_thr) ? a.drop_inv : 0.f;
+            pv[r] = pr * mm;
+            dv[r] = pr * (dpe[r] * mm - dl[r >> 2][r & 3]);
+          } else {
+            pv[r] = pr;
+            dv[r] = pr * dpe[r];
           }
+          if (r & 1) {
+            pmc[r >> 3][(r & 7) - 1] = (__bf16)pv[r - 1];
+            pmc[r >> 3][r & 7] = (__bf16)pv[r];
+            dsc[r >> 3][(r & 7) - 1] = (__bf16)dv[r - 1];
+            dsc[r >> 3][r & 7] = (__bf16)dv[r];
+          }
+        };
+        fence();
+#pragma unroll
+        for (int k = 0; k < NSD; ++k) {
+          const bf16x8& o = op[k & 7];
+          if (k & 1) {
+            if (k == 1 && FOLD)
+              mfma_v_init(dp, o, vr[k >> 1]);
+            else if (k == 1)
+              mfma_v0(dp, o, vr[k >> 1]);
+            else
+              mfma_v(dp, o, vr[k >> 1]);
+          } else {
+            if (k == 0)
+              mfma_v0(s, o, kr[k >> 1]);
+            else
+              mfma_v(s, o, kr[k >> 1]);
+          }
+          if (k + PF < NSD) op[(k + PF) & 7] = rd_op(ms, sts, k + PF);
+          if (k >= NSD - 2 * NP) trp[k - (NSD - 2 * NP)] = rd_tr(me, ste, k - (NSD - 2 * NP));
+          // elements [e0, e0 + ne) in slot k
+          int e0, ne;
+          if constexpr (NSD == 16) {
+            e0 = k < 2 ? 0 : (k < 14 ? k - 2 : 12 + 2 * (k - 14));
+            ne = k < 2 ? 0 : (k < 14 ? 1 : 2);
+          } else {
+            e0 = k < 1 ? 0 : 2 * (k - 1);
+            ne = k < 1 ? 0 : (k < 7 ? 2 : 4);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i < ne) ew_elem(e0 + i);
+          slot_extra(k);
+          fence();
         }
+        // The packed P/dS are complete here, and S/dP (and P/dS, 24 wait states
+        // later) may be read by anything once the drain has passed.
+        materialise(pmc, dsc);
+        mfma_drain(s, dp);
+        fence();
       };
-      auto tile = [&](auto full_c) {
-        f32x16 s0, dp0, s1, dp1;
-        bf16x8 pm0[2], ds0[2], pm1[2], ds1[2];
-        mma_sdp(0, s0, dp0);
-        mma_sdp(1, s1, dp1);
-        elementwise(full_c, 0, s0, dp0, pm0, ds0);
-        mma_dkdv(0, pm0, ds0);
-        elementwise(full_c, 1, s1, dp1, pm1, ds1);
-        mma_dkdv(1, pm1, ds1);
+      // Section "dV/dK" of half m (stage stq): MFMAs 0 .. NP-1 take the transposed
+      // operands read by the previous section; slot n reads those of MFMA n + NP.
+      auto sec_dkv = [&](int m, int stq, const bf16x4 (&trp)[2 * NP], const bf16x8 (&pmc)[2], const bf16x8 (&dsc)[2],
+                         auto&& slot_extra) {
+        constexpr int W = NP + 1;  // operand pairs in flight
+        bf16x4 buf[2 * W];
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+          buf[2 * n] = trp[2 * n];
+          buf[2 * n + 1] = trp[2 * n + 1];
+        }
+#pragma unroll
+        for (int n = 0; n < NDK; ++n) {
+          const int sl = n % W;
+          mma_dkv(n, buf[2 * sl], buf[2 * sl + 1], pmc, dsc);
+          if (n + NP < NDK) {
+            const int sn = (n + NP) % W;
+            buf[2 * sn] = rd_tr(m, stq, 2 * (n + NP));
+            buf[2 * sn + 1] = rd_tr(m, stq, 2 * (n + NP) + 1);
+          }
+          slot_extra(n);
+          fence();
+        }
       };
 
-      tile(std::integral_constant<bool, KIND == 2>{});
+      // Prologue: L/Delta of tiles 0-3, Q/dO of tiles 0-2; all landed; L/Delta
+      // of tiles 0 and 1 fixed (steps 0 and 1 fix those of tiles 2 and 3).
+      Cursor cq{0, 0}, cl{0, 0};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        issue_ld(cl, s);
+        advance(cl);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      store_rk(stage2);
-      advance();
-      st = stage1;
-      wait_vmcnt<2 * NIW>();  // tile it+1 and the L/Delta of tile it+2 landed; its rows may still be in flight
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        issue_qdo(cq, s);
+        advance(cq);
+      }
+      // A tile's copies go out over four sections: the first half in sections C
+      // and D of one step, the second half in sections A and B of the next (the
+      // vector-memory unit takes a copy per ~16 cycles per CU, so a burst of them
+      // would hold up the issuing wave).  Tile 2: first half now.
+      Job pend = job_of(cq, 2);
+#pragma unroll
+      for (int u = 0; u < NC / 2; ++u) issue_job(pend, u);
+      advance(cq);
+      wait_vmcnt<0>();
+      fix_ld(0);
+      fix_ld(1);
       barrier_lds();
-    };
 
-    const std::integral_constant<int, 0> kSkip;
-    const std::integral_constant<int, 1> kEdge;
-    const std::integral_constant<int, 2> kInner;
-    for (int g = 0; g < a.group; ++g) {
-      // This wave's tiles of head g, in order: [0,v0) invisible, [v0,f0) boundary,
-      // [f0,f1) interior, [f1,v1) boundary, [v1,ntq) invisible (the visible key
-      // interval moves monotonically with the query row, so the classes are contiguous).
-      auto none = [&](int t) { return rect_none_visible(a, qb + t * BQ, qb + t * BQ + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1); };
-      auto all = [&](int t) { return rect_all_visible(a, qb + t * BQ, qb + t * BQ + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1); };
-      int v0 = 0;
-      while (v0 < ntq && none(v0)) ++v0;
-      int v1 = v0;
-      while (v1 < ntq && !none(v1)) ++v1;
-      int f0 = v1, f1 = v1;
-      if constexpr (!MASK && !DROP) {
-        f0 = v0;
-        while (f0 < v1 && !all(f0)) ++f0;
-        f1 = f0;
-        while (f1 < v1 && all(f1)) ++f1;
+      // S/dP of half 0 of the current tile, carried between steps.
+      f32x16 s0, dp0;
+      {
+        bf16x8 pm[2], ds[2];
+        bf16x4 trp[2 * NP];
+        f32x16 z{};
+        // a section with no exp/dS work to overlap: only its S/dP result is kept
+        sec_sdp_ew(std::true_type{}, 0, 0, 0, s0, dp0, 0, 0, 0, qb, 0, z, z, pm, ds, trp, [](int) {});  // nothing to copy
       }
-      int t = 0;
-      for (; t < v0; ++t) step(kSkip, g, t);
-      for (; t < f0; ++t) step(kEdge, g, t);
-      for (; t < f1; ++t) step(kInner, g, t);
-      for (; t < v1; ++t) step(kEdge, g, t);
-      for (; t < ntq; ++t) step(kSkip, g, t);
+
+      int it = 0;
+      // One step (see the header comment).  KIND 1 = boundary tile (per-element
+      // predicate), 2 = interior tile (every element counted); each kind runs in a
+      // loop of its own, so no loop body branches.
+      auto step = [&](auto kind_c, int g, int t) {
+        constexpr bool FULL = decltype(kind_c)::value == 2;
+        const std::integral_constant<bool, FULL> full_c;
+        const int stq = it & (NST - 1);
+        const int stq1 = (it + 1) & (NST - 1);
+        const int stq3 = (it + 3) & (NST - 1);
+        const int lst = it & (NSL - 1);
+        const int lst1 = (it + 1) & (NSL - 1);
+        const int lst2 = (it + 2) & (NSL - 1);
+        const int lst4 = (it + 4) & (NSL - 1);
+        const int qt = qb + t * BQ;
+        const int h = kvh * a.group + g;
+        bf16x8 pm[2], ds[2];
+        bf16x4 trp[2 * NP];
+        f32x16 s1, dp1;
+        // A: S/dP of half 1 with exp/dS of half 0
+        sec_sdp_ew(full_c, 1, stq, lst, s1, dp1, 0, stq, lst, qt, h, s0, dp0, pm, ds, trp,
+                   [&](int k) { copies_at(pend, NC / 2, k, NSD); });
+        // B: dV/dK of half 0
+        sec_dkv(0, stq, trp, pm, ds, [&](int n) { copies_at(pend, NC / 2 + PER, n, NDK); });
+        wait_prev();  // tile it+1 landed everywhere once all waves pass the barrier
+        barrier_lds();
+        issue_ld(cl, lst4);
+        advance(cl);
+        fix_ld(lst2);
+        fence();
+        // C: S/dP of half 0 of tile it+1 with exp/dS of half 1; the copies of
+        // tile it+3 go out one every NSD/(2*NIW) slots
+        const Job next = job_of(cq, stq3);
+        sec_sdp_ew(full_c, 0, stq1, lst1, s0, dp0, 1, stq, lst, qt, h, s1, dp1, pm, ds, trp,
+                   [&](int k) { copies_at(next, 0, k, NSD); });
+        // D: dV/dK of half 1
+        sec_dkv(1, stq, trp, pm, ds, [&](int n) { copies_at(next, PER, n, NDK); });
+        pend = next;
+        advance(cq);
+        ++it;
+      };
+
+      const std::integral_constant<int, 1> kEdge;
+      const std::integral_constant<int, 2> kInner;
+      for (int g = 0; g < a.group; ++g) {
+        // This wave's tiles of head g: [0,f0) boundary, [f0,f1) interior,
+        // [f1,ntq) boundary (the visible key interval moves monotonically with
+        // the query row, so the interior tiles are contiguous).  Boundary tiles
+        // include tiles this wave cannot see at all; the predicate zeroes them.
+        auto all = [&](int t) { return rect_all_visible(a, qb + t * BQ, qb + t * BQ + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1); };
+        int f0 = ntq, f1 = ntq;
+        if constexpr (!MASK) {
+          f0 = 0;
+          while (f0 < ntq && !all(f0)) ++f0;
+          f1 = f0;
+          while (f1 < ntq && all(f1)) ++f1;
+        }
+        int t = 0;
+        for (; t < f0; ++t) step(kEdge, g, t);
+        for (; t < f1; ++t) step(kInner, g, t);
+        for (; t < ntq; ++t) step(kEdge, g, t);
+      }
+      wait_vmcnt<0>();  // the repeated copies of the last steps have landed
+      barrier_lds();    // every wave is done with the ring before the next pass refills it
     }
-    wait_vmcnt<0>();  // the repeated copies of the last steps have landed
+    mfma_drain_acc(acck, accv);  // the accumulators' last MFMAs have finished before they are read
 
     if (jl < a.Sk) {
 #pragma unroll

@@ -93,6 +93,67 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// v_mfma_f32_32x32x16_bf16 as inline assembly, with the register file of each
+// operand fixed: the accumulators of long sums (dK, dV) and the stationary B
+// operands (K, V rows) live in accumulation registers (AGPRs), the short-lived
+// results (S, dP) and the streamed A operands in VGPRs.  The compiler's hazard
+// tracking does not see inside the asm, so callers keep these rules:
+//  * a result is read by anything other than the next MFMA of its own chain
+//    (same accumulator, which the hardware forwards) only after mfma_drain();
+//  * a VGPR written by VALU is read as an operand only after two wait states
+//    (mfma_v_init has them; B operands packed by VALU are separated from their
+//    MFMAs by an mfma_drain());
+//  * no VALU writes a register that an MFMA in flight reads as accumulator
+//    (accumulators are written only by MFMAs).
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {  // acc (AGPR) += a b
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_v0(f32x16& c, const bf16x8& a, const bf16x8& b) {  // c = a b, b in AGPRs
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mfma_v(f32x16& c, const bf16x8& a, const bf16x8& b) {  // c += a b, b in AGPRs
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+// The first MFMA of a chain whose starting value was just written into c.
+__device__ __forceinline__ void mfma_v_init(f32x16& c, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+
+// 16-byte global load straight into accumulation registers (the home of the
+// stationary B operands), as inline assembly: the compiler neither copies the
+// value between register files nor waits for it; the caller waits with
+// wait_vmcnt before the first MFMA that reads it.
+__device__ __forceinline__ bf16x8 ld16_agpr(const void* p) {
+  bf16x8 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(v) : "v"(p) : "memory");
+  return v;
+}
+
+// Wait states after the last MFMA of a group before its results are read by
+// other instructions (an XDL result read by VALU, LDS or memory instructions).
+// The results pass through the asm, so no read of them can be placed before it.
+__device__ __forceinline__ void mfma_drain(f32x16& x, f32x16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
+template <int N>
+__device__ __forceinline__ void mfma_drain_acc(f32x16 (&x)[N], f32x16 (&y)[N]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(x[i]), "+a"(y[i]));
+}
+// Values computed by VALU are materialised here: no instruction selection may
+// sink their computation past this point (next to the MFMA that reads them).
+__device__ __forceinline__ void materialise(bf16x8 (&x)[2], bf16x8 (&y)[2]) {
+  asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(y[0]), "+v"(y[1]));
+}
+
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgValu = 0x002 | 0x400;  // VALU incl. transcendental
+constexpr int kSgSalu = 0x004;
+constexpr int kSgMfma = 0x008;
+constexpr int kSgDsRead = 0x100;
+constexpr int kSgDsWrite = 0x200;
+
 // Per-lane element offset, relative to a 16-row block, of the transposed read
 // that gives lane l column 32*db + l%32 and rows rb + 4*(l/32) + 0..3 of the
 // block (rb = 0 for the first half of an MFMA operand, 8 for the second).
