@@ -33,18 +33,11 @@ SOURCES = [
 
 ARCH = "gfx950"
 
-# The MFMA tile kernels run one wave per SIMD by design, so they are scheduled
-# for instruction-level parallelism (LDS reads issued ahead of their MFMAs,
-# VALU interleaved with MFMAs) rather than for minimum register pressure.  The
-# dQ kernel also asks for the VGPR form of MFMA: S and dP then come out in the
-# registers the exp/dS arithmetic reads, and the compiler moves only the dQ
-# accumulators into accumulation registers.
-ILP = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
-VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA_FLAGS = {
-    "fa_dkdv_bf16.hip": VGPR_FORM,
-    "fa_dq_bf16.hip": ILP + VGPR_FORM,
-}
+# Per-file extra flags (none at present: the bf16 tile kernels fix their own
+# instruction order with scheduling fences and issue their MFMAs as inline
+# assembly, so the compiler's scheduling strategy and MFMA register form do
+# not shape them).
+EXTRA_FLAGS: dict = {}
 
 COMMON_FLAGS = [
     "-O3",

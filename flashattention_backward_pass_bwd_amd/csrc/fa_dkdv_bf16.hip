@@ -244,36 +244,58 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           mfma_acc(accv[d], concat(lo, hi), pmc[t]);
       };
 
-      // Section "S/dP + exp/dS": S/dP of half ms from stage sts (with FOLD the dP
-      // chain starts from the rows' -Delta, L ring stage lsts), overlapped with the
-      // exp/dS of half me of tile (qt, h) (values se, dpe; L ring stage lste) and
-      // with the transposed reads of the first NP MFMAs of that half's dV/dK (stage ste).
-      // Operand reads run PF MFMAs ahead; the 16 exp/dS elements are spread over
-      // the slots after the first (which wait for the L/Delta reads).
-      auto sec_sdp_ew = [&](auto full_c, int ms, int sts, int lsts, f32x16& s, f32x16& dp, int me, int ste,
-                            int lste, int qt, int h, const f32x16& se, const f32x16& dpe, bf16x8 (&pmc)[2],
-                            bf16x8 (&dsc)[2], bf16x4 (&trp)[2 * NP], auto&& slot_extra) {
-        constexpr bool FULL = decltype(full_c)::value;
-        constexpr int PF = 6;
-        bf16x8 op[8];
+      // What an S/dP + exp/dS section needs first, read by the section before it:
+      // the A operands of its first PF MFMAs, the -Delta rows its dP chain starts
+      // from (FOLD), and the -L*log2(e) (and Delta) rows of the exp/dS half.
+      constexpr int PF = 6;
+      struct SdpPre {
+        bf16x8 op[PF];
+        f32x16 dpi;
         f32x4 nl[4], dl[4];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          nl[r4] = *reinterpret_cast<const f32x4*>(&sL[lste][32 * me + 8 * r4 + 4 * h2]);
-          if constexpr (!FOLD) dl[r4] = *reinterpret_cast<const f32x4*>(&sDel[lste][32 * me + 8 * r4 + 4 * h2]);
+      };
+      constexpr int NPRE = PF + (FOLD ? 4 : 0) + (FOLD ? 4 : 8);  // LDS reads of a prefetch
+      // Prefetch read p (0 .. NPRE-1) for a section computing S/dP of half ms
+      // (stage sts, L ring stage lsts) and exp/dS of half me (L ring stage lste).
+      auto prefetch = [&](SdpPre& pre, int p, int ms, int sts, int lsts, int me, int lste) {
+        if (p < PF) {
+          pre.op[p] = rd_op(ms, sts, p);
+          return;
         }
-        op[0] = rd_op(ms, sts, 0);
-        op[1] = rd_op(ms, sts, 1);
+        p -= PF;
         if constexpr (FOLD) {
+          if (p < 4) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[lsts][32 * ms + 8 * p + 4 * h2]);
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[lsts][32 * ms + 8 * r4 + 4 * h2]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dp[4 * r4 + e] = d4[e];
+            for (int e = 0; e < 4; ++e) pre.dpi[4 * p + e] = d4[e];
+            return;
           }
+          p -= 4;
         }
+        if (p < 4) {
+          pre.nl[p] = *reinterpret_cast<const f32x4*>(&sL[lste][32 * me + 8 * p + 4 * h2]);
+          return;
+        }
+        p -= 4;
+        if constexpr (!FOLD) pre.dl[p] = *reinterpret_cast<const f32x4*>(&sDel[lste][32 * me + 8 * p + 4 * h2]);
+      };
+      auto prefetch_all = [&](SdpPre& pre, int ms, int sts, int lsts, int me, int lste) {
 #pragma unroll
-        for (int k = 2; k < PF; ++k) op[k] = rd_op(ms, sts, k);
+        for (int p = 0; p < NPRE; ++p) prefetch(pre, p, ms, sts, lsts, me, lste);
+      };
+
+      // Section "S/dP + exp/dS": S/dP of half ms from stage sts (with FOLD the dP
+      // chain starts from the rows' -Delta), overlapped with the exp/dS of half me
+      // of tile (qt, h) (values se, dpe; L ring stage lste) and with the transposed
+      // reads of the first NP MFMAs of that half's dV/dK (stage ste).  Operand
+      // reads run PF MFMAs ahead; the 16 exp/dS elements are spread over the slots.
+      auto sec_sdp_ew = [&](auto full_c, int ms, int sts, f32x16& s, f32x16& dp, const SdpPre& pre, int me,
+                            int ste, int lste, int qt, int h, const f32x16& se, const f32x16& dpe,
+                            bf16x8 (&pmc)[2], bf16x8 (&dsc)[2], bf16x4 (&trp)[2 * NP], auto&& slot_extra) {
+        constexpr bool FULL = decltype(full_c)::value;
+        bf16x8 op[8];
+#pragma unroll
+        for (int k = 0; k < PF; ++k) op[k] = pre.op[k];
+        if constexpr (FOLD) dp = pre.dpi;
         const int dl0 = jl - qt;  // d = j - i = dl0 - row
         const int rlim = a.Sq - qt;
         const bool jin = jl < a.Sk;
@@ -282,7 +304,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         // exp/dS of element r (C-layout register r of half me); odd r packs the pair.
         auto ew_elem = [&](int r) {
           const int row = 32 * me + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          float x = __builtin_fmaf(se[r], a.scale_log2, nl[r >> 2][r & 3]);
+          float x = __builtin_fmaf(se[r], a.scale_log2, pre.nl[r >> 2][r & 3]);
           if constexpr (!FULL) {
             const int dd = dl0 - row;
             bool ok = jin && row < rlim && dd > vb.dlo && dd < vb.dhi;
@@ -298,7 +320,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           if constexpr (DROP) {
             const float mm = drop_keep(sRK[lste][row], jl, a.drop_thr) ? a.drop_inv : 0.f;
             pv[r] = pr * mm;
-            dv[r] = pr * (dpe[r] * mm - dl[r >> 2][r & 3]);
+            dv[r] = pr * (dpe[r] * mm - pre.dl[r >> 2][r & 3]);
           } else {
             pv[r] = pr;
             dv[r] = pr * dpe[r];
@@ -332,14 +354,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           // elements [e0, e0 + ne) in slot k
           int e0, ne;
           if constexpr (NSD == 16) {
-            e0 = k < 2 ? 0 : (k < 14 ? k - 2 : 12 + 2 * (k - 14));
-            ne = k < 2 ? 0 : (k < 14 ? 1 : 2);
+            e0 = k;
+            ne = 1;
           } else {
-            e0 = k < 1 ? 0 : 2 * (k - 1);
-            ne = k < 1 ? 0 : (k < 7 ? 2 : 4);
+            e0 = 2 * k;
+            ne = 2;
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
+          for (int i = 0; i < 2; ++i)
             if (i < ne) ew_elem(e0 + i);
           slot_extra(k);
           fence();
@@ -375,8 +397,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         }
       };
 
-      // Prologue: L/Delta of tiles 0-3, Q/dO of tiles 0-2; all landed; L/Delta
-      // of tiles 0 and 1 fixed (steps 0 and 1 fix those of tiles 2 and 3).
+      // Prologue: L/Delta of tiles 0-3, Q/dO of tiles 0 and 1 and most of tile 2's
+      // copies; all landed; L/Delta of tiles 0 and 1 fixed (steps 0 and 1
+      // fix those of tiles 2 and 3).
       Cursor cq{0, 0}, cl{0, 0};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -388,27 +411,31 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         issue_qdo(cq, s);
         advance(cq);
       }
-      // A tile's copies go out over four sections: the first half in sections C
-      // and D of one step, the second half in sections A and B of the next (the
+      // A tile's copies go out over four sections, from the barrier on (the
       // vector-memory unit takes a copy per ~16 cycles per CU, so a burst of them
-      // would hold up the issuing wave).  Tile 2: first half now.
+      // would hold up the issuing wave): a quarter each in sections B, C and D of
+      // one step and in A of the next.  Tile 2: its first three quarters now.
       Job pend = job_of(cq, 2);
 #pragma unroll
-      for (int u = 0; u < NC / 2; ++u) issue_job(pend, u);
+      for (int u = 0; u < NC - PER; ++u) issue_job(pend, u);
       advance(cq);
       wait_vmcnt<0>();
       fix_ld(0);
       fix_ld(1);
       barrier_lds();
 
-      // S/dP of half 0 of the current tile, carried between steps.
+      // S/dP of half 0 of the current tile, carried between steps, and the
+      // prefetch of the next S/dP + exp/dS section.
       f32x16 s0, dp0;
+      SdpPre pre;
       {
         bf16x8 pm[2], ds[2];
         bf16x4 trp[2 * NP];
         f32x16 z{};
+        prefetch_all(pre, 0, 0, 0, 0, 0);
         // a section with no exp/dS work to overlap: only its S/dP result is kept
-        sec_sdp_ew(std::true_type{}, 0, 0, 0, s0, dp0, 0, 0, 0, qb, 0, z, z, pm, ds, trp, [](int) {});  // nothing to copy
+        sec_sdp_ew(std::true_type{}, 0, 0, s0, dp0, pre, 0, 0, 0, qb, 0, z, z, pm, ds, trp, [](int) {});
+        prefetch_all(pre, 1, 0, 0, 0, 0);  // for section A of step 0
       }
 
       int it = 0;
@@ -430,24 +457,38 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         bf16x8 pm[2], ds[2];
         bf16x4 trp[2 * NP];
         f32x16 s1, dp1;
-        // A: S/dP of half 1 with exp/dS of half 0
-        sec_sdp_ew(full_c, 1, stq, lst, s1, dp1, 0, stq, lst, qt, h, s0, dp0, pm, ds, trp,
-                   [&](int k) { copies_at(pend, NC / 2, k, NSD); });
-        // B: dV/dK of half 0
-        sec_dkv(0, stq, trp, pm, ds, [&](int n) { copies_at(pend, NC / 2 + PER, n, NDK); });
+        // Prefetch read p goes into slot pre_slot(p) of a dV/dK section (the last
+        // NPRE slots, or spread over all of them when there are fewer).
+        auto pre_at = [&](int n, int ms, int sts, int lsts, int me, int lste) {
+#pragma unroll
+          for (int p = 0; p < NPRE; ++p) {
+            const int slot = NPRE <= NDK ? NDK - NPRE + p : p * NDK / NPRE;
+            if (slot == n) prefetch(pre, p, ms, sts, lsts, me, lste);
+          }
+        };
+        // A: S/dP of half 1 with exp/dS of half 0; the second half of tile it+2's copies
+        sec_sdp_ew(full_c, 1, stq, s1, dp1, pre, 0, stq, lst, qt, h, s0, dp0, pm, ds, trp,
+                   [&](int k) { copies_at(pend, NC / 2 + PER, k, NSD); });
         wait_prev();  // tile it+1 landed everywhere once all waves pass the barrier
         barrier_lds();
         issue_ld(cl, lst4);
         advance(cl);
         fix_ld(lst2);
         fence();
-        // C: S/dP of half 0 of tile it+1 with exp/dS of half 1; the copies of
-        // tile it+3 go out one every NSD/(2*NIW) slots
         const Job next = job_of(cq, stq3);
-        sec_sdp_ew(full_c, 0, stq1, lst1, s0, dp0, 1, stq, lst, qt, h, s1, dp1, pm, ds, trp,
-                   [&](int k) { copies_at(next, 0, k, NSD); });
-        // D: dV/dK of half 1
-        sec_dkv(1, stq, trp, pm, ds, [&](int n) { copies_at(next, PER, n, NDK); });
+        // B: dV/dK of half 0; prefetch for C (S/dP of half 0 of tile it+1, exp/dS of half 1)
+        sec_dkv(0, stq, trp, pm, ds, [&](int n) {
+          copies_at(next, 0, n, NDK);
+          pre_at(n, 0, stq1, lst1, 1, lst);
+        });
+        // C: S/dP of half 0 of tile it+1 with exp/dS of half 1
+        sec_sdp_ew(full_c, 0, stq1, s0, dp0, pre, 1, stq, lst, qt, h, s1, dp1, pm, ds, trp,
+                   [&](int k) { copies_at(next, PER, k, NSD); });
+        // D: dV/dK of half 1; prefetch for A of the next step
+        sec_dkv(1, stq, trp, pm, ds, [&](int n) {
+          copies_at(next, 2 * PER, n, NDK);
+          pre_at(n, 1, stq1, lst1, 0, lst1);
+        });
         pend = next;
         advance(cq);
         ++it;

@@ -3,15 +3,26 @@
 // flash_attention_v2_backward.wgsl, flash_bwd_dq second sweep, L supplied):
 //   dQ_i = scale * sum_j dS_ij K_j,  dS_ij = P_ij (M_ij dO_i.V_j - Delta_i).
 //
-// Block: 4 waves own 128 consecutive query rows of one (b, h); wave w keeps
-// its 32 rows of Q and dO in registers as MFMA B operands and accumulates
-// dQ^T (D x 32 fp32).  K and V tiles of 64 keys live in a 3-stage LDS ring
-// (swizzled, see fa_tiles.h) filled by direct global->LDS copies issued two
-// tiles ahead; one fence-free barrier per tile.  S^T = K Q^T and dP^T = V dO^T read row-major
-// operands; dQ^T += K^T dS^T reads K transposed through ds_read_b64_tr_b16.
-// S^T has one query per lane column, so L_i and Delta_i are per-lane scalars
-// (without dropout the dP^T chain starts from -Delta_i, so dP - Delta comes
-// out of the MFMAs) and dS^T is already the B operand of the last contraction.  Blocks of the
+// Block: 4 waves own 128 consecutive query rows of one (b, h); wave w keeps its
+// 32 rows of Q and dO in accumulation registers as MFMA B operands
+// (v_mfma_f32_32x32x16_bf16) and accumulates dQ^T (D x 32 fp32) there too.
+// Per 64-key tile and wave: S^T = K Q^T and dP^T = V dO^T (row-major A
+// operands from LDS), P and dS^T in registers, then dQ^T += K^T dS^T (K
+// transposed through ds_read_b64_tr_b16).  S^T has one query per lane column,
+// so L_i and Delta_i are per-lane scalars (without dropout the dP^T chain
+// starts from -Delta_i, so dP - Delta comes out of the MFMAs) and dS^T is
+// already the B operand of the last contraction.
+//
+// Software pipeline, as in the dK/dV kernel: a tile is two 32-key halves and
+// the step of tile it runs
+//   A: S/dP of half 1 (MFMA)      with  exp/dS of half 0 (VALU)
+//      -- wait for tile it+1's copies, block barrier --
+//   B: dQ of half 0
+//   C: S/dP of half 0 of tile it+1 with exp/dS of half 1
+//   D: dQ of half 1
+// with every section's first operands read by the section before it.  K and V
+// tiles live in a 4-stage LDS ring (swizzled, see fa_tiles.h) filled by direct
+// global->LDS copies three tiles ahead, spread over the step.  Blocks of the
 // query heads sharing a KV head are dealt to one XCD; for causal attention
 // without a window, block i also takes query block nqb-1-i.
 #include <type_traits>
@@ -29,18 +40,26 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
                                                          const float* __restrict__ L,
                                                          const float* __restrict__ Dl,
                                                          __bf16* __restrict__ dQ, int nqb, int paired) {
-  using M = Mma<__bf16>;
   constexpr int BK = 64;
   constexpr int NCH = D / 8;
   constexpr int KS = D / 16;
   constexpr int DB = D / 32;
-  constexpr int NST = 3;                    // LDS ring stages
+  constexpr int NST = 4;                    // K/V ring stages
   constexpr int RPI = 1024 / (2 * D);       // tile rows per 1 KB global->LDS copy
   constexpr int NIW = BK / RPI / 4;         // copies per wave per tile per tensor
   constexpr int TILE = BK * D;
+  constexpr bool FOLD = !DROP;              // dP chain seeded with -Delta
+  constexpr int NSD = 2 * KS;               // S/dP MFMAs per 32-key half
+  constexpr int NDQ = 2 * DB;               // dQ MFMAs per 32-key half
+  constexpr int NP = NDQ / 2;               // dQ MFMAs whose operands the preceding section reads
+  constexpr int PF = NDQ < 6 ? NDQ : 6;     // S/dP operand reads in flight
+  constexpr int NC = 2 * NIW;               // copies per tile per wave
+  constexpr int PER = NC / 4;               // copies per section
+  static_assert(NC % 4 == 0 && NDQ % PER == 0 && NSD % PER == 0, "a tile's copies spread over four sections");
+  static_assert(2 * NP <= NSD && PF <= NSD && PF <= NDQ, "prefetches fit their sections");
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[NST][TILE];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[NST][TILE];
+  // Ring stage s holds the K tile (sT[s][0]) and the V tile (sT[s][1]).
+  __shared__ __attribute__((aligned(16))) __bf16 sT[NST][2][TILE];
 
   const int nbh = a.B * a.Hq;
   const int wi = blockIdx.x / nbh;
@@ -81,165 +100,264 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
     const int qw0 = q0 + wave * kDqRowsPerWave;
     const int il = qw0 + l32;
 
+    // Q and dO rows of this wave's queries, straight into accumulation registers
+    // (rows past the end repeat the last row; their results are not written).
     bf16x8 qr[KS], gr[KS];
     const int64_t qoff = (int64_t)b * a.qsb + (int64_t)il * a.qss + (int64_t)h * a.qsh;
+    const int64_t qclamp = (int64_t)b * a.qsb + (int64_t)min(il, a.Sq - 1) * a.qss + (int64_t)h * a.qsh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      qr[s] = bf16x8{};
-      gr[s] = bf16x8{};
-      if (il < a.Sq) {
-        qr[s] = *reinterpret_cast<const bf16x8*>(Q + qoff + 16 * s + 8 * h2);
-        gr[s] = *reinterpret_cast<const bf16x8*>(dO + qoff + 16 * s + 8 * h2);
-      }
+      qr[s] = ld16_agpr(Q + qclamp + 16 * s + 8 * h2);
+      gr[s] = ld16_agpr(dO + qclamp + 16 * s + 8 * h2);
     }
-    const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq + il;
-    const float l2 = il < a.Sq ? L[lrow] * kLog2e : __builtin_inff();
+    const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq + min(il, a.Sq - 1);
+    const float nl = il < a.Sq ? -L[lrow] * kLog2e : -__builtin_inff();
     const float del = il < a.Sq ? Dl[lrow] : 0.f;
     uint32_t rk = 0;
     if constexpr (DROP) rk = drop_row_key(a, b, h, il);
-    wait_all_vmem();  // Q, dO rows, L and Delta are in registers before the copy ring starts
-
-    // Without dropout dP - Delta comes straight out of the MFMA chain: it starts from -Delta.
-    f32x16 dp_init;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dp_init[r] = DROP ? 0.f : -del;
     f32x16 accq[DB];
 #pragma unroll
     for (int d = 0; d < DB; ++d) accq[d] = f32x16{};
+    wait_all_vmem();  // Q, dO rows, L and Delta are in registers before the copy ring starts
 
     int kb, ke;
     key_range(a, q0, min(q0 + kDqRowsPerBlock, a.Sq) - 1, kb, ke);
     const int ntiles = (ke - kb + BK - 1) / BK;
 
-    // Copy u of this wave fills key rows (wave*NIW + u)*RPI + lane/NCH of a tile.
-    // Rows past the end repeat the last key; they are never counted.  Per-lane
-    // offsets are 32-bit, relative to the tile's first key (the host bounds the
-    // row stride).
-    auto issue_tile = [&](int it, int stage) {
-      const int kt = kb + it * BK;
-      const int lim = a.Sk - 1 - kt;
-      const int64_t base = (int64_t)b * a.ksb + (int64_t)kt * a.kss + (int64_t)kvh * a.ksh;
+    if (ntiles > 0) {
+      // The dP^T chain starts from -Delta_i (every C register of a lane is row i).
+      f32x16 dpi;
 #pragma unroll
-      for (int u = 0; u < NIW; ++u) {
-        const int blk = wave * NIW + u;
+      for (int r = 0; r < 16; ++r) dpi[r] = FOLD ? -del : 0.f;
+
+      // K and V rows of tile tt (clamped to the last tile, so copies past the end
+      // repeat it into stages that are never read) into a ring stage: copy u
+      // (even: K, odd: V) of this wave fills rows (wave*NIW + u/2)*RPI + lane/NCH.
+      // Rows past the end repeat the last key; they are never counted.
+      struct Job {
+        int64_t base;
+        int lim, stage;
+      };
+      auto job_of = [&](int tt, int stage) {
+        const int kt = kb + min(tt, ntiles - 1) * BK;
+        return Job{(int64_t)b * a.ksb + (int64_t)kt * a.kss + (int64_t)kvh * a.ksh, a.Sk - 1 - kt, stage};
+      };
+      auto issue_job = [&](const Job& j, int u) {
+        const int blk = wave * NIW + (u >> 1);
         const int r = blk * RPI + cp_row;
-        const uint32_t off = 2u * ((uint32_t)min(r, lim) * (uint32_t)a.kss + 8u * (uint32_t)(cp_pc ^ swz<D>(r)));
-        dma16(K + base, off, lds_addr(&sK[stage][blk * RPI * D]));
-        dma16(V + base, off, lds_addr(&sV[stage][blk * RPI * D]));
-      }
-    };
+        const uint32_t off = 2u * ((uint32_t)min(r, j.lim) * (uint32_t)a.kss + 8u * (uint32_t)(cp_pc ^ swz<D>(r)));
+        if (u & 1)
+          dma16(V + j.base, off, lds_addr(&sT[j.stage][1][blk * RPI * D]));
+        else
+          dma16(K + j.base, off, lds_addr(&sT[j.stage][0][blk * RPI * D]));
+      };
+      // Slot hook: copies u0 .. u0+PER-1 of job j, one every nslots/PER slots.
+      auto copies_at = [&](const Job& j, int u0, int k, int nslots) {
+        if (k % (nslots / PER) == 0) issue_job(j, u0 + k / (nslots / PER));
+      };
 
-    if (ntiles > 0) issue_tile(0, 0);
-    if (ntiles > 1) {
-      issue_tile(1, 1);
-      wait_vmcnt<2 * NIW>();  // tile 0 landed; tile 1 may still be in flight
-    } else {
+      auto fence = []() { __builtin_amdgcn_sched_barrier(0); };
+      // Row-major A operand of S/dP MFMA k (even: K chunk k/2 for S^T, odd: V chunk for dP^T).
+      auto rd_op = [&](int m, int stq, int k) {
+        return lds_read_b128(sT[stq][0] + rd_off[k >> 1] + (k & 1) * TILE + 32 * m * D);
+      };
+      // Transposed A operand half j of dQ MFMA n = j/2 = DB*t + d of half m: K^T
+      // column block d over keys 32m + 16t .. +15; j even = first 8 keys, odd = last 8.
+      auto rd_tr = [&](int m, int stq, int j) {
+        const int n = j >> 1, t = n / DB, d = n % DB;
+        return lds_read_tr(sT[stq][0] + (32 * m + 16 * t) * D + ((j & 1) ? tr_hi[d] : tr_lo[d]));
+      };
+
+      // Section "S/dP + exp/dS": S^T/dP^T of half ms from stage sts (operands of
+      // its first PF MFMAs in pre), overlapped with the exp/dS of half me of key
+      // tile kt (values se, dpe) and with the transposed reads of the first NP
+      // MFMAs of that half's dQ (stage ste).
+      auto sec_sdp_ew = [&](auto full_c, int ms, int sts, f32x16& s, f32x16& dp, const bf16x8 (&pre)[PF], int me,
+                            int ste, int kt, const f32x16& se, const f32x16& dpe, bf16x8 (&dsc)[2],
+                            bf16x4 (&trp)[2 * NP], auto&& slot_extra) {
+        constexpr bool FULL = decltype(full_c)::value;
+        bf16x8 op[8];
+#pragma unroll
+        for (int k = 0; k < PF; ++k) op[k] = pre[k];
+        if constexpr (FOLD) dp = dpi;
+        const int dl0 = kt - il;  // d = j - i = dl0 + key
+        const int klim = a.Sk - kt;
+        const bool iin = il < a.Sq;
+        const int ic = min(il, a.Sq - 1);
+        float dv[16];
+        // exp/dS of element r (C-layout register r of half me: key 32me + 8(r/4) + 4h2 + r%4).
+        auto ew_elem = [&](int r) {
+          const int key = 32 * me + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          float x = __builtin_fmaf(se[r], a.scale_log2, nl);
+          if constexpr (!FULL) {
+            const int dd = dl0 + key;
+            bool ok = iin && key < klim && dd > vb.dlo && dd < vb.dhi;
+            if constexpr (MASK) {
+              // clamped indices keep the load in bounds; ok discards out-of-range elements
+              const float mv = mask_at(a, b, h, ic, min(kt + key, a.Sk - 1));
+              ok = ok && !(mv <= kMaskedSentinel);
+              x = __builtin_fmaf(mv, kLog2e, x);
+            }
+            x = ok ? x : -__builtin_inff();
+          }
+          const float pr = __builtin_amdgcn_exp2f(x);
+          if constexpr (DROP) {
+            const float mm = drop_keep(rk, kt + key, a.drop_thr) ? a.drop_inv : 0.f;
+            dv[r] = pr * (dpe[r] * mm - del);
+          } else {
+            dv[r] = pr * dpe[r];
+          }
+          if (r & 1) {
+            dsc[r >> 3][(r & 7) - 1] = (__bf16)dv[r - 1];
+            dsc[r >> 3][r & 7] = (__bf16)dv[r];
+          }
+        };
+        fence();
+#pragma unroll
+        for (int k = 0; k < NSD; ++k) {
+          const bf16x8& o = op[k & 7];
+          if (k & 1) {
+            if (k == 1 && FOLD)
+              mfma_v_init(dp, o, gr[k >> 1]);
+            else if (k == 1)
+              mfma_v0(dp, o, gr[k >> 1]);
+            else
+              mfma_v(dp, o, gr[k >> 1]);
+          } else {
+            if (k == 0)
+              mfma_v0(s, o, qr[k >> 1]);
+            else
+              mfma_v(s, o, qr[k >> 1]);
+          }
+          if (k + PF < NSD) op[(k + PF) & 7] = rd_op(ms, sts, k + PF);
+          if (k >= NSD - 2 * NP) trp[k - (NSD - 2 * NP)] = rd_tr(me, ste, k - (NSD - 2 * NP));
+          // 16 exp/dS elements over the NSD slots
+#pragma unroll
+          for (int i = 0; i < 16 / NSD; ++i) ew_elem(k * (16 / NSD) + i);
+          slot_extra(k);
+          fence();
+        }
+        // dS^T is complete here, and S/dP (and dS^T, 24 wait states later) may
+        // be read by anything once the drain has passed.
+        materialise(dsc);
+        mfma_drain(s, dp);
+        fence();
+      };
+      // Section "dQ" of half m (stage stq): MFMAs 0 .. NP-1 take the transposed
+      // operands read by the previous section; slot n reads those of MFMA n + NP.
+      auto sec_dq = [&](int m, int stq, const bf16x4 (&trp)[2 * NP], const bf16x8 (&dsc)[2], auto&& slot_extra) {
+        constexpr int W = NP + 1;  // operand pairs in flight
+        bf16x4 buf[2 * W];
+#pragma unroll
+        for (int n = 0; n < NP; ++n) {
+          buf[2 * n] = trp[2 * n];
+          buf[2 * n + 1] = trp[2 * n + 1];
+        }
+#pragma unroll
+        for (int n = 0; n < NDQ; ++n) {
+          const int sl = n % W;
+          mfma_acc(accq[n % DB], concat(buf[2 * sl], buf[2 * sl + 1]), dsc[n / DB]);
+          if (n + NP < NDQ) {
+            const int sn = (n + NP) % W;
+            buf[2 * sn] = rd_tr(m, stq, 2 * (n + NP));
+            buf[2 * sn + 1] = rd_tr(m, stq, 2 * (n + NP) + 1);
+          }
+          slot_extra(n);
+          fence();
+        }
+      };
+
+      // Prologue: K/V of tiles 0 and 1 and three quarters of tile 2's copies; all
+      // landed.  A tile's copies go out over four sections from the barrier on
+      // (a quarter each in B, C and D of one step and in A of the next).
+#pragma unroll
+      for (int u = 0; u < NC; ++u) issue_job(job_of(0, 0), u);
+#pragma unroll
+      for (int u = 0; u < NC; ++u) issue_job(job_of(1, 1), u);
+      Job pend = job_of(2, 2);
+#pragma unroll
+      for (int u = 0; u < NC - PER; ++u) issue_job(pend, u);
       wait_vmcnt<0>();
-    }
-    barrier_lds();
-
-    // One step: start the copies of tile it+2 while computing tile it.  KIND 0
-    // = no element visible to this wave, 1 = boundary tile (per-element
-    // predicate), 2 = interior tile; each kind runs in a loop of its own.
-    auto step = [&](auto kind_c, int it) {
-      constexpr int KIND = decltype(kind_c)::value;
-      const int stage = it % NST;
-      const bool has2 = it + 2 < ntiles;
-      if (has2) issue_tile(it + 2, (it + 2) % NST);
-      if constexpr (KIND != 0) {
-        const int kt = kb + it * BK;
-        const __bf16* tk = sK[stage];
-        const __bf16* tv = sV[stage];
-        // S^T (m-th 32-key half) = K Q^T and dP^T = V dO^T.
-        auto mma_sdp = [&](int m, f32x16& s, f32x16& dp) {
-          s = f32x16{};
-          dp = dp_init;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            M::run(s, lds_read_b128(tk + rd_off[ks] + 32 * m * D), qr[ks]);
-            M::run(dp, lds_read_b128(tv + rd_off[ks] + 32 * m * D), gr[ks]);
-          }
-        };
-        // P, dropout and dS for one half, packed into the bf16 B operands of dQ^T += K^T dS^T.
-        auto elementwise = [&](int m, const f32x16& s, const f32x16& dp, bf16x8 (&dsc)[2]) {
-          const int dl0 = kt - il;  // d = j - i = dl0 + row
-          const int rlim = a.Sk - kt;
-          const bool iin = il < a.Sq;
-          const int ic = min(il, a.Sq - 1);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float x = __builtin_fmaf(s[r], a.scale_log2, -l2);
-            float dpv = dp[r];
-            if constexpr (KIND == 1) {
-              const int row = 32 * m + 8 * (r / 4) + 4 * h2 + (r % 4);
-              const int dd = dl0 + row;
-              bool ok = iin && row < rlim && dd > vb.dlo && dd < vb.dhi;
-              if constexpr (MASK) {
-                // clamped indices keep the load in bounds; ok discards out-of-range elements
-                const float mv = mask_at(a, b, h, ic, min(kt + row, a.Sk - 1));
-                ok = ok && !(mv <= kMaskedSentinel);
-                x = __builtin_fmaf(mv, kLog2e, x);
-              }
-              x = ok ? x : -__builtin_inff();
-              if constexpr (DROP) dpv *= drop_keep(rk, kt + row, a.drop_thr) ? a.drop_inv : 0.f;
-            }
-            const float p = __builtin_amdgcn_exp2f(x);
-            if constexpr (DROP) dsc[r >> 3][r & 7] = (__bf16)(p * (dpv - del));
-            else dsc[r >> 3][r & 7] = (__bf16)(p * dpv);
-          }
-        };
-        auto mma_dq = [&](int m, const bf16x8 (&dsc)[2]) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int rb = (32 * m + 16 * t) * D;
-#pragma unroll
-            for (int d = 0; d < DB; ++d) {
-              const bf16x8 ak = concat(lds_read_tr(tk + tr_lo[d] + rb), lds_read_tr(tk + tr_hi[d] + rb));
-              M::run(accq[d], ak, dsc[t]);
-            }
-          }
-        };
-        f32x16 s0, dp0, s1, dp1;
-        bf16x8 ds0[2], ds1[2];
-        mma_sdp(0, s0, dp0);
-        mma_sdp(1, s1, dp1);
-        elementwise(0, s0, dp0, ds0);
-        mma_dq(0, ds0);
-        elementwise(1, s1, dp1, ds1);
-        mma_dq(1, ds1);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (has2)
-        wait_vmcnt<2 * NIW>();  // tile it+1 landed; tile it+2 may still be in flight
-      else
-        wait_vmcnt<0>();
       barrier_lds();
-    };
 
-    // This wave's key tiles in order: [0,v0) invisible, [v0,f0) boundary, [f0,f1)
-    // interior, [f1,v1) boundary, [v1,ntiles) invisible.
-    auto none = [&](int t) { return rect_none_visible(a, qw0, qw0 + kDqRowsPerWave - 1, kb + t * BK, kb + t * BK + BK - 1); };
-    auto all = [&](int t) { return rect_all_visible(a, qw0, qw0 + kDqRowsPerWave - 1, kb + t * BK, kb + t * BK + BK - 1); };
-    int v0 = 0;
-    while (v0 < ntiles && none(v0)) ++v0;
-    int v1 = v0;
-    while (v1 < ntiles && !none(v1)) ++v1;
-    int f0 = v1, f1 = v1;
-    if constexpr (!MASK && !DROP) {
-      f0 = v0;
-      while (f0 < v1 && !all(f0)) ++f0;
-      f1 = f0;
-      while (f1 < v1 && all(f1)) ++f1;
+      // S/dP of half 0 of the current tile, carried between steps, and the
+      // prefetched operands of the next S/dP section.
+      f32x16 s0, dp0;
+      bf16x8 pre[PF];
+      {
+        bf16x8 ds[2];
+        bf16x4 trp[2 * NP];
+        f32x16 z{};
+#pragma unroll
+        for (int k = 0; k < PF; ++k) pre[k] = rd_op(0, 0, k);
+        // a section with no exp/dS work to overlap: only its S/dP result is kept
+        sec_sdp_ew(std::true_type{}, 0, 0, s0, dp0, pre, 0, 0, kb, z, z, ds, trp, [](int) {});
+#pragma unroll
+        for (int k = 0; k < PF; ++k) pre[k] = rd_op(1, 0, k);
+      }
+
+      int it = 0;
+      // One step (see the header comment).  KIND 1 = boundary tile (per-element
+      // predicate), 2 = interior tile (every element counted); each kind runs in a
+      // loop of its own, so no loop body branches.
+      auto step = [&](auto kind_c) {
+        constexpr bool FULL = decltype(kind_c)::value == 2;
+        const std::integral_constant<bool, FULL> full_c;
+        const int stq = it & (NST - 1);
+        const int stq1 = (it + 1) & (NST - 1);
+        const int stq3 = (it + 3) & (NST - 1);
+        const int kt = kb + it * BK;
+        bf16x8 ds[2];
+        bf16x4 trp[2 * NP];
+        f32x16 s1, dp1;
+        // Prefetch read p of the next S/dP section goes into slot n = NDQ - PF + p.
+        auto pre_at = [&](int n, int ms) {
+          if (n >= NDQ - PF) pre[n - (NDQ - PF)] = rd_op(ms, stq1, n - (NDQ - PF));
+        };
+        // A: S/dP of half 1 with exp/dS of half 0; the last quarter of tile it+2's copies
+        sec_sdp_ew(full_c, 1, stq, s1, dp1, pre, 0, stq, kt, s0, dp0, ds, trp,
+                   [&](int k) { copies_at(pend, NC - PER, k, NSD); });
+        wait_vmcnt<NC>();  // tile it+1 landed everywhere once all waves pass the barrier
+        barrier_lds();
+        const Job next = job_of(it + 3, stq3);
+        // B: dQ of half 0; prefetch for C
+        sec_dq(0, stq, trp, ds, [&](int n) {
+          copies_at(next, 0, n, NDQ);
+          pre_at(n, 0);
+        });
+        // C: S/dP of half 0 of tile it+1 with exp/dS of half 1
+        sec_sdp_ew(full_c, 0, stq1, s0, dp0, pre, 1, stq, kt, s1, dp1, ds, trp,
+                   [&](int k) { copies_at(next, PER, k, NSD); });
+        // D: dQ of half 1; prefetch for A of the next step
+        sec_dq(1, stq, trp, ds, [&](int n) {
+          copies_at(next, 2 * PER, n, NDQ);
+          pre_at(n, 1);
+        });
+        pend = next;
+        ++it;
+      };
+
+      // This wave's key tiles: [0,f0) boundary, [f0,f1) interior, [f1,ntiles)
+      // boundary.  Boundary tiles include tiles this wave cannot see at all; the
+      // predicate zeroes them.
+      auto all = [&](int t) { return rect_all_visible(a, qw0, qw0 + kDqRowsPerWave - 1, kb + t * BK, kb + t * BK + BK - 1); };
+      int f0 = ntiles, f1 = ntiles;
+      if constexpr (!MASK) {
+        f0 = 0;
+        while (f0 < ntiles && !all(f0)) ++f0;
+        f1 = f0;
+        while (f1 < ntiles && all(f1)) ++f1;
+      }
+      const std::integral_constant<int, 1> kEdge;
+      const std::integral_constant<int, 2> kInner;
+      int t = 0;
+      for (; t < f0; ++t) step(kEdge);
+      for (; t < f1; ++t) step(kInner);
+      for (; t < ntiles; ++t) step(kEdge);
+      wait_vmcnt<0>();  // the repeated copies of the last steps have landed
+      barrier_lds();    // every wave is done with the ring before the next pass refills it
     }
-    const std::integral_constant<int, 0> kSkip;
-    const std::integral_constant<int, 1> kEdge;
-    const std::integral_constant<int, 2> kInner;
-    int t = 0;
-    for (; t < v0; ++t) step(kSkip, t);
-    for (; t < f0; ++t) step(kEdge, t);
-    for (; t < f1; ++t) step(kInner, t);
-    for (; t < v1; ++t) step(kEdge, t);
-    for (; t < ntiles; ++t) step(kSkip, t);
+    mfma_drain_acc(accq);  // the accumulators' last MFMAs have finished before they are read
 
     if (il < a.Sq) {
 #pragma unroll

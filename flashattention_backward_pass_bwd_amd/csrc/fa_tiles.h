@@ -141,11 +141,18 @@ __device__ __forceinline__ void mfma_drain_acc(f32x16 (&x)[N], f32x16 (&y)[N]) {
 #pragma unroll
   for (int i = 0; i < N; ++i) asm volatile("" : "+a"(x[i]), "+a"(y[i]));
 }
+template <int N>
+__device__ __forceinline__ void mfma_drain_acc(f32x16 (&x)[N]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(x[i]));
+}
 // Values computed by VALU are materialised here: no instruction selection may
 // sink their computation past this point (next to the MFMA that reads them).
 __device__ __forceinline__ void materialise(bf16x8 (&x)[2], bf16x8 (&y)[2]) {
   asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(y[0]), "+v"(y[1]));
 }
+__device__ __forceinline__ void materialise(bf16x8 (&x)[2]) { asm volatile("" : "+v"(x[0]), "+v"(x[1])); }
 
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSgValu = 0x002 | 0x400;  // VALU incl. transcendental
