@@ -27,9 +27,10 @@
 // barrier per tile separates the last reads of a stage from its refill.  L and
 // Delta (64 floats per tile) travel through an 8-stage ring four tiles ahead;
 // two tiles before use, wave 0 turns L into -L*log2(e) and wave 1 turns Delta
-// into -Delta in place, so P = exp2(S*scale*log2(e) - L*log2(e)) is one FMA
-// and one exp2, and (without dropout) the dP chain starts from -Delta and
-// yields dP - Delta directly.  For causal attention without a window, block i
+// into -Delta in place.  K is held multiplied by scale*log2(e) and the S chain
+// starts from the rows' -L*log2(e), so the MFMAs yield the exponent and P is a
+// single exp2; without dropout the dP chain starts from -Delta and yields
+// dP - Delta directly.  For causal attention without a window, block i
 // also takes key block nkb-1-i, so every block carries the same work.
 #include <type_traits>
 
@@ -109,15 +110,23 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     const int kw0 = k0 + wave * kDkdvKeysPerWave;
     const int jl = kw0 + l32;
 
-    // K and V rows of this wave's keys, straight into accumulation registers
-    // (keys past the end repeat the last key; no element of theirs is counted).
+    // K and V rows of this wave's keys in accumulation registers (keys past the
+    // end repeat the last key; no element of theirs is counted).  K is stored
+    // multiplied by scale*log2(e) (rounded to bf16), so the S chain yields the
+    // exponent's first term directly.
     bf16x8 kr[KS], vr[KS];
     const int64_t koff = (int64_t)b * a.ksb + (int64_t)jl * a.kss + (int64_t)kvh * a.ksh;
     const int64_t kclamp = (int64_t)b * a.ksb + (int64_t)min(jl, a.Sk - 1) * a.kss + (int64_t)kvh * a.ksh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      kr[s] = ld16_agpr(K + kclamp + 16 * s + 8 * h2);
+      kr[s] = *reinterpret_cast<const bf16x8*>(K + kclamp + 16 * s + 8 * h2);
       vr[s] = ld16_agpr(V + kclamp + 16 * s + 8 * h2);
+    }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kr[s][e] = (__bf16)((float)kr[s][e] * a.scale_log2);
+      to_agpr(kr[s]);
     }
     f32x16 acck[DB], accv[DB];
 #pragma unroll
@@ -157,36 +166,37 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         const int qt = qb + c.t * BQ;
         return (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)qt * a.qss;
       };
-      // Copy u (0 .. 2*NIW-1; even: Q, odd: dO) of the cursor's tile into a stage.
-      auto issue_copy = [&](const Cursor& c, int64_t base, int stage, int u) {
-        const int lim = a.Sq - 1 - (qb + c.t * BQ);
-        const int blk = wave * NIW + (u >> 1);
-        const int r = blk * RPI + cp_row;
-        const uint32_t off = 2u * ((uint32_t)min(r, lim) * (uint32_t)a.qss + 8u * (uint32_t)(cp_pc ^ swz<D>(r)));
-        if (u & 1)
-          dma16(dO + base, off, lds_addr(&sT[stage][1][blk * RPI * D]));
-        else
-          dma16(Q + base, off, lds_addr(&sT[stage][0][blk * RPI * D]));
-      };
-      // A pending set of copies: the tile, its row base and its ring stage.
+      // A pending set of copies: the tile's first row in Q and in dO, the LDS
+      // address of this wave's first Q row in the ring stage, the last row.
       struct Job {
-        Cursor c;
-        int64_t base;
-        int stage;
+        const __bf16* qp;
+        const __bf16* dop;
+        uint32_t lds;
+        int lim;
       };
       constexpr int NC = 2 * NIW;  // copies per tile per wave
       constexpr int PER = NC / 4;  // copies per section
       static_assert(NC % 4 == 0, "a tile's copies spread over four sections");
-      auto job_of = [&](const Cursor& c, int stage) { return Job{c, qdo_base(c), stage}; };
-      auto issue_job = [&](const Job& j, int u) { issue_copy(j.c, j.base, j.stage, u); };
+      auto job_of = [&](const Cursor& c, int stage) {
+        const int64_t base = qdo_base(c);
+        return Job{Q + base, dO + base, lds_addr(&sT[stage][0][wave * NIW * RPI * D]), a.Sq - 1 - (qb + c.t * BQ)};
+      };
+      // Copy u (0 .. 2*NIW-1; even: Q, odd: dO) of a job.
+      auto issue_job = [&](const Job& j, int u) {
+        const int blk = wave * NIW + (u >> 1);
+        const int r = blk * RPI + cp_row;
+        const uint32_t off = 2u * ((uint32_t)min(r, j.lim) * (uint32_t)a.qss + 8u * (uint32_t)(cp_pc ^ swz<D>(r)));
+        const uint32_t lds = j.lds + 2u * (uint32_t)((u >> 1) * RPI * D + (u & 1) * TILE);
+        dma16((u & 1) ? j.dop : j.qp, off, lds);
+      };
       // Slot hook: copies u0 .. u0+PER-1 of job j, one every nslots/PER slots.
       auto copies_at = [&](const Job& j, int u0, int k, int nslots) {
         if (k % (nslots / PER) == 0) issue_job(j, u0 + k / (nslots / PER));
       };
       auto issue_qdo = [&](const Cursor& c, int stage) {
-        const int64_t base = qdo_base(c);
+        const Job j = job_of(c, stage);
 #pragma unroll
-        for (int u = 0; u < 2 * NIW; ++u) issue_copy(c, base, stage, u);
+        for (int u = 0; u < 2 * NIW; ++u) issue_job(j, u);
       };
       // L (wave 0) and Delta (wave 1) of a tile into an L ring stage (rows past
       // the end repeat the last row), and the tile's dropout row keys (lanes
@@ -245,15 +255,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       };
 
       // What an S/dP + exp/dS section needs first, read by the section before it:
-      // the A operands of its first PF MFMAs, the -Delta rows its dP chain starts
-      // from (FOLD), and the -L*log2(e) (and Delta) rows of the exp/dS half.
+      // the A operands of its first PF MFMAs, the -L*log2(e) rows its S chain
+      // starts from, and the -Delta rows its dP chain starts from (FOLD) or the
+      // Delta rows of the exp/dS half (dropout).
       constexpr int PF = 6;
       struct SdpPre {
         bf16x8 op[PF];
-        f32x16 dpi;
-        f32x4 nl[4], dl[4];
+        f32x16 nls, dpi;
+        f32x4 dl[4];
       };
-      constexpr int NPRE = PF + (FOLD ? 4 : 0) + (FOLD ? 4 : 8);  // LDS reads of a prefetch
+      constexpr int NPRE = PF + 8;  // LDS reads of a prefetch
       // Prefetch read p (0 .. NPRE-1) for a section computing S/dP of half ms
       // (stage sts, L ring stage lsts) and exp/dS of half me (L ring stage lste).
       auto prefetch = [&](SdpPre& pre, int p, int ms, int sts, int lsts, int me, int lste) {
@@ -262,21 +273,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           return;
         }
         p -= PF;
-        if constexpr (FOLD) {
-          if (p < 4) {
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[lsts][32 * ms + 8 * p + 4 * h2]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pre.dpi[4 * p + e] = d4[e];
-            return;
-          }
-          p -= 4;
-        }
         if (p < 4) {
-          pre.nl[p] = *reinterpret_cast<const f32x4*>(&sL[lste][32 * me + 8 * p + 4 * h2]);
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[lsts][32 * ms + 8 * p + 4 * h2]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pre.nls[4 * p + e] = l4[e];
           return;
         }
         p -= 4;
-        if constexpr (!FOLD) pre.dl[p] = *reinterpret_cast<const f32x4*>(&sDel[lste][32 * me + 8 * p + 4 * h2]);
+        if constexpr (FOLD) {
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[lsts][32 * ms + 8 * p + 4 * h2]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pre.dpi[4 * p + e] = d4[e];
+        } else {
+          pre.dl[p] = *reinterpret_cast<const f32x4*>(&sDel[lste][32 * me + 8 * p + 4 * h2]);
+        }
       };
       auto prefetch_all = [&](SdpPre& pre, int ms, int sts, int lsts, int me, int lste) {
 #pragma unroll
@@ -295,16 +305,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         bf16x8 op[8];
 #pragma unroll
         for (int k = 0; k < PF; ++k) op[k] = pre.op[k];
-        if constexpr (FOLD) dp = pre.dpi;
         const int dl0 = jl - qt;  // d = j - i = dl0 - row
         const int rlim = a.Sq - qt;
         const bool jin = jl < a.Sk;
         const int jc = min(jl, a.Sk - 1);
-        float pv[16], dv[16];
-        // exp/dS of element r (C-layout register r of half me); odd r packs the pair.
-        auto ew_elem = [&](int r) {
+        float pr[16], pv[16], dv[16];
+        // exp of element r (C-layout register r of half me); se holds
+        // S*scale*log2(e) - L*log2(e).
+        auto ew_exp = [&](int r) {
           const int row = 32 * me + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          float x = __builtin_fmaf(se[r], a.scale_log2, pre.nl[r >> 2][r & 3]);
+          float x = se[r];
           if constexpr (!FULL) {
             const int dd = dl0 - row;
             bool ok = jin && row < rlim && dd > vb.dlo && dd < vb.dhi;
@@ -316,14 +326,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
             }
             x = ok ? x : -__builtin_inff();
           }
-          const float pr = __builtin_amdgcn_exp2f(x);
+          pr[r] = __builtin_amdgcn_exp2f(x);
+        };
+        // P and dS of element r, one slot after its exp; odd r packs the pair.
+        auto ew_ds = [&](int r) {
           if constexpr (DROP) {
+            const int row = 32 * me + 8 * (r >> 2) + 4 * h2 + (r & 3);
             const float mm = drop_keep(sRK[lste][row], jl, a.drop_thr) ? a.drop_inv : 0.f;
-            pv[r] = pr * mm;
-            dv[r] = pr * (dpe[r] * mm - pre.dl[r >> 2][r & 3]);
+            pv[r] = pr[r] * mm;
+            dv[r] = pr[r] * (dpe[r] * mm - pre.dl[r >> 2][r & 3]);
           } else {
-            pv[r] = pr;
-            dv[r] = pr * dpe[r];
+            pv[r] = pr[r];
+            dv[r] = pr[r] * dpe[r];
           }
           if (r & 1) {
             pmc[r >> 3][(r & 7) - 1] = (__bf16)pv[r - 1];
@@ -338,34 +352,33 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           const bf16x8& o = op[k & 7];
           if (k & 1) {
             if (k == 1 && FOLD)
-              mfma_v_init(dp, o, vr[k >> 1]);
+              mfma_v_seed(dp, o, vr[k >> 1], pre.dpi);
             else if (k == 1)
               mfma_v0(dp, o, vr[k >> 1]);
             else
               mfma_v(dp, o, vr[k >> 1]);
           } else {
             if (k == 0)
-              mfma_v0(s, o, kr[k >> 1]);
+              mfma_v_seed(s, o, kr[k >> 1], pre.nls);
             else
               mfma_v(s, o, kr[k >> 1]);
           }
           if (k + PF < NSD) op[(k + PF) & 7] = rd_op(ms, sts, k + PF);
           if (k >= NSD - 2 * NP) trp[k - (NSD - 2 * NP)] = rd_tr(me, ste, k - (NSD - 2 * NP));
-          // elements [e0, e0 + ne) in slot k
-          int e0, ne;
-          if constexpr (NSD == 16) {
-            e0 = k;
-            ne = 1;
-          } else {
-            e0 = 2 * k;
-            ne = 2;
-          }
+          // 16 exp/dS elements over the NSD slots: the exps of this slot's elements
+          // and the P/dS of the previous slot's (no result is read right after its exp)
+          constexpr int E = 16 / NSD;
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
-            if (i < ne) ew_elem(e0 + i);
+          for (int i = 0; i < E; ++i) ew_exp(k * E + i);
+          if (k > 0) {
+#pragma unroll
+            for (int i = 0; i < E; ++i) ew_ds((k - 1) * E + i);
+          }
           slot_extra(k);
           fence();
         }
+#pragma unroll
+        for (int i = 0; i < 16 / NSD; ++i) ew_ds(16 - 16 / NSD + i);
         // The packed P/dS are complete here, and S/dP (and P/dS, 24 wait states
         // later) may be read by anything once the drain has passed.
         materialise(pmc, dsc);

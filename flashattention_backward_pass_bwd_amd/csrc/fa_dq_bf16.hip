@@ -9,9 +9,11 @@
 // Per 64-key tile and wave: S^T = K Q^T and dP^T = V dO^T (row-major A
 // operands from LDS), P and dS^T in registers, then dQ^T += K^T dS^T (K
 // transposed through ds_read_b64_tr_b16).  S^T has one query per lane column,
-// so L_i and Delta_i are per-lane scalars (without dropout the dP^T chain
-// starts from -Delta_i, so dP - Delta comes out of the MFMAs) and dS^T is
-// already the B operand of the last contraction.
+// so L_i and Delta_i are per-lane scalars: Q is held multiplied by
+// scale*log2(e) and the S^T chain starts from -L_i*log2(e), so P is a single
+// exp2 of the MFMA result, and without dropout the dP^T chain starts from
+// -Delta_i, so dP - Delta comes out of the MFMAs.  dS^T is already the B
+// operand of the last contraction.
 //
 // Software pipeline, as in the dK/dV kernel: a tile is two 32-key halves and
 // the step of tile it runs
@@ -102,12 +104,14 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
 
     // Q and dO rows of this wave's queries, straight into accumulation registers
     // (rows past the end repeat the last row; their results are not written).
+    // Q is stored multiplied by scale*log2(e) (rounded to bf16), so the S^T chain
+    // yields the exponent's first term directly.
     bf16x8 qr[KS], gr[KS];
     const int64_t qoff = (int64_t)b * a.qsb + (int64_t)il * a.qss + (int64_t)h * a.qsh;
     const int64_t qclamp = (int64_t)b * a.qsb + (int64_t)min(il, a.Sq - 1) * a.qss + (int64_t)h * a.qsh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      qr[s] = ld16_agpr(Q + qclamp + 16 * s + 8 * h2);
+      qr[s] = *reinterpret_cast<const bf16x8*>(Q + qclamp + 16 * s + 8 * h2);
       gr[s] = ld16_agpr(dO + qclamp + 16 * s + 8 * h2);
     }
     const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq + min(il, a.Sq - 1);
@@ -119,37 +123,51 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
 #pragma unroll
     for (int d = 0; d < DB; ++d) accq[d] = f32x16{};
     wait_all_vmem();  // Q, dO rows, L and Delta are in registers before the copy ring starts
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qr[s][e] = (__bf16)((float)qr[s][e] * a.scale_log2);
+      to_agpr(qr[s]);
+    }
 
     int kb, ke;
     key_range(a, q0, min(q0 + kDqRowsPerBlock, a.Sq) - 1, kb, ke);
     const int ntiles = (ke - kb + BK - 1) / BK;
 
     if (ntiles > 0) {
-      // The dP^T chain starts from -Delta_i (every C register of a lane is row i).
-      f32x16 dpi;
+      // The S^T chain starts from -L_i*log2(e) and (without dropout) the dP^T
+      // chain from -Delta_i: every C register of a lane is query row i.
+      f32x16 nls, dpi;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dpi[r] = FOLD ? -del : 0.f;
+      for (int r = 0; r < 16; ++r) {
+        nls[r] = nl;
+        dpi[r] = -del;
+      }
+      // kept in registers as they are, not rebuilt next to each use
+      asm volatile("" : "+v"(nls));
+      if constexpr (FOLD) asm volatile("" : "+v"(dpi));
 
       // K and V rows of tile tt (clamped to the last tile, so copies past the end
       // repeat it into stages that are never read) into a ring stage: copy u
       // (even: K, odd: V) of this wave fills rows (wave*NIW + u/2)*RPI + lane/NCH.
       // Rows past the end repeat the last key; they are never counted.
       struct Job {
-        int64_t base;
-        int lim, stage;
+        const __bf16* kp;  // first row of the tile in K and in V
+        const __bf16* vp;
+        uint32_t lds;      // LDS address of this wave's first K row in the stage
+        int lim;
       };
       auto job_of = [&](int tt, int stage) {
         const int kt = kb + min(tt, ntiles - 1) * BK;
-        return Job{(int64_t)b * a.ksb + (int64_t)kt * a.kss + (int64_t)kvh * a.ksh, a.Sk - 1 - kt, stage};
+        const int64_t base = (int64_t)b * a.ksb + (int64_t)kt * a.kss + (int64_t)kvh * a.ksh;
+        return Job{K + base, V + base, lds_addr(&sT[stage][0][wave * NIW * RPI * D]), a.Sk - 1 - kt};
       };
       auto issue_job = [&](const Job& j, int u) {
         const int blk = wave * NIW + (u >> 1);
         const int r = blk * RPI + cp_row;
         const uint32_t off = 2u * ((uint32_t)min(r, j.lim) * (uint32_t)a.kss + 8u * (uint32_t)(cp_pc ^ swz<D>(r)));
-        if (u & 1)
-          dma16(V + j.base, off, lds_addr(&sT[j.stage][1][blk * RPI * D]));
-        else
-          dma16(K + j.base, off, lds_addr(&sT[j.stage][0][blk * RPI * D]));
+        const uint32_t lds = j.lds + 2u * (uint32_t)((u >> 1) * RPI * D + (u & 1) * TILE);
+        dma16((u & 1) ? j.vp : j.kp, off, lds);
       };
       // Slot hook: copies u0 .. u0+PER-1 of job j, one every nslots/PER slots.
       auto copies_at = [&](const Job& j, int u0, int k, int nslots) {
@@ -179,16 +197,16 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         bf16x8 op[8];
 #pragma unroll
         for (int k = 0; k < PF; ++k) op[k] = pre[k];
-        if constexpr (FOLD) dp = dpi;
         const int dl0 = kt - il;  // d = j - i = dl0 + key
         const int klim = a.Sk - kt;
         const bool iin = il < a.Sq;
         const int ic = min(il, a.Sq - 1);
-        float dv[16];
-        // exp/dS of element r (C-layout register r of half me: key 32me + 8(r/4) + 4h2 + r%4).
-        auto ew_elem = [&](int r) {
+        float pv[16], dv[16];
+        // exp of element r (C-layout register r of half me: key 32me + 8(r/4) + 4h2 + r%4);
+        // se holds S*scale*log2(e) - L*log2(e).
+        auto ew_exp = [&](int r) {
           const int key = 32 * me + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          float x = __builtin_fmaf(se[r], a.scale_log2, nl);
+          float x = se[r];
           if constexpr (!FULL) {
             const int dd = dl0 + key;
             bool ok = iin && key < klim && dd > vb.dlo && dd < vb.dhi;
@@ -200,12 +218,16 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
             }
             x = ok ? x : -__builtin_inff();
           }
-          const float pr = __builtin_amdgcn_exp2f(x);
+          pv[r] = __builtin_amdgcn_exp2f(x);
+        };
+        // dS of element r, one slot after its exp; odd r packs the pair.
+        auto ew_ds = [&](int r) {
           if constexpr (DROP) {
+            const int key = 32 * me + 8 * (r >> 2) + 4 * h2 + (r & 3);
             const float mm = drop_keep(rk, kt + key, a.drop_thr) ? a.drop_inv : 0.f;
-            dv[r] = pr * (dpe[r] * mm - del);
+            dv[r] = pv[r] * (dpe[r] * mm - del);
           } else {
-            dv[r] = pr * dpe[r];
+            dv[r] = pv[r] * dpe[r];
           }
           if (r & 1) {
             dsc[r >> 3][(r & 7) - 1] = (__bf16)dv[r - 1];
@@ -218,25 +240,33 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
           const bf16x8& o = op[k & 7];
           if (k & 1) {
             if (k == 1 && FOLD)
-              mfma_v_init(dp, o, gr[k >> 1]);
+              mfma_v_seed(dp, o, gr[k >> 1], dpi);
             else if (k == 1)
               mfma_v0(dp, o, gr[k >> 1]);
             else
               mfma_v(dp, o, gr[k >> 1]);
           } else {
             if (k == 0)
-              mfma_v0(s, o, qr[k >> 1]);
+              mfma_v_seed(s, o, qr[k >> 1], nls);
             else
               mfma_v(s, o, qr[k >> 1]);
           }
           if (k + PF < NSD) op[(k + PF) & 7] = rd_op(ms, sts, k + PF);
           if (k >= NSD - 2 * NP) trp[k - (NSD - 2 * NP)] = rd_tr(me, ste, k - (NSD - 2 * NP));
-          // 16 exp/dS elements over the NSD slots
+          // 16 exp/dS elements over the NSD slots: the exps of this slot's elements
+          // and the dS of the previous slot's (no result is read right after its exp)
+          constexpr int E = 16 / NSD;
 #pragma unroll
-          for (int i = 0; i < 16 / NSD; ++i) ew_elem(k * (16 / NSD) + i);
+          for (int i = 0; i < E; ++i) ew_exp(k * E + i);
+          if (k > 0) {
+#pragma unroll
+            for (int i = 0; i < E; ++i) ew_ds((k - 1) * E + i);
+          }
           slot_extra(k);
           fence();
         }
+#pragma unroll
+        for (int i = 0; i < 16 / NSD; ++i) ew_ds(16 - 16 / NSD + i);
         // dS^T is complete here, and S/dP (and dS^T, 24 wait states later) may
         // be read by anything once the drain has passed.
         materialise(dsc);

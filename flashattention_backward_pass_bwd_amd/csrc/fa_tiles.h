@@ -57,22 +57,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 // as LDS writes and does not wait for every copy in flight before each later
 // LDS read, which would serialise the copy ring.  Callers order them with
 // wait_vmcnt (every wave waits for its own copies) and a block barrier.
-// M0 holds the LDS address for the copy; it is saved and restored around it,
-// with the one wait state an M0 write needs before an LDS DMA.
+// M0 holds the LDS address for the copy.  It is written without being saved:
+// the compiler itself never reads or writes M0 in the kernels that use these
+// copies (gfx9 LDS instructions do not need it, and these kernels have no
+// dynamically indexed register arrays or messages), which
+// tests/test_m0_ownership.py checks on the generated assembly.  One wait state
+// separates the M0 write from the copy.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  uint32_t sv;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
-      : "=&s"(sv)
-      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)));
 }
 
 __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
-  uint32_t sv;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
-      : "=&s"(sv)
-      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)));
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)));
 }
 
 // Block barrier without a memory fence: LDS writes of this wave are complete
@@ -118,6 +118,17 @@ __device__ __forceinline__ void mfma_v(f32x16& c, const bf16x8& a, const bf16x8&
 __device__ __forceinline__ void mfma_v_init(f32x16& c, const bf16x8& a, const bf16x8& b) {
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
 }
+
+// c = a b + seed: the first MFMA of a chain that starts from a register block
+// holding its initial value (the block itself is left as it is).  The two wait
+// states cover a seed written by VALU just before.
+__device__ __forceinline__ void mfma_v_seed(f32x16& c, const bf16x8& a, const bf16x8& b, const f32x16& seed) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(c) : "v"(a), "a"(b), "v"(seed));
+}
+
+// Moves a value into accumulation registers once, so that later MFMAs read it
+// there as a B operand without a copy per use.
+__device__ __forceinline__ void to_agpr(bf16x8& v) { asm volatile("" : "+a"(v)); }
 
 // 16-byte global load straight into accumulation registers (the home of the
 // stationary B operands), as inline assembly: the compiler neither copies the
