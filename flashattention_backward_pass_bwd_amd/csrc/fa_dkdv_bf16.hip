@@ -212,13 +212,19 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           if (lane < 16) sRK[lst][16 * wave + lane] = drop_row_key(a, b, h, qt + 16 * wave + lane);
         }
       };
-      // Once a stage's L/Delta landed: L -> -L*log2(e) (wave 0), Delta -> -Delta
-      // (wave 1, when the dP chain is seeded with it).
-      auto fix_ld = [&](int lst) {
-        if (wave == 0) sL[lst][lane] *= -kLog2e;
-        if constexpr (FOLD) {
-          if (wave == 1) sDel[lst][lane] = -sDel[lst][lane];
-        }
+      // Once a stage's L/Delta landed and a barrier passed, each wave rewrites 16
+      // rows of it in place: L -> -L*log2(e) (lanes 0-15) and, when the dP chain
+      // is seeded with it, Delta -> -Delta (lanes 16-31).  The read and the write
+      // go into different sections, so the LDS latency hides behind MFMAs.
+      const bool fix_lane = lane < (FOLD ? 32 : 16);
+      float* const fix_p = lane < 16 ? &sL[0][16 * wave + lane] : &sDel[0][16 * wave + (lane & 15)];
+      const float fix_f = lane < 16 ? -kLog2e : -1.f;
+      float fix_v = 0.f;
+      auto fix_rd = [&](int lst) {
+        if (fix_lane) fix_v = fix_p[lst * BQ];
+      };
+      auto fix_wr = [&](int lst) {
+        if (fix_lane) fix_p[lst * BQ] = fix_v * fix_f;
       };
       // Waits until this wave's copies issued before the previous step's have
       // landed (waves 0 and 1 issue one more copy per step: L or Delta).
@@ -379,10 +385,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         }
 #pragma unroll
         for (int i = 0; i < 16 / NSD; ++i) ew_ds(16 - 16 / NSD + i);
-        // The packed P/dS are complete here, and S/dP (and P/dS, 24 wait states
-        // later) may be read by anything once the drain has passed.
+        // The packed P/dS are complete here; S/dP are next read a whole section
+        // later (the prologue drains them explicitly).
         materialise(pmc, dsc);
-        mfma_drain(s, dp);
+        mfma_settle(s, dp);
         fence();
       };
       // Section "dV/dK" of half m (stage stq): MFMAs 0 .. NP-1 take the transposed
@@ -433,8 +439,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       for (int u = 0; u < NC - PER; ++u) issue_job(pend, u);
       advance(cq);
       wait_vmcnt<0>();
-      fix_ld(0);
-      fix_ld(1);
+      barrier_lds();
+      fix_rd(0);
+      fix_wr(0);
+      fix_rd(1);
+      fix_wr(1);
       barrier_lds();
 
       // S/dP of half 0 of the current tile, carried between steps, and the
@@ -448,6 +457,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         prefetch_all(pre, 0, 0, 0, 0, 0);
         // a section with no exp/dS work to overlap: only its S/dP result is kept
         sec_sdp_ew(std::true_type{}, 0, 0, s0, dp0, pre, 0, 0, 0, qb, 0, z, z, pm, ds, trp, [](int) {});
+        mfma_drain(s0, dp0);  // read by the first step's exp/dS after only a few instructions
         prefetch_all(pre, 1, 0, 0, 0, 0);  // for section A of step 0
       }
 
@@ -483,20 +493,22 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         sec_sdp_ew(full_c, 1, stq, s1, dp1, pre, 0, stq, lst, qt, h, s0, dp0, pm, ds, trp,
                    [&](int k) { copies_at(pend, NC / 2 + PER, k, NSD); });
         wait_prev();  // tile it+1 landed everywhere once all waves pass the barrier
-        barrier_lds();
+        barrier_only();
         issue_ld(cl, lst4);
         advance(cl);
-        fix_ld(lst2);
         fence();
         const Job next = job_of(cq, stq3);
         // B: dV/dK of half 0; prefetch for C (S/dP of half 0 of tile it+1, exp/dS of half 1)
         sec_dkv(0, stq, trp, pm, ds, [&](int n) {
           copies_at(next, 0, n, NDK);
           pre_at(n, 0, stq1, lst1, 1, lst);
+          if (n == NDK / 2) fix_rd(lst2);  // L/Delta of tile it+2 (its copy landed before this step's barrier)
         });
         // C: S/dP of half 0 of tile it+1 with exp/dS of half 1
-        sec_sdp_ew(full_c, 0, stq1, s0, dp0, pre, 1, stq, lst, qt, h, s1, dp1, pm, ds, trp,
-                   [&](int k) { copies_at(next, PER, k, NSD); });
+        sec_sdp_ew(full_c, 0, stq1, s0, dp0, pre, 1, stq, lst, qt, h, s1, dp1, pm, ds, trp, [&](int k) {
+          copies_at(next, PER, k, NSD);
+          if (k == 1) fix_wr(lst2);
+        });
         // D: dV/dK of half 1; prefetch for A of the next step
         sec_dkv(1, stq, trp, pm, ds, [&](int n) {
           copies_at(next, 2 * PER, n, NDK);

@@ -267,10 +267,10 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         }
 #pragma unroll
         for (int i = 0; i < 16 / NSD; ++i) ew_ds(16 - 16 / NSD + i);
-        // dS^T is complete here, and S/dP (and dS^T, 24 wait states later) may
-        // be read by anything once the drain has passed.
+        // dS^T is complete here; S/dP are next read a whole section later (the
+        // prologue drains them explicitly).
         materialise(dsc);
-        mfma_drain(s, dp);
+        mfma_settle(s, dp);
         fence();
       };
       // Section "dQ" of half m (stage stq): MFMAs 0 .. NP-1 take the transposed
@@ -322,6 +322,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         for (int k = 0; k < PF; ++k) pre[k] = rd_op(0, 0, k);
         // a section with no exp/dS work to overlap: only its S/dP result is kept
         sec_sdp_ew(std::true_type{}, 0, 0, s0, dp0, pre, 0, 0, kb, z, z, ds, trp, [](int) {});
+        mfma_drain(s0, dp0);  // read by the first step's exp/dS after only a few instructions
 #pragma unroll
         for (int k = 0; k < PF; ++k) pre[k] = rd_op(1, 0, k);
       }
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         sec_sdp_ew(full_c, 1, stq, s1, dp1, pre, 0, stq, kt, s0, dp0, ds, trp,
                    [&](int k) { copies_at(pend, NC - PER, k, NSD); });
         wait_vmcnt<NC>();  // tile it+1 landed everywhere once all waves pass the barrier
-        barrier_lds();
+        barrier_only();
         const Job next = job_of(it + 3, stq3);
         // B: dQ of half 0; prefetch for C
         sec_dq(0, stq, trp, ds, [&](int n) {

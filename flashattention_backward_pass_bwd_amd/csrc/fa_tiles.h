@@ -81,6 +81,13 @@ __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t 
 // they need with wait_vmcnt first.
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Block barrier that waits for nothing: for a ring step whose only LDS
+// accesses still in flight are reads of stages no copy refills before the next
+// barrier, and whose LDS writes are older than the operand reads that later
+// waits of the wave (lgkmcnt, LDS accesses complete in order) cover before the
+// readers' barrier.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
 // Waits for every vector memory access of this wave, as an instruction the
 // compiler sees: loads the compiler issued (register operands loaded before a
 // copy ring starts) are then known complete, and it places no wait of its own
@@ -146,6 +153,12 @@ __device__ __forceinline__ bf16x8 ld16_agpr(const void* p) {
 __device__ __forceinline__ void mfma_drain(f32x16& x, f32x16& y) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
 }
+// End of a chain whose results are next read only after a whole section of
+// other MFMAs (more wait states than an XDL result needs): it keeps the two
+// wait states a VALU-written B operand needs before the next section's first
+// MFMA, and passes the results through the asm so that no read of them moves
+// up next to the chain.
+__device__ __forceinline__ void mfma_settle(f32x16& x, f32x16& y) { asm volatile("s_nop 1" : "+v"(x), "+v"(y)); }
 template <int N>
 __device__ __forceinline__ void mfma_drain_acc(f32x16 (&x)[N], f32x16 (&y)[N]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
