@@ -16,8 +16,9 @@ int elem_bytes(int dtype) { return dtype == FA_DTYPE_BF16 ? 2 : 4; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int64_t kMaxSeq = int64_t(1) << 30;
+constexpr int64_t kMaxSeq = int64_t(1) << 29;  // sequence lengths, causal offset, window
 constexpr int64_t kMaxRowStride = int64_t(1) << 24;  // elements between consecutive rows
+constexpr int64_t kMaxMaskStride = int64_t(1) << 22;  // mask row / column stride, elements (bf16 path)
 
 fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
   if (p == nullptr) return FA_ERR_NULL;
@@ -41,10 +42,19 @@ fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
   }
   // Tile copies address rows by 32-bit byte offsets from a tile's first row.
   if (p->q_stride_s > kMaxRowStride || p->kv_stride_s > kMaxRowStride) return FA_ERR_UNSUPPORTED;
+  int64_t mask_rec = 0;
   if (p->mask != nullptr) {
     if (p->mask_stride_b < 0 || p->mask_stride_h < 0 || p->mask_stride_q < 0 || p->mask_stride_k < 0)
       return FA_ERR_ARG;
     if ((reinterpret_cast<uintptr_t>(p->mask) & 3u) != 0) return FA_ERR_ALIGN;
+    // The bf16 tile kernels read the mask of one (b, h) through a 32-bit byte
+    // range with 24-bit row and column strides.
+    if (p->mask_stride_q >= kMaxMaskStride || p->mask_stride_k >= kMaxMaskStride) {
+      if (p->dtype == FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    } else {
+      mask_rec = ((int64_t)(p->seq_q - 1) * p->mask_stride_q + (int64_t)(p->seq_k - 1) * p->mask_stride_k + 1) * 4;
+      if (mask_rec > (int64_t)UINT32_MAX && p->dtype == FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    }
   }
   // Grid sizes (the kernels index blocks with 32-bit integers).
   const int64_t nq = (p->seq_q + fa::kDqRowsPerBlock - 1) / fa::kDqRowsPerBlock;
@@ -79,6 +89,7 @@ fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
   a->msh = p->mask_stride_h;
   a->msq = p->mask_stride_q;
   a->msk = p->mask_stride_k;
+  a->mask_rec = (uint32_t)(mask_rec > (int64_t)UINT32_MAX ? UINT32_MAX : mask_rec);
   return FA_OK;
 }
 

@@ -31,6 +31,7 @@ struct PrefillArgs {
   uint32_t seed_mix;              // fmix32(seed)
   const float* mask;
   int64_t msb, msh, msq, msk;
+  uint32_t mask_rec;  // bytes of one (b, h) slice of the mask: ((Sq-1)*msq + (Sk-1)*msk + 1)*4 (bf16 path)
 };
 
 // MurmurHash3 32-bit finaliser (Appleby, public domain).

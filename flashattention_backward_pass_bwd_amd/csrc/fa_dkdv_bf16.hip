@@ -73,6 +73,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
   __shared__ __attribute__((aligned(16))) float sL[NSL][BQ];
   __shared__ __attribute__((aligned(16))) float sDel[NSL][BQ];
   __shared__ __attribute__((aligned(16))) uint32_t sRK[DROP ? NSL : 1][DROP ? BQ : 1];
+  // Mask values of one exp/dS half per wave: element r of lane l at sM[wave][r][l].
+  __shared__ __attribute__((aligned(16))) float sM[MASK ? 4 : 1][MASK ? 16 : 1][64];
 
   const int nbh = a.B * a.Hkv;
   const int wi = blockIdx.x / nbh;
@@ -136,6 +138,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     }
     wait_vmcnt<0>();  // K and V rows landed before the copy ring starts
 
+    // Mask reads: byte offset of element (row, key) in the (b, h) slice is
+    // row*msq*4 + key*msk*4; lanes fix the key (clamped) and the 4-row group.
+    const uint32_t msq4 = MASK ? (uint32_t)a.msq * 4u : 0u;
+    const uint32_t m_lvo = MASK ? ((uint32_t)min(jl, a.Sk - 1) * (uint32_t)a.msk + 4u * h2 * (uint32_t)a.msq) * 4u : 0u;
+    const uint32_t jg = (uint32_t)jl * 0x9E3779B9u;  // key part of the dropout draw
+
     int qb, qe;
     query_range(a, k0, min(k0 + kDkdvKeysPerBlock, a.Sk) - 1, qb, qe);
     const int ntq = (qe - qb + BQ - 1) / BQ;
@@ -177,6 +185,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       constexpr int NC = 2 * NIW;  // copies per tile per wave
       constexpr int PER = NC / 4;  // copies per section
       static_assert(NC % 4 == 0, "a tile's copies spread over four sections");
+      // Mask staging (MASK): element r of a half is copied into sM right after the
+      // same element of the other half was used (sections A and C, the slot of
+      // element r), and read MF slots before its own use two sections later.  Of
+      // the copies issued after it, at least 16 - E*(MF+1) mask copies and
+      // PER - 1 tile copies are issued before that read (E elements per slot),
+      // so waiting for at most kMaskWait accesses in flight covers it.
+      constexpr int MF = 2;
+      constexpr int kMaskWait = 16 - (16 / NSD) * (MF + 1) + PER - 1;
+      static_assert(kMaskWait >= 0, "mask staging wait");
       auto job_of = [&](const Cursor& c, int stage) {
         const int64_t base = qdo_base(c);
         return Job{Q + base, dO + base, lds_addr(&sT[stage][0][wave * NIW * RPI * D]), a.Sq - 1 - (qb + c.t * BQ)};
@@ -228,11 +245,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       };
       // Waits until this wave's copies issued before the previous step's have
       // landed (waves 0 and 1 issue one more copy per step: L or Delta).
+      // With a mask, the 32 mask copies of a step count too, and those of section
+      // A issued after its last tile copy (16 / PER of them).
+      constexpr int NMV = MASK ? 32 + 16 / PER : 0;
       auto wait_prev = [&]() {
         if (wave < 2)
-          wait_vmcnt<2 * NIW + 1>();
+          wait_vmcnt<2 * NIW + NMV + 1>();
         else
-          wait_vmcnt<2 * NIW>();
+          wait_vmcnt<2 * NIW + NMV>();
       };
 
       // Instruction order inside a step is fixed by hand: one wave per SIMD means
@@ -265,12 +285,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       // starts from, and the -Delta rows its dP chain starts from (FOLD) or the
       // Delta rows of the exp/dS half (dropout).
       constexpr int PF = 6;
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       struct SdpPre {
         bf16x8 op[PF];
         f32x16 nls, dpi;
         f32x4 dl[4];
+        u32x4 rk[DROP ? 4 : 1];  // dropout row keys of the exp/dS half
       };
-      constexpr int NPRE = PF + 8;  // LDS reads of a prefetch
+      constexpr int NPRE = PF + 8 + (DROP ? 4 : 0);  // LDS reads of a prefetch
       // Prefetch read p (0 .. NPRE-1) for a section computing S/dP of half ms
       // (stage sts, L ring stage lsts) and exp/dS of half me (L ring stage lste).
       auto prefetch = [&](SdpPre& pre, int p, int ms, int sts, int lsts, int me, int lste) {
@@ -286,13 +308,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           return;
         }
         p -= 4;
-        if constexpr (FOLD) {
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[lsts][32 * ms + 8 * p + 4 * h2]);
+        if (p < 4) {
+          if constexpr (FOLD) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[lsts][32 * ms + 8 * p + 4 * h2]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pre.dpi[4 * p + e] = d4[e];
-        } else {
-          pre.dl[p] = *reinterpret_cast<const f32x4*>(&sDel[lste][32 * me + 8 * p + 4 * h2]);
+            for (int e = 0; e < 4; ++e) pre.dpi[4 * p + e] = d4[e];
+          } else {
+            pre.dl[p] = *reinterpret_cast<const f32x4*>(&sDel[lste][32 * me + 8 * p + 4 * h2]);
+          }
+          return;
         }
+        p -= 4;
+        if constexpr (DROP) pre.rk[p] = *reinterpret_cast<const u32x4*>(&sRK[lste][32 * me + 8 * p + 4 * h2]);
       };
       auto prefetch_all = [&](SdpPre& pre, int ms, int sts, int lsts, int me, int lste) {
 #pragma unroll
@@ -305,28 +332,36 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       // reads of the first NP MFMAs of that half's dV/dK (stage ste).  Operand
       // reads run PF MFMAs ahead; the 16 exp/dS elements are spread over the slots.
       auto sec_sdp_ew = [&](auto full_c, int ms, int sts, f32x16& s, f32x16& dp, const SdpPre& pre, int me,
-                            int ste, int lste, int qt, int h, const f32x16& se, const f32x16& dpe,
+                            int ste, int qt, const f32x16& se, const f32x16& dpe,
                             bf16x8 (&pmc)[2], bf16x8 (&dsc)[2], bf16x4 (&trp)[2 * NP], auto&& slot_extra) {
         constexpr bool FULL = decltype(full_c)::value;
         bf16x8 op[8];
 #pragma unroll
         for (int k = 0; k < PF; ++k) op[k] = pre.op[k];
-        const int dl0 = jl - qt;  // d = j - i = dl0 - row
-        const int rlim = a.Sq - qt;
-        const bool jin = jl < a.Sk;
-        const int jc = min(jl, a.Sk - 1);
+        // Visible rows of this lane's key in the tile: d = j - i in (dlo, dhi), row
+        // in range, key in range, i.e. tile rows [lo, hi).  Element r sits at row
+        // 32*me + 4*h2 + c(r), c(r) = 8*(r/4) + r%4, so it is visible iff
+        // c(r) - lb < span (unsigned) with lb = lo - 32*me - 4*h2.
+        int lb = 0;
+        uint32_t span = 0;
+        if constexpr (!FULL) {
+          // no overflow: |dl0| <= 2^29 + 128 and the bounds lie within +-(2^30 + 1)
+          const int dl0 = jl - qt;  // d = dl0 - row
+          const int lo = max(dl0 - vb.dhi + 1, 0);
+          const int hi = jl < a.Sk ? min(dl0 - vb.dlo, a.Sq - qt) : 0;
+          span = (uint32_t)max(hi - lo, 0);
+          lb = lo - 32 * me - 4 * h2;
+        }
         float pr[16], pv[16], dv[16];
+        float mk[16];  // mask values of the half (MASK), read ahead from sM
         // exp of element r (C-layout register r of half me); se holds
         // S*scale*log2(e) - L*log2(e).
         auto ew_exp = [&](int r) {
-          const int row = 32 * me + 8 * (r >> 2) + 4 * h2 + (r & 3);
           float x = se[r];
           if constexpr (!FULL) {
-            const int dd = dl0 - row;
-            bool ok = jin && row < rlim && dd > vb.dlo && dd < vb.dhi;
+            bool ok = (uint32_t)(8 * (r >> 2) + (r & 3) - lb) < span;
             if constexpr (MASK) {
-              // clamped indices keep the load in bounds; ok discards out-of-range elements
-              const float mv = mask_at(a, b, h, min(qt + row, a.Sq - 1), jc);
+              const float mv = mk[r];
               ok = ok && !(mv <= kMaskedSentinel);
               x = __builtin_fmaf(mv, kLog2e, x);
             }
@@ -337,8 +372,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         // P and dS of element r, one slot after its exp; odd r packs the pair.
         auto ew_ds = [&](int r) {
           if constexpr (DROP) {
-            const int row = 32 * me + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            const float mm = drop_keep(sRK[lste][row], jl, a.drop_thr) ? a.drop_inv : 0.f;
+            const float mm = fmix32(pre.rk[r >> 2][r & 3] ^ jg) >= a.drop_thr ? a.drop_inv : 0.f;
             pv[r] = pr[r] * mm;
             dv[r] = pr[r] * (dpe[r] * mm - pre.dl[r >> 2][r & 3]);
           } else {
@@ -352,6 +386,19 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
             dsc[r >> 3][r & 7] = (__bf16)dv[r];
           }
         };
+        // Mask values of the half, read from this wave's LDS staging MF slots ahead
+        // of their use, each once its copy (issued two sections earlier) landed.
+        auto mask_rd = [&](int kk) {
+          if constexpr (MASK && !FULL) {
+            if (kk < NSD) {
+              wait_vmcnt<kMaskWait>();
+#pragma unroll
+              for (int i = 0; i < 16 / NSD; ++i) mk[kk * (16 / NSD) + i] = sM[wave][kk * (16 / NSD) + i][lane];
+            }
+          }
+        };
+#pragma unroll
+        for (int k = 0; k < MF; ++k) mask_rd(k);
         fence();
 #pragma unroll
         for (int k = 0; k < NSD; ++k) {
@@ -380,6 +427,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
 #pragma unroll
             for (int i = 0; i < E; ++i) ew_ds((k - 1) * E + i);
           }
+          mask_rd(k + MF);
           slot_extra(k);
           fence();
         }
@@ -419,6 +467,24 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       // Prologue: L/Delta of tiles 0-3, Q/dO of tiles 0 and 1 and most of tile 2's
       // copies; all landed; L/Delta of tiles 0 and 1 fixed (steps 0 and 1
       // fix those of tiles 2 and 3).
+      // Mask staging: element r of half `half` of tile (g, t) into sM[wave][r].
+      auto mask_src = [&](int g) {
+        return raw_rsrc(a.mask + (int64_t)b * a.msb + (int64_t)(kvh * a.group + g) * a.msh, a.mask_rec);
+      };
+      auto mask_vb = [&](int t, int half) { return m_lvo + (uint32_t)(qb + t * BQ + 32 * half) * msq4; };
+      auto mask_cp = [&](rsrc_t rs, uint32_t vb0, int r) {
+        dma_buf4(rs, mad24(8 * (r >> 2) + (r & 3), msq4, vb0), lds_addr(&sM[wave][r][0]));
+      };
+      // The cursor cm names tile it+1, whose half 0 section C of step it stages.
+      Cursor cm{0, 0};
+      if constexpr (MASK) {
+        const rsrc_t rs = mask_src(0);
+        const uint32_t v0 = mask_vb(0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mask_cp(rs, v0, r);
+        advance(cm);
+      }
+
       Cursor cq{0, 0}, cl{0, 0};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -456,7 +522,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         f32x16 z{};
         prefetch_all(pre, 0, 0, 0, 0, 0);
         // a section with no exp/dS work to overlap: only its S/dP result is kept
-        sec_sdp_ew(std::true_type{}, 0, 0, s0, dp0, pre, 0, 0, 0, qb, 0, z, z, pm, ds, trp, [](int) {});
+        sec_sdp_ew(std::true_type{}, 0, 0, s0, dp0, pre, 0, 0, qb, z, z, pm, ds, trp, [](int) {});
         mfma_drain(s0, dp0);  // read by the first step's exp/dS after only a few instructions
         prefetch_all(pre, 1, 0, 0, 0, 0);  // for section A of step 0
       }
@@ -489,9 +555,18 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
             if (slot == n) prefetch(pre, p, ms, sts, lsts, me, lste);
           }
         };
-        // A: S/dP of half 1 with exp/dS of half 0; the second half of tile it+2's copies
-        sec_sdp_ew(full_c, 1, stq, s1, dp1, pre, 0, stq, lst, qt, h, s0, dp0, pm, ds, trp,
-                   [&](int k) { copies_at(pend, NC / 2 + PER, k, NSD); });
+        // A: S/dP of half 1 with exp/dS of half 0; the last quarter of tile it+2's copies.
+        // Each slot then stages the mask of half 1 of this tile in place of the
+        // half-0 elements it used.
+        const rsrc_t mrs_a = mask_src(g);
+        const uint32_t mvb_a = MASK ? mask_vb(t, 1) : 0u;
+        sec_sdp_ew(full_c, 1, stq, s1, dp1, pre, 0, stq, qt, s0, dp0, pm, ds, trp, [&](int k) {
+          copies_at(pend, NC / 2 + PER, k, NSD);
+          if constexpr (MASK) {
+#pragma unroll
+            for (int i = 0; i < 16 / NSD; ++i) mask_cp(mrs_a, mvb_a, k * (16 / NSD) + i);
+          }
+        });
         wait_prev();  // tile it+1 landed everywhere once all waves pass the barrier
         barrier_only();
         issue_ld(cl, lst4);
@@ -504,10 +579,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           pre_at(n, 0, stq1, lst1, 1, lst);
           if (n == NDK / 2) fix_rd(lst2);  // L/Delta of tile it+2 (its copy landed before this step's barrier)
         });
-        // C: S/dP of half 0 of tile it+1 with exp/dS of half 1
-        sec_sdp_ew(full_c, 0, stq1, s0, dp0, pre, 1, stq, lst, qt, h, s1, dp1, pm, ds, trp, [&](int k) {
+        // C: S/dP of half 0 of tile it+1 with exp/dS of half 1; each slot then
+        // stages the mask of half 0 of tile it+1 in place of the elements it used
+        const rsrc_t mrs_c = mask_src(cm.g);
+        const uint32_t mvb_c = MASK ? mask_vb(cm.t, 0) : 0u;
+        sec_sdp_ew(full_c, 0, stq1, s0, dp0, pre, 1, stq, qt, s1, dp1, pm, ds, trp, [&](int k) {
           copies_at(next, PER, k, NSD);
           if (k == 1) fix_wr(lst2);
+          if constexpr (MASK) {
+#pragma unroll
+            for (int i = 0; i < 16 / NSD; ++i) mask_cp(mrs_c, mvb_c, k * (16 / NSD) + i);
+          }
         });
         // D: dV/dK of half 1; prefetch for A of the next step
         sec_dkv(1, stq, trp, pm, ds, [&](int n) {
@@ -516,6 +598,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         });
         pend = next;
         advance(cq);
+        if constexpr (MASK) advance(cm);
         ++it;
       };
 

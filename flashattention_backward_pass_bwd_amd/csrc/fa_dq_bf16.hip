@@ -57,11 +57,22 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
   constexpr int PF = NDQ < 6 ? NDQ : 6;     // S/dP operand reads in flight
   constexpr int NC = 2 * NIW;               // copies per tile per wave
   constexpr int PER = NC / 4;               // copies per section
+  // Mask staging (MASK): element r of a half is copied into sM right after the
+  // same element of the other half was used (sections A and C, the slot of
+  // element r), and read MF slots before its own use two sections later.  Of
+  // the copies issued after it, at least 16 - E*(MF+1) mask copies and PER - 1
+  // tile copies are issued before that read (E elements per slot), so waiting
+  // for at most kMaskWait accesses in flight covers it.
+  constexpr int MF = 2;
+  constexpr int kMaskWait = 16 - (16 / NSD) * (MF + 1) + PER - 1;
+  static_assert(kMaskWait >= 0, "mask staging wait");
   static_assert(NC % 4 == 0 && NDQ % PER == 0 && NSD % PER == 0, "a tile's copies spread over four sections");
   static_assert(2 * NP <= NSD && PF <= NSD && PF <= NDQ, "prefetches fit their sections");
 
   // Ring stage s holds the K tile (sT[s][0]) and the V tile (sT[s][1]).
   __shared__ __attribute__((aligned(16))) __bf16 sT[NST][2][TILE];
+  // Mask values of one exp/dS half per wave: element r of lane l at sM[wave][r][l].
+  __shared__ __attribute__((aligned(16))) float sM[MASK ? 4 : 1][MASK ? 16 : 1][64];
 
   const int nbh = a.B * a.Hq;
   const int wi = blockIdx.x / nbh;
@@ -119,6 +130,10 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
     const float del = il < a.Sq ? Dl[lrow] : 0.f;
     uint32_t rk = 0;
     if constexpr (DROP) rk = drop_row_key(a, b, h, il);
+    // Mask reads: byte offset of element (row, key) in the (b, h) slice is
+    // row*msq*4 + key*msk*4; lanes fix the row (clamped) and the 4-key group.
+    const uint32_t msk4 = MASK ? (uint32_t)a.msk * 4u : 0u;
+    const uint32_t m_lvo = MASK ? ((uint32_t)min(il, a.Sq - 1) * (uint32_t)a.msq + 4u * h2 * (uint32_t)a.msk) * 4u : 0u;
     f32x16 accq[DB];
 #pragma unroll
     for (int d = 0; d < DB; ++d) accq[d] = f32x16{};
@@ -191,28 +206,38 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
       // tile kt (values se, dpe) and with the transposed reads of the first NP
       // MFMAs of that half's dQ (stage ste).
       auto sec_sdp_ew = [&](auto full_c, int ms, int sts, f32x16& s, f32x16& dp, const bf16x8 (&pre)[PF], int me,
-                            int ste, int kt, const f32x16& se, const f32x16& dpe, bf16x8 (&dsc)[2],
-                            bf16x4 (&trp)[2 * NP], auto&& slot_extra) {
+                            int ste, int kt, const f32x16& se, const f32x16& dpe,
+                            bf16x8 (&dsc)[2], bf16x4 (&trp)[2 * NP], auto&& slot_extra) {
         constexpr bool FULL = decltype(full_c)::value;
         bf16x8 op[8];
 #pragma unroll
         for (int k = 0; k < PF; ++k) op[k] = pre[k];
-        const int dl0 = kt - il;  // d = j - i = dl0 + key
-        const int klim = a.Sk - kt;
-        const bool iin = il < a.Sq;
-        const int ic = min(il, a.Sq - 1);
+        // Visible keys of this lane's row in the tile: d = j - i in (dlo, dhi), key
+        // and row in range, i.e. tile keys [lo, hi).  Element r sits at key
+        // 32*me + 4*h2 + c(r), c(r) = 8*(r/4) + r%4, so it is visible iff
+        // c(r) - lb < span (unsigned) with lb = lo - 32*me - 4*h2.
+        int lb = 0;
+        uint32_t span = 0;
+        if constexpr (!FULL) {
+          // no overflow: |dl0| <= 2^29 + 128 and the bounds lie within +-(2^30 + 1)
+          const int dl0 = kt - il;  // d = dl0 + key
+          const int lo = max(vb.dlo - dl0 + 1, 0);
+          const int hi = il < a.Sq ? min(vb.dhi - dl0, a.Sk - kt) : 0;
+          span = (uint32_t)max(hi - lo, 0);
+          lb = lo - 32 * me - 4 * h2;
+        }
+        // key part of the dropout draw of element r: (kt + 32*me + 4*h2 + c(r)) * 0x9E3779B9
+        const uint32_t jb = DROP ? (uint32_t)(kt + 32 * me + 4 * h2) * 0x9E3779B9u : 0u;
         float pv[16], dv[16];
-        // exp of element r (C-layout register r of half me: key 32me + 8(r/4) + 4h2 + r%4);
-        // se holds S*scale*log2(e) - L*log2(e).
+        float mk[16];  // mask values of the half (MASK), read ahead from sM
+        // exp of element r (C-layout register r of half me); se holds
+        // S*scale*log2(e) - L*log2(e).
         auto ew_exp = [&](int r) {
-          const int key = 32 * me + 8 * (r >> 2) + 4 * h2 + (r & 3);
           float x = se[r];
           if constexpr (!FULL) {
-            const int dd = dl0 + key;
-            bool ok = iin && key < klim && dd > vb.dlo && dd < vb.dhi;
+            bool ok = (uint32_t)(8 * (r >> 2) + (r & 3) - lb) < span;
             if constexpr (MASK) {
-              // clamped indices keep the load in bounds; ok discards out-of-range elements
-              const float mv = mask_at(a, b, h, ic, min(kt + key, a.Sk - 1));
+              const float mv = mk[r];
               ok = ok && !(mv <= kMaskedSentinel);
               x = __builtin_fmaf(mv, kLog2e, x);
             }
@@ -223,8 +248,8 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         // dS of element r, one slot after its exp; odd r packs the pair.
         auto ew_ds = [&](int r) {
           if constexpr (DROP) {
-            const int key = 32 * me + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            const float mm = drop_keep(rk, kt + key, a.drop_thr) ? a.drop_inv : 0.f;
+            const uint32_t jg = jb + (uint32_t)(8 * (r >> 2) + (r & 3)) * 0x9E3779B9u;
+            const float mm = fmix32(rk ^ jg) >= a.drop_thr ? a.drop_inv : 0.f;
             dv[r] = pv[r] * (dpe[r] * mm - del);
           } else {
             dv[r] = pv[r] * dpe[r];
@@ -234,6 +259,19 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
             dsc[r >> 3][r & 7] = (__bf16)dv[r];
           }
         };
+        // Mask values of the half, read from this wave's LDS staging MF slots ahead
+        // of their use, each once its copy (issued two sections earlier) landed.
+        auto mask_rd = [&](int kk) {
+          if constexpr (MASK && !FULL) {
+            if (kk < NSD) {
+              wait_vmcnt<kMaskWait>();
+#pragma unroll
+              for (int i = 0; i < 16 / NSD; ++i) mk[kk * (16 / NSD) + i] = sM[wave][kk * (16 / NSD) + i][lane];
+            }
+          }
+        };
+#pragma unroll
+        for (int k = 0; k < MF; ++k) mask_rd(k);
         fence();
 #pragma unroll
         for (int k = 0; k < NSD; ++k) {
@@ -262,6 +300,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
 #pragma unroll
             for (int i = 0; i < E; ++i) ew_ds((k - 1) * E + i);
           }
+          mask_rd(k + MF);
           slot_extra(k);
           fence();
         }
@@ -296,6 +335,21 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
           fence();
         }
       };
+
+      // Mask staging: element r of half `half` of key tile tt into sM[wave][r].
+      // unused (and dropped) without a mask
+      const rsrc_t mrs = raw_rsrc(a.mask + (int64_t)b * a.msb + (int64_t)h * a.msh, a.mask_rec);
+      auto mask_vb = [&](int tt, int half) {
+        return m_lvo + (uint32_t)(kb + min(tt, ntiles - 1) * BK + 32 * half) * msk4;
+      };
+      auto mask_cp = [&](uint32_t vb0, int r) {
+        dma_buf4(mrs, mad24(8 * (r >> 2) + (r & 3), msk4, vb0), lds_addr(&sM[wave][r][0]));
+      };
+      if constexpr (MASK) {
+        const uint32_t v0 = mask_vb(0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mask_cp(v0, r);
+      }
 
       // Prologue: K/V of tiles 0 and 1 and three quarters of tile 2's copies; all
       // landed.  A tile's copies go out over four sections from the barrier on
@@ -345,10 +399,21 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         auto pre_at = [&](int n, int ms) {
           if (n >= NDQ - PF) pre[n - (NDQ - PF)] = rd_op(ms, stq1, n - (NDQ - PF));
         };
-        // A: S/dP of half 1 with exp/dS of half 0; the last quarter of tile it+2's copies
-        sec_sdp_ew(full_c, 1, stq, s1, dp1, pre, 0, stq, kt, s0, dp0, ds, trp,
-                   [&](int k) { copies_at(pend, NC - PER, k, NSD); });
-        wait_vmcnt<NC>();  // tile it+1 landed everywhere once all waves pass the barrier
+        // A: S/dP of half 1 with exp/dS of half 0; the last quarter of tile it+2's copies.
+        // Each slot then stages the mask of half 1 of this tile in place of the
+        // half-0 elements it used.
+        const uint32_t mvb_a = MASK ? mask_vb(it, 1) : 0u;
+        sec_sdp_ew(full_c, 1, stq, s1, dp1, pre, 0, stq, kt, s0, dp0, ds, trp, [&](int k) {
+          copies_at(pend, NC - PER, k, NSD);
+          if constexpr (MASK) {
+#pragma unroll
+            for (int i = 0; i < 16 / NSD; ++i) mask_cp(mvb_a, k * (16 / NSD) + i);
+          }
+        });
+        // tile it+1 landed everywhere once all waves pass the barrier (with a mask,
+        // the 32 mask copies of a step count too, and those of section A issued
+        // after its last tile copy, 16 / PER of them)
+        wait_vmcnt<NC + (MASK ? 32 + 16 / PER : 0)>();
         barrier_only();
         const Job next = job_of(it + 3, stq3);
         // B: dQ of half 0; prefetch for C
@@ -356,9 +421,16 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
           copies_at(next, 0, n, NDQ);
           pre_at(n, 0);
         });
-        // C: S/dP of half 0 of tile it+1 with exp/dS of half 1
-        sec_sdp_ew(full_c, 0, stq1, s0, dp0, pre, 1, stq, kt, s1, dp1, ds, trp,
-                   [&](int k) { copies_at(next, PER, k, NSD); });
+        // C: S/dP of half 0 of tile it+1 with exp/dS of half 1; each slot then
+        // stages the mask of half 0 of tile it+1 in place of the elements it used
+        const uint32_t mvb_c = MASK ? mask_vb(it + 1, 0) : 0u;
+        sec_sdp_ew(full_c, 0, stq1, s0, dp0, pre, 1, stq, kt, s1, dp1, ds, trp, [&](int k) {
+          copies_at(next, PER, k, NSD);
+          if constexpr (MASK) {
+#pragma unroll
+            for (int i = 0; i < 16 / NSD; ++i) mask_cp(mvb_c, k * (16 / NSD) + i);
+          }
+        });
         // D: dQ of half 1; prefetch for A of the next step
         sec_dq(1, stq, trp, ds, [&](int n) {
           copies_at(next, 2 * PER, n, NDQ);

@@ -75,6 +75,32 @@ __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t 
                : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)));
 }
 
+// Buffer descriptor of a raw fp32 range of `bytes` bytes at base: a read at a
+// byte offset past the range returns 0 instead of touching memory.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Direct raw-buffer->LDS copy of one fp32 per lane: lane l's value at byte
+// offset voff lands at LDS byte address lds + 4*l (a zero when voff is past the
+// range).  Inline assembly like dma16, with M0 likewise; ordered after the
+// reads of the LDS it overwrites.
+__device__ __forceinline__ void dma_buf4(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
+// a*b + c with a, b < 2^24 (one full-rate VALU instruction); a must fold to
+// an inline constant (0 .. 64) once loops are unrolled, b is wave-uniform.
+__device__ __forceinline__ uint32_t mad24(int a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(r) : "i"(a), "s"(b), "v"(c));
+  return r;
+}
+
 // Block barrier without a memory fence: LDS writes of this wave are complete
 // (lgkmcnt(0)) but outstanding global->LDS copies are not waited for, so the
 // copies of later tiles stay in flight across it.  Callers wait for the copies

@@ -42,7 +42,8 @@ typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = -1,        /* a required pointer is NULL */
   FA_ERR_SHAPE = -2,       /* a size <= 0, or num_heads % num_kv_heads != 0 */
-  FA_ERR_UNSUPPORTED = -3, /* head_dim / dtype / history length / row stride outside the built kernels */
+  FA_ERR_UNSUPPORTED = -3, /* head_dim / dtype / history length / row stride outside the built kernels,
+                              or seq_q, seq_k, causal_offset or window above 2^29 */
   FA_ERR_ALIGN = -4,       /* base or row stride not a multiple of 16 bytes, or D not unit-stride */
   FA_ERR_ARG = -5,         /* dropout_p not in [0,1), causal_offset < 0, window < 0, bad stride */
   FA_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
@@ -68,7 +69,11 @@ typedef void* fa_stream_t;
  * by choosing the strides.  head_dim is unit-stride.  The four query-side
  * tensors share one stride set; the four key-side tensors share the other.
  * The sequence strides q_stride_s and kv_stride_s may not exceed 2^24
- * elements (FA_ERR_UNSUPPORTED): tile copies use 32-bit row offsets.
+ * elements (FA_ERR_UNSUPPORTED): tile copies use 32-bit row offsets.  For
+ * bf16 with a mask, mask_stride_q and mask_stride_k must be below 2^22
+ * elements and one (b, h) slice of the mask, ((seq_q-1)*mask_stride_q +
+ * (seq_k-1)*mask_stride_k + 1)*4 bytes, must fit in 32 bits
+ * (FA_ERR_UNSUPPORTED).
  * L (natural-log log-sum-exp from the forward) and Delta are fp32,
  * contiguous [batch, num_heads, seq_q].
  *
