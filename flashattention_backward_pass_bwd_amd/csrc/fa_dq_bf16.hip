@@ -34,7 +34,9 @@
 
 namespace fa {
 
-template <int D, bool MASK, bool DROP>
+// MK: 0 no mask, 1 a mask of any strides, 2 a mask whose keys are contiguous and
+// whose 4-key groups are 16-byte aligned (read four keys per lane and copy).
+template <int D, int MK, bool DROP>
 __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __bf16* __restrict__ Q,
                                                          const __bf16* __restrict__ K,
                                                          const __bf16* __restrict__ V,
@@ -42,6 +44,8 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
                                                          const float* __restrict__ L,
                                                          const float* __restrict__ Dl,
                                                          __bf16* __restrict__ dQ, int nqb, int paired) {
+  constexpr bool MASK = MK != 0;
+  constexpr bool MVEC = MK == 2;
   constexpr int BK = 64;
   constexpr int NCH = D / 8;
   constexpr int KS = D / 16;
@@ -66,6 +70,17 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
   constexpr int MF = 2;
   constexpr int kMaskWait = 16 - (16 / NSD) * (MF + 1) + PER - 1;
   static_assert(kMaskWait >= 0, "mask staging wait");
+  // With MVEC, group g (elements 4g .. 4g+3, one 16-byte copy per lane) is copied
+  // after its last element's slot and read at the start of the previous group's
+  // slots (SG slots per group): at least 2 group copies and PER tile copies are
+  // issued in between, so waiting for at most 1 + PER accesses in flight covers it.
+  constexpr int SG = 4 / (16 / NSD);
+  constexpr int kMaskWaitV = 1 + PER;
+  // Mask copies of section A issued after its last tile copy (slot sl).
+  constexpr int sl = (PER - 1) * (NSD / PER);
+  constexpr int kMaskLateA = MVEC ? (SG - 1 >= sl) + (2 * SG - 1 >= sl) + (3 * SG - 1 >= sl) + (4 * SG - 1 >= sl)
+                                  : 16 / PER;
+  constexpr int kMaskPerStep = MVEC ? 8 : 32;
   static_assert(NC % 4 == 0 && NDQ % PER == 0 && NSD % PER == 0, "a tile's copies spread over four sections");
   static_assert(2 * NP <= NSD && PF <= NSD && PF <= NDQ, "prefetches fit their sections");
 
@@ -132,7 +147,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
     if constexpr (DROP) rk = drop_row_key(a, b, h, il);
     // Mask reads: byte offset of element (row, key) in the (b, h) slice is
     // row*msq*4 + key*msk*4; lanes fix the row (clamped) and the 4-key group.
-    const uint32_t msk4 = MASK ? (uint32_t)a.msk * 4u : 0u;
+    const uint32_t msk4 = MASK ? (uint32_t)a.msk * 4u : 0u;  // 4 with MVEC
     const uint32_t m_lvo = MASK ? ((uint32_t)min(il, a.Sq - 1) * (uint32_t)a.msq + 4u * h2 * (uint32_t)a.msk) * 4u : 0u;
     f32x16 accq[DB];
 #pragma unroll
@@ -262,7 +277,16 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         // Mask values of the half, read from this wave's LDS staging MF slots ahead
         // of their use, each once its copy (issued two sections earlier) landed.
         auto mask_rd = [&](int kk) {
-          if constexpr (MASK && !FULL) {
+          if constexpr (MVEC && !FULL) {
+            // group g = kk / SG + 1 at the start of group g - 1's slots (kk < 0: group 0)
+            const int g = kk < 0 ? 0 : kk / SG + 1;
+            if ((kk < 0 || kk % SG == 0) && g < 4) {
+              wait_vmcnt<kMaskWaitV>();
+              const f32x4 v4 = *reinterpret_cast<const f32x4*>(&sM[wave][4 * g][4 * lane]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) mk[4 * g + e] = v4[e];
+            }
+          } else if constexpr (MASK && !FULL) {
             if (kk < NSD) {
               wait_vmcnt<kMaskWait>();
 #pragma unroll
@@ -270,8 +294,18 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
             }
           }
         };
+        if constexpr (MVEC) {
+          mask_rd(-1);
+        } else {
 #pragma unroll
-        for (int k = 0; k < MF; ++k) mask_rd(k);
+          for (int k = 0; k < MF; ++k) {
+            if constexpr (MASK && !FULL) {
+              wait_vmcnt<kMaskWait>();
+#pragma unroll
+              for (int i = 0; i < 16 / NSD; ++i) mk[k * (16 / NSD) + i] = sM[wave][k * (16 / NSD) + i][lane];
+            }
+          }
+        }
         fence();
 #pragma unroll
         for (int k = 0; k < NSD; ++k) {
@@ -300,7 +334,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
 #pragma unroll
             for (int i = 0; i < E; ++i) ew_ds((k - 1) * E + i);
           }
-          mask_rd(k + MF);
+          mask_rd(MVEC ? k : k + MF);
           slot_extra(k);
           fence();
         }
@@ -345,10 +379,22 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
       auto mask_cp = [&](uint32_t vb0, int r) {
         dma_buf4(mrs, mad24(8 * (r >> 2) + (r & 3), msk4, vb0), lds_addr(&sM[wave][r][0]));
       };
+      // MVEC: keys 8g + 4*h2 .. +3 of the lane's row, to sM[wave][4g .. 4g+3] (16 bytes per lane)
+      auto mask_cpv = [&](uint32_t vb0, int g) { dma_buf16(mrs, vb0 + 32u * g, lds_addr(&sM[wave][4 * g][0])); };
+      // Slot hook of sections A and C: the copies that refill the elements (MVEC:
+      // the groups) whose last use was slot k.
+      auto mask_refill = [&](uint32_t vb0, int k) {
+        if constexpr (MVEC) {
+          if (k % SG == SG - 1) mask_cpv(vb0, k / SG);
+        } else if constexpr (MASK) {
+#pragma unroll
+          for (int i = 0; i < 16 / NSD; ++i) mask_cp(vb0, k * (16 / NSD) + i);
+        }
+      };
       if constexpr (MASK) {
         const uint32_t v0 = mask_vb(0, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mask_cp(v0, r);
+        for (int k = 0; k < NSD; ++k) mask_refill(v0, k);
       }
 
       // Prologue: K/V of tiles 0 and 1 and three quarters of tile 2's copies; all
@@ -405,15 +451,12 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         const uint32_t mvb_a = MASK ? mask_vb(it, 1) : 0u;
         sec_sdp_ew(full_c, 1, stq, s1, dp1, pre, 0, stq, kt, s0, dp0, ds, trp, [&](int k) {
           copies_at(pend, NC - PER, k, NSD);
-          if constexpr (MASK) {
-#pragma unroll
-            for (int i = 0; i < 16 / NSD; ++i) mask_cp(mvb_a, k * (16 / NSD) + i);
-          }
+          mask_refill(mvb_a, k);
         });
         // tile it+1 landed everywhere once all waves pass the barrier (with a mask,
-        // the 32 mask copies of a step count too, and those of section A issued
-        // after its last tile copy, 16 / PER of them)
-        wait_vmcnt<NC + (MASK ? 32 + 16 / PER : 0)>();
+        // the mask copies of a step count too, and those of section A issued after
+        // its last tile copy)
+        wait_vmcnt<NC + (MASK ? kMaskPerStep + kMaskLateA : 0)>();
         barrier_only();
         const Job next = job_of(it + 3, stq3);
         // B: dQ of half 0; prefetch for C
@@ -426,10 +469,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         const uint32_t mvb_c = MASK ? mask_vb(it + 1, 0) : 0u;
         sec_sdp_ew(full_c, 0, stq1, s0, dp0, pre, 1, stq, kt, s1, dp1, ds, trp, [&](int k) {
           copies_at(next, PER, k, NSD);
-          if constexpr (MASK) {
-#pragma unroll
-            for (int i = 0; i < 16 / NSD; ++i) mask_cp(mvb_c, k * (16 / NSD) + i);
-          }
+          mask_refill(mvb_c, k);
         });
         // D: dQ of half 1; prefetch for A of the next step
         sec_dq(1, stq, trp, ds, [&](int n) {
@@ -478,14 +518,14 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
   }
 }
 
-template <int D, bool MASK, bool DROP>
+template <int D, int MK, bool DROP>
 static hipError_t launch_t(const PrefillArgs& a, const void* Q, const void* K, const void* V, const void* dO,
                            const float* L, const float* delta, void* dQ, hipStream_t st) {
   const int nqb = (a.Sq + kDqRowsPerBlock - 1) / kDqRowsPerBlock;
   const int paired = (a.causal && a.window == 0 && nqb > 1) ? 1 : 0;
   const int nwi = paired ? (nqb + 1) / 2 : nqb;
   const unsigned grid = (unsigned)(nwi * a.B * a.Hq);
-  hipLaunchKernelGGL((dq_bf16_kernel<D, MASK, DROP>), dim3(grid), dim3(256), 0, st, a,
+  hipLaunchKernelGGL((dq_bf16_kernel<D, MK, DROP>), dim3(grid), dim3(256), 0, st, a,
                      static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
                      static_cast<const __bf16*>(dO), L, delta, static_cast<__bf16*>(dQ), nqb, paired);
   return hipGetLastError();
@@ -494,12 +534,18 @@ static hipError_t launch_t(const PrefillArgs& a, const void* Q, const void* K, c
 template <int D>
 static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, const void* V, const void* dO,
                            const float* L, const float* delta, void* dQ, hipStream_t st) {
-  const bool mask = a.mask != nullptr;
   const bool drop = a.drop != 0;
-  if (mask && drop) return launch_t<D, true, true>(a, Q, K, V, dO, L, delta, dQ, st);
-  if (mask) return launch_t<D, true, false>(a, Q, K, V, dO, L, delta, dQ, st);
-  if (drop) return launch_t<D, false, true>(a, Q, K, V, dO, L, delta, dQ, st);
-  return launch_t<D, false, false>(a, Q, K, V, dO, L, delta, dQ, st);
+  // keys contiguous and every 4-key group 16-byte aligned: rows, heads and
+  // batches start on 16 bytes
+  const bool vec = a.mask != nullptr && a.msk == 1 && a.msq % 4 == 0 && a.msh % 4 == 0 && a.msb % 4 == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.mask) & 15u) == 0;
+  const int mk = a.mask == nullptr ? 0 : (vec ? 2 : 1);
+  if (mk == 2) return drop ? launch_t<D, 2, true>(a, Q, K, V, dO, L, delta, dQ, st)
+                           : launch_t<D, 2, false>(a, Q, K, V, dO, L, delta, dQ, st);
+  if (mk == 1) return drop ? launch_t<D, 1, true>(a, Q, K, V, dO, L, delta, dQ, st)
+                           : launch_t<D, 1, false>(a, Q, K, V, dO, L, delta, dQ, st);
+  return drop ? launch_t<D, 0, true>(a, Q, K, V, dO, L, delta, dQ, st)
+              : launch_t<D, 0, false>(a, Q, K, V, dO, L, delta, dQ, st);
 }
 
 hipError_t launch_dq_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V,

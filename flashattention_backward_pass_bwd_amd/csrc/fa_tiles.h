@@ -93,6 +93,15 @@ __device__ __forceinline__ void dma_buf4(rsrc_t rsrc, uint32_t voff, uint32_t ld
                : "memory");
 }
 
+// The same for four consecutive fp32 per lane (16 bytes, 16-byte aligned):
+// lane l's values land at lds + 16*l.
+__device__ __forceinline__ void dma_buf16(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
+}
+
 // a*b + c with a, b < 2^24 (one full-rate VALU instruction); a must fold to
 // an inline constant (0 .. 64) once loops are unrolled, b is wave-uniform.
 __device__ __forceinline__ uint32_t mad24(int a, uint32_t b, uint32_t c) {
