@@ -154,34 +154,56 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       // tile t).  A cursor names the tile whose copies are issued next; past
       // the last tile it stays there, so the last copies repeat into stages
       // that are never read and every step runs the same straight-line code.
+      // The cursor also carries the element offsets of the tile's first row in
+      // Q/dO and in L/Delta, moved on by per-pass increments (no multiplies per step).
       struct Cursor {
-        int g, t;
+        int g, t, qt;
+        int64_t qoff, loff;
+      };
+      const int64_t inc_qt = (int64_t)BQ * a.qss;                           // next tile
+      const int64_t inc_qh = a.qsh - (int64_t)(ntq - 1) * BQ * a.qss;       // next head's first tile
+      const int64_t inc_lh = (int64_t)a.Sq - (int64_t)(ntq - 1) * BQ;
+      auto cursor0 = [&]() {
+        const int h0 = kvh * a.group;
+        return Cursor{0, 0, qb, (int64_t)b * a.qsb + (int64_t)h0 * a.qsh + (int64_t)qb * a.qss,
+                      ((int64_t)b * a.Hq + h0) * a.Sq + qb};
       };
       auto advance = [&](Cursor& c) {
-        const int tn = c.t + 1;
-        const bool wrap = tn == ntq;
-        const int gn = c.g + (wrap ? 1 : 0);
-        const bool end = gn == a.group;
-        c.t = end ? c.t : (wrap ? 0 : tn);
-        c.g = end ? c.g : gn;
+        if (c.t + 1 < ntq) {
+          c.t += 1;
+          c.qt += BQ;
+          c.qoff += inc_qt;
+          c.loff += BQ;
+        } else if (c.g + 1 < a.group) {
+          c.t = 0;
+          c.g += 1;
+          c.qt = qb;
+          c.qoff += inc_qh;
+          c.loff += inc_lh;
+        }
       };
       // Q and dO rows of a tile into a ring stage: copy u of this wave fills rows
       // (wave*NIW + u)*RPI + lane/NCH.  Rows past the end repeat the last row;
       // they are never counted.  Per-lane offsets are 32-bit, relative to the
       // tile's first row (the host bounds the row stride).
-      auto qdo_base = [&](const Cursor& c) {
-        const int h = kvh * a.group + c.g;
-        const int qt = qb + c.t * BQ;
-        return (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)qt * a.qss;
-      };
       // A pending set of copies: the tile's first row in Q and in dO, the LDS
       // address of this wave's first Q row in the ring stage, the last row.
       struct Job {
         const __bf16* qp;
         const __bf16* dop;
         uint32_t lds;
-        int lim;
+        uint32_t lim2;  // byte offset of the tile's last row (rows past it repeat it), at most 2*BQ*qss
       };
+      // Per-lane byte offsets of copy pair i's row (cp_off) and of its chunk alone
+      // (cp_chk): a row r at most the last row lim is read at cp_off, else the last
+      // row's chunk at lim2 + cp_chk, i.e. min(cp_off, lim2 + cp_chk).
+      uint32_t cp_off[NIW], cp_chk[NIW];
+#pragma unroll
+      for (int i = 0; i < NIW; ++i) {
+        const int r = (wave * NIW + i) * RPI + cp_row;
+        cp_chk[i] = 16u * (uint32_t)(cp_pc ^ swz<D>(r));
+        cp_off[i] = 2u * (uint32_t)r * (uint32_t)a.qss + cp_chk[i];
+      }
       constexpr int NC = 2 * NIW;  // copies per tile per wave
       constexpr int PER = NC / 4;  // copies per section
       static_assert(NC % 4 == 0, "a tile's copies spread over four sections");
@@ -195,14 +217,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       constexpr int kMaskWait = 16 - (16 / NSD) * (MF + 1) + PER - 1;
       static_assert(kMaskWait >= 0, "mask staging wait");
       auto job_of = [&](const Cursor& c, int stage) {
-        const int64_t base = qdo_base(c);
-        return Job{Q + base, dO + base, lds_addr(&sT[stage][0][wave * NIW * RPI * D]), a.Sq - 1 - (qb + c.t * BQ)};
+        const uint32_t lim = (uint32_t)min(a.Sq - 1 - c.qt, BQ);
+        return Job{Q + c.qoff, dO + c.qoff, lds_addr(&sT[stage][0][wave * NIW * RPI * D]), 2u * lim * (uint32_t)a.qss};
       };
       // Copy u (0 .. 2*NIW-1; even: Q, odd: dO) of a job.
       auto issue_job = [&](const Job& j, int u) {
-        const int blk = wave * NIW + (u >> 1);
-        const int r = blk * RPI + cp_row;
-        const uint32_t off = 2u * ((uint32_t)min(r, j.lim) * (uint32_t)a.qss + 8u * (uint32_t)(cp_pc ^ swz<D>(r)));
+        const uint32_t off = min(cp_off[u >> 1], j.lim2 + cp_chk[u >> 1]);
         const uint32_t lds = j.lds + 2u * (uint32_t)((u >> 1) * RPI * D + (u & 1) * TILE);
         dma16((u & 1) ? j.dop : j.qp, off, lds);
       };
@@ -219,14 +239,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       // the end repeat the last row), and the tile's dropout row keys (lanes
       // 0-15 of each wave, 16 rows per wave).
       auto issue_ld = [&](const Cursor& c, int lst) {
-        const int h = kvh * a.group + c.g;
-        const int qt = qb + c.t * BQ;
         if (wave < 2) {
-          const float* src = (wave == 0 ? L : Dl) + (((int64_t)b * a.Hq + h) * a.Sq + qt);
-          dma4(src, 4u * (uint32_t)min(lane, a.Sq - 1 - qt), lds_addr(wave == 0 ? sL[lst] : sDel[lst]));
+          const float* src = (wave == 0 ? L : Dl) + c.loff;
+          dma4(src, 4u * (uint32_t)min(lane, a.Sq - 1 - c.qt), lds_addr(wave == 0 ? sL[lst] : sDel[lst]));
         }
         if constexpr (DROP) {
-          if (lane < 16) sRK[lst][16 * wave + lane] = drop_row_key(a, b, h, qt + 16 * wave + lane);
+          // the row's global index ((b*Hq + h)*Sq + i) mod 2^32 (drop_row_key)
+          if (lane < 16) sRK[lst][16 * wave + lane] = fmix32((uint32_t)c.loff + (uint32_t)(16 * wave + lane) + a.seed_mix);
         }
       };
       // Once a stage's L/Delta landed and a barrier passed, each wave rewrites 16
@@ -471,21 +490,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       auto mask_src = [&](int g) {
         return raw_rsrc(a.mask + (int64_t)b * a.msb + (int64_t)(kvh * a.group + g) * a.msh, a.mask_rec);
       };
-      auto mask_vb = [&](int t, int half) { return m_lvo + (uint32_t)(qb + t * BQ + 32 * half) * msq4; };
+      auto mask_vb = [&](int qt, int half) { return m_lvo + (uint32_t)(qt + 32 * half) * msq4; };
       auto mask_cp = [&](rsrc_t rs, uint32_t vb0, int r) {
         dma_buf4(rs, mad24(8 * (r >> 2) + (r & 3), msq4, vb0), lds_addr(&sM[wave][r][0]));
       };
       // The cursor cm names tile it+1, whose half 0 section C of step it stages.
-      Cursor cm{0, 0};
+      Cursor cm = cursor0();
       if constexpr (MASK) {
         const rsrc_t rs = mask_src(0);
-        const uint32_t v0 = mask_vb(0, 0);
+        const uint32_t v0 = mask_vb(qb, 0);
 #pragma unroll
         for (int r = 0; r < 16; ++r) mask_cp(rs, v0, r);
         advance(cm);
       }
 
-      Cursor cq{0, 0}, cl{0, 0};
+      Cursor cq = cursor0(), cl = cursor0();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         issue_ld(cl, s);
@@ -559,7 +578,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         // Each slot then stages the mask of half 1 of this tile in place of the
         // half-0 elements it used.
         const rsrc_t mrs_a = mask_src(g);
-        const uint32_t mvb_a = MASK ? mask_vb(t, 1) : 0u;
+        const uint32_t mvb_a = MASK ? mask_vb(qt, 1) : 0u;
         sec_sdp_ew(full_c, 1, stq, s1, dp1, pre, 0, stq, qt, s0, dp0, pm, ds, trp, [&](int k) {
           copies_at(pend, NC / 2 + PER, k, NSD);
           if constexpr (MASK) {
@@ -569,6 +588,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         });
         wait_prev();  // tile it+1 landed everywhere once all waves pass the barrier
         barrier_only();
+        const Cursor cl_now = cl;  // tile it+4: the copies' cursor of the next step
         issue_ld(cl, lst4);
         advance(cl);
         fence();
@@ -582,7 +602,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         // C: S/dP of half 0 of tile it+1 with exp/dS of half 1; each slot then
         // stages the mask of half 0 of tile it+1 in place of the elements it used
         const rsrc_t mrs_c = mask_src(cm.g);
-        const uint32_t mvb_c = MASK ? mask_vb(cm.t, 0) : 0u;
+        const uint32_t mvb_c = MASK ? mask_vb(cm.qt, 0) : 0u;
         sec_sdp_ew(full_c, 0, stq1, s0, dp0, pre, 1, stq, qt, s1, dp1, pm, ds, trp, [&](int k) {
           copies_at(next, PER, k, NSD);
           if (k == 1) fix_wr(lst2);
@@ -597,7 +617,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           pre_at(n, 1, stq1, lst1, 0, lst1);
         });
         pend = next;
-        advance(cq);
+        cq = cl_now;
         if constexpr (MASK) advance(cm);
         ++it;
       };

@@ -185,17 +185,35 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         const __bf16* kp;  // first row of the tile in K and in V
         const __bf16* vp;
         uint32_t lds;      // LDS address of this wave's first K row in the stage
-        int lim;
+        uint32_t lim2;     // byte offset of the tile's last row (rows past it repeat it), at most 2*BK*kss
+      };
+      // Per-lane byte offsets of copy pair i's row (cp_off) and of its chunk alone
+      // (cp_chk): a row r at most the last row lim is read at cp_off, else the last
+      // row's chunk at lim2 + cp_chk, i.e. min(cp_off, lim2 + cp_chk).
+      uint32_t cp_off[NIW], cp_chk[NIW];
+#pragma unroll
+      for (int i = 0; i < NIW; ++i) {
+        const int r = (wave * NIW + i) * RPI + cp_row;
+        cp_chk[i] = 16u * (uint32_t)(cp_pc ^ swz<D>(r));
+        cp_off[i] = 2u * (uint32_t)r * (uint32_t)a.kss + cp_chk[i];
+      }
+      // A job from a tile's first key and its element offset in K/V.
+      auto job_at = [&](int kt, int64_t base, int stage) {
+        const uint32_t lim = (uint32_t)min(a.Sk - 1 - kt, BK);
+        return Job{K + base, V + base, lds_addr(&sT[stage][0][wave * NIW * RPI * D]), 2u * lim * (uint32_t)a.kss};
       };
       auto job_of = [&](int tt, int stage) {
         const int kt = kb + min(tt, ntiles - 1) * BK;
-        const int64_t base = (int64_t)b * a.ksb + (int64_t)kt * a.kss + (int64_t)kvh * a.ksh;
-        return Job{K + base, V + base, lds_addr(&sT[stage][0][wave * NIW * RPI * D]), a.Sk - 1 - kt};
+        return job_at(kt, (int64_t)b * a.ksb + (int64_t)kt * a.kss + (int64_t)kvh * a.ksh, stage);
       };
+      // The copies' tile of the next step (it+3, held at the last tile), moved on
+      // by one tile per step without multiplies.
+      int ct_kt = kb + min(3, ntiles - 1) * BK;
+      int64_t ct_base = (int64_t)b * a.ksb + (int64_t)ct_kt * a.kss + (int64_t)kvh * a.ksh;
+      const int kt_last = kb + (ntiles - 1) * BK;
+      const int64_t inc_kt = (int64_t)BK * a.kss;
       auto issue_job = [&](const Job& j, int u) {
-        const int blk = wave * NIW + (u >> 1);
-        const int r = blk * RPI + cp_row;
-        const uint32_t off = 2u * ((uint32_t)min(r, j.lim) * (uint32_t)a.kss + 8u * (uint32_t)(cp_pc ^ swz<D>(r)));
+        const uint32_t off = min(cp_off[u >> 1], j.lim2 + cp_chk[u >> 1]);
         const uint32_t lds = j.lds + 2u * (uint32_t)((u >> 1) * RPI * D + (u & 1) * TILE);
         dma16((u & 1) ? j.vp : j.kp, off, lds);
       };
@@ -458,7 +476,11 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         // its last tile copy)
         wait_vmcnt<NC + (MASK ? kMaskPerStep + kMaskLateA : 0)>();
         barrier_only();
-        const Job next = job_of(it + 3, stq3);
+        const Job next = job_at(ct_kt, ct_base, stq3);
+        if (ct_kt < kt_last) {
+          ct_kt += BK;
+          ct_base += inc_kt;
+        }
         // B: dQ of half 0; prefetch for C
         sec_dq(0, stq, trp, ds, [&](int n) {
           copies_at(next, 0, n, NDQ);
