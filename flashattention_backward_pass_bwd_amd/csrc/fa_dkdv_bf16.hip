@@ -314,12 +314,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       constexpr int NPRE = PF + 8 + (DROP ? 4 : 0);  // LDS reads of a prefetch
       // Prefetch read p (0 .. NPRE-1) for a section computing S/dP of half ms
       // (stage sts, L ring stage lsts) and exp/dS of half me (L ring stage lste).
+      // Read order: the chain seeds first (the section's first two MFMAs need
+      // them), then the dropout row keys, then the A operands in MFMA order.
       auto prefetch = [&](SdpPre& pre, int p, int ms, int sts, int lsts, int me, int lste) {
-        if (p < PF) {
-          pre.op[p] = rd_op(ms, sts, p);
-          return;
-        }
-        p -= PF;
         if (p < 4) {
           const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[lsts][32 * ms + 8 * p + 4 * h2]);
 #pragma unroll
@@ -338,7 +335,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           return;
         }
         p -= 4;
-        if constexpr (DROP) pre.rk[p] = *reinterpret_cast<const u32x4*>(&sRK[lste][32 * me + 8 * p + 4 * h2]);
+        if constexpr (DROP) {
+          if (p < 4) {
+            pre.rk[p] = *reinterpret_cast<const u32x4*>(&sRK[lste][32 * me + 8 * p + 4 * h2]);
+            return;
+          }
+          p -= 4;
+        }
+        pre.op[p] = rd_op(ms, sts, p);
       };
       auto prefetch_all = [&](SdpPre& pre, int ms, int sts, int lsts, int me, int lste) {
 #pragma unroll
@@ -570,7 +574,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         auto pre_at = [&](int n, int ms, int sts, int lsts, int me, int lste) {
 #pragma unroll
           for (int p = 0; p < NPRE; ++p) {
-            const int slot = NPRE <= NDK ? NDK - NPRE + p : p * NDK / NPRE;
+            const int slot = NPRE <= NDK ? p : p * NDK / NPRE;
             if (slot == n) prefetch(pre, p, ms, sts, lsts, me, lste);
           }
         };
