@@ -75,6 +75,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
   __shared__ __attribute__((aligned(16))) uint32_t sRK[DROP ? NSL : 1][DROP ? BQ : 1];
   // Mask values of one exp/dS half per wave: element r of lane l at sM[wave][r][l].
   __shared__ __attribute__((aligned(16))) float sM[MASK ? 4 : 1][MASK ? 16 : 1][64];
+  // Landing place of the per-step writes that a wave or lane has no row for (so
+  // that every wave runs the same code without branches); never read.
+  __shared__ __attribute__((aligned(16))) float sDum[2][64];
 
   const int nbh = a.B * a.Hkv;
   const int wi = blockIdx.x / nbh;
@@ -168,19 +171,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         return Cursor{0, 0, qb, (int64_t)b * a.qsb + (int64_t)h0 * a.qsh + (int64_t)qb * a.qss,
                       ((int64_t)b * a.Hq + h0) * a.Sq + qb};
       };
-      auto advance = [&](Cursor& c) {
-        if (c.t + 1 < ntq) {
-          c.t += 1;
-          c.qt += BQ;
-          c.qoff += inc_qt;
-          c.loff += BQ;
-        } else if (c.g + 1 < a.group) {
-          c.t = 0;
-          c.g += 1;
-          c.qt = qb;
-          c.qoff += inc_qh;
-          c.loff += inc_lh;
-        }
+      auto advance = [&](Cursor& c) {  // next tile, else next head's first, else stay
+        const bool nx = c.t + 1 < ntq;
+        const bool ng = c.g + 1 < a.group;
+        c.qoff += nx ? inc_qt : (ng ? inc_qh : 0);
+        c.loff += nx ? (int64_t)BQ : (ng ? inc_lh : 0);
+        c.qt = nx ? c.qt + BQ : (ng ? qb : c.qt);
+        c.t = nx ? c.t + 1 : (ng ? 0 : c.t);
+        c.g = nx ? c.g : (ng ? c.g + 1 : c.g);
       };
       // Q and dO rows of a tile into a ring stage: copy u of this wave fills rows
       // (wave*NIW + u)*RPI + lane/NCH.  Rows past the end repeat the last row;
@@ -236,16 +234,17 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         for (int u = 0; u < 2 * NIW; ++u) issue_job(j, u);
       };
       // L (wave 0) and Delta (wave 1) of a tile into an L ring stage (rows past
-      // the end repeat the last row), and the tile's dropout row keys (lanes
-      // 0-15 of each wave, 16 rows per wave).
+      // the end repeat the last row; waves 2 and 3 make the same copy into sDum),
+      // and the tile's dropout row keys (lanes 0-15 of each wave, 16 rows per wave).
+      const float* const ld_src = (wave & 1) ? Dl : L;
+      const uint32_t ld_dst = lds_addr(wave == 0 ? &sL[0][0] : (wave == 1 ? &sDel[0][0] : &sDum[wave & 1][0]));
+      const uint32_t ld_stride = wave < 2 ? 4u * BQ : 0u;  // bytes per ring stage
       auto issue_ld = [&](const Cursor& c, int lst) {
-        if (wave < 2) {
-          const float* src = (wave == 0 ? L : Dl) + c.loff;
-          dma4(src, 4u * (uint32_t)min(lane, a.Sq - 1 - c.qt), lds_addr(wave == 0 ? sL[lst] : sDel[lst]));
-        }
+        dma4(ld_src + c.loff, 4u * (uint32_t)min(lane, a.Sq - 1 - c.qt), ld_dst + (uint32_t)lst * ld_stride);
         if constexpr (DROP) {
           // the row's global index ((b*Hq + h)*Sq + i) mod 2^32 (drop_row_key)
-          if (lane < 16) sRK[lst][16 * wave + lane] = fmix32((uint32_t)c.loff + (uint32_t)(16 * wave + lane) + a.seed_mix);
+          uint32_t* rp = lane < 16 ? &sRK[lst][16 * wave + lane] : reinterpret_cast<uint32_t*>(&sDum[1][lane]);
+          *rp = fmix32((uint32_t)c.loff + (uint32_t)(16 * wave + lane) + a.seed_mix);
         }
       };
       // Once a stage's L/Delta landed and a barrier passed, each wave rewrites 16
@@ -256,23 +255,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       float* const fix_p = lane < 16 ? &sL[0][16 * wave + lane] : &sDel[0][16 * wave + (lane & 15)];
       const float fix_f = lane < 16 ? -kLog2e : -1.f;
       float fix_v = 0.f;
-      auto fix_rd = [&](int lst) {
-        if (fix_lane) fix_v = fix_p[lst * BQ];
-      };
-      auto fix_wr = [&](int lst) {
-        if (fix_lane) fix_p[lst * BQ] = fix_v * fix_f;
-      };
+      auto fix_at = [&](int lst) { return fix_lane ? fix_p + lst * BQ : &sDum[0][lane]; };
+      auto fix_rd = [&](int lst) { fix_v = *fix_at(lst); };
+      auto fix_wr = [&](int lst) { *fix_at(lst) = fix_v * fix_f; };
       // Waits until this wave's copies issued before the previous step's have
-      // landed (waves 0 and 1 issue one more copy per step: L or Delta).
-      // With a mask, the 32 mask copies of a step count too, and those of section
-      // A issued after its last tile copy (16 / PER of them).
+      // landed (the tile copies and the L/Delta copy of a step; with a mask, the 32
+      // mask copies of a step too, and those of section A issued after its last
+      // tile copy, 16 / PER of them).
       constexpr int NMV = MASK ? 32 + 16 / PER : 0;
-      auto wait_prev = [&]() {
-        if (wave < 2)
-          wait_vmcnt<2 * NIW + NMV + 1>();
-        else
-          wait_vmcnt<2 * NIW + NMV>();
-      };
+      auto wait_prev = [&]() { wait_vmcnt<2 * NIW + NMV + 1>(); };
 
       // Instruction order inside a step is fixed by hand: one wave per SIMD means
       // the MFMAs overlap only the VALU and LDS work placed between them, so every
