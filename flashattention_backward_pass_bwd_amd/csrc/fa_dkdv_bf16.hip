@@ -63,8 +63,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
 #ifndef FA_DKDV_NP
 #define FA_DKDV_NP 3
 #endif
-  constexpr int NP = FA_DKDV_NP;            // dV/dK MFMAs whose operands the preceding section reads
+  constexpr int NP = 2 * FA_DKDV_NP <= NSD ? FA_DKDV_NP : NSD / 2;  // dV/dK MFMAs whose operands the preceding section reads
   static_assert(NSD == NDK, "the S/dP section carries one transposed read per MFMA");
+  static_assert(2 * NP <= NSD, "the transposed reads of NP MFMAs fit the S/dP section's slots");
   static_assert(NSD % (NIW / 2) == 0, "a section carries a quarter of a tile's copies evenly");
 
   // Ring stage s holds the Q tile (sT[s][0]) and the dO tile (sT[s][1]) side by
@@ -443,6 +444,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           }
           mask_rd(k + MF);
           slot_extra(k);
+          // The seed blocks are read as accumulator inputs by the chains' first
+          // MFMAs (slots 0 and 1) while those run: they stay allocated until the
+          // chains' second MFMAs (which wait for the first ones' results) have
+          // issued, so nothing is written into them earlier.
+          if (k == 3) {
+            keep_live(pre.nls);
+            if constexpr (FOLD) keep_live(pre.dpi);
+          }
           fence();
         }
 #pragma unroll

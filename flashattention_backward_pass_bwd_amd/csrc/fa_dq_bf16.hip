@@ -57,7 +57,10 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
   constexpr bool FOLD = !DROP;              // dP chain seeded with -Delta
   constexpr int NSD = 2 * KS;               // S/dP MFMAs per 32-key half
   constexpr int NDQ = 2 * DB;               // dQ MFMAs per 32-key half
-  constexpr int NP = NDQ / 2;               // dQ MFMAs whose operands the preceding section reads
+#ifndef FA_DQ_NP
+#define FA_DQ_NP 4
+#endif
+  constexpr int NP = FA_DQ_NP < NDQ ? FA_DQ_NP : NDQ;  // dQ MFMAs whose operands the preceding section reads
   constexpr int PF = NDQ < 6 ? NDQ : 6;     // S/dP operand reads in flight
   constexpr int NC = 2 * NIW;               // copies per tile per wave
   constexpr int PER = NC / 4;               // copies per section
@@ -174,8 +177,8 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         dpi[r] = -del;
       }
       // kept in registers as they are, not rebuilt next to each use
-      asm volatile("" : "+v"(nls));
-      if constexpr (FOLD) asm volatile("" : "+v"(dpi));
+      pin(nls);
+      if constexpr (FOLD) pin(dpi);
 
       // K and V rows of tile tt (clamped to the last tile, so copies past the end
       // repeat it into stages that are never read) into a ring stage: copy u

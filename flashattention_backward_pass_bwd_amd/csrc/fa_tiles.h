@@ -61,7 +61,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 // the compiler itself never reads or writes M0 in the kernels that use these
 // copies (gfx9 LDS instructions do not need it, and these kernels have no
 // dynamically indexed register arrays or messages), which
-// tests/test_m0_ownership.py checks on the generated assembly.  One wait state
+// tests/test_asm_checks.py checks on the generated assembly.  One wait state
 // separates the M0 write from the copy.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
@@ -212,6 +212,12 @@ __device__ __forceinline__ void materialise(bf16x8 (&x)[2], bf16x8 (&y)[2]) {
   asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(y[0]), "+v"(y[1]));
 }
 __device__ __forceinline__ void materialise(bf16x8 (&x)[2]) { asm volatile("" : "+v"(x[0]), "+v"(x[1])); }
+// Makes a register block opaque here: the compiler keeps it as it is and does
+// not rebuild it next to each later use.
+__device__ __forceinline__ void pin(f32x16& x) { asm volatile("" : "+v"(x)); }
+// Keeps a register block allocated up to this point (a use the compiler cannot
+// see through), e.g. an accumulator input that an MFMA in flight still reads.
+__device__ __forceinline__ void keep_live(const f32x16& x) { asm volatile("" ::"v"(x)); }
 
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSgValu = 0x002 | 0x400;  // VALU incl. transcendental

@@ -1,0 +1,171 @@
+"""Checks on the generated gfx950 assembly of the tile kernels (CPU only).
+
+* The global->LDS copies write M0 without saving it (fa_tiles.h).  That is
+  only sound while the compiler itself never reads or writes M0 in those
+  kernels: M0 may appear only inside inline-assembly blocks.
+* The MFMAs are inline assembly, so the compiler's hazard tracking does not
+  see them.  Two hazards it would otherwise resolve are checked here:
+  a register written by an instruction outside the asm and read as an MFMA
+  operand within the two instructions before it (two wait states are needed),
+  and a register that an MFMA reads as its accumulator input (other than its
+  own result) written within the ten instructions after it, while the MFMA
+  may still read it.
+"""
+import concurrent.futures
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+from flashattention_backward_pass_bwd_amd import build
+
+SOURCES = [s for s in build.SOURCES if s.endswith(".hip") and "dma16(" in open(os.path.join(build.CSRC, s)).read()]
+
+
+def _have_hipcc() -> bool:
+    try:
+        build._hipcc()
+        return True
+    except RuntimeError:
+        return False
+
+
+pytestmark = pytest.mark.skipif(not _have_hipcc(), reason="hipcc not available")
+
+
+def _asm(src: str, out_dir: str) -> str:
+    out = os.path.join(out_dir, src + ".s")
+    cmd = [build._hipcc(), *build.COMMON_FLAGS, *build.EXTRA_FLAGS.get(src, []), "--cuda-device-only", "-x", "hip", "-S", os.path.join(build.CSRC, src), "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return open(out).read()
+
+
+def _m0_outside_inline_asm(text: str):
+    bad, inside = [], False
+    for line in text.splitlines():
+        s = line.strip()
+        if s.startswith(";;#ASMSTART"):
+            inside = True
+        elif s.startswith(";;#ASMEND"):
+            inside = False
+        elif not inside and re.search(r"\bm0\b", s.split(";")[0]):
+            bad.append(s.split(";")[0].strip())
+    return bad
+
+
+_TEXTS = {}
+
+
+def _compiled():
+    if not _TEXTS:
+        with tempfile.TemporaryDirectory() as d:
+            with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+                _TEXTS.update(zip(SOURCES, ex.map(lambda s: _asm(s, d), SOURCES)))
+    return _TEXTS
+
+
+def _regs(txt):
+    out = set()
+    for m in re.finditer(r"\b([va])(\d+)\b|\b([va])\[(\d+):(\d+)\]", txt):
+        if m.group(1):
+            out.add((m.group(1), int(m.group(2))))
+        else:
+            out.update((m.group(3), r) for r in range(int(m.group(4)), int(m.group(5)) + 1))
+    return out
+
+
+def _instructions(text):
+    """(text, inside inline asm) for every instruction, per kernel."""
+    seq, inside = [], False
+    for line in text.splitlines():
+        s = line.strip()
+        if s.startswith(";;#ASMSTART"):
+            inside = True
+        elif s.startswith(";;#ASMEND"):
+            inside = False
+        elif s and not s.startswith((";", ".")) and not s.endswith(":"):
+            seq.append((s.split(";")[0].strip(), inside))
+        elif re.match(r"^_Z\w+:", line):
+            seq.append(("<kernel>", False))
+    return seq
+
+
+def _writes(ins):
+    op = ins.split()[0]
+    if op.startswith(("s_", "global_load_lds", "buffer_", "global_store", "ds_write")):
+        return set()
+    return _regs(ins[len(op):].split(",")[0])
+
+
+def _mfma_hazards(text):
+    bad = []
+    seq = _instructions(text)
+    for i, (ins, inside) in enumerate(seq):
+        op = ins.split()[0]
+        if not (inside and op.startswith("v_mfma")):
+            continue
+        parts = [p.strip() for p in ins[len(op):].split(",")]
+        srcs = _regs(",".join(parts[1:]))
+        ws = 0
+        for j in range(i - 1, -1, -1):  # writes just before
+            pins, pin = seq[j]
+            if pins == "<kernel>":
+                break
+            pop = pins.split()[0]
+            if pop == "s_nop":
+                ws += int(pins.split()[1], 0) + 1
+            else:
+                if not pin and _writes(pins) & srcs:
+                    bad.append(f"{pins} -> {ins}")
+                ws += 1
+            if ws >= 2:
+                break
+        if len(parts) >= 4:  # accumulator input that is not the result
+            vd, sc = _regs(parts[0]), _regs(parts[3])
+            if sc and sc != vd:
+                for nins, nin in seq[i + 1:i + 11]:
+                    if nins == "<kernel>":
+                        break
+                    if not (nin and nins.startswith("v_mfma")) and _writes(nins) & sc:
+                        bad.append(f"{ins} -> {nins}")
+                        break
+    return bad
+
+
+def test_copy_sources_found():
+    assert {"fa_dkdv_bf16.hip", "fa_dq_bf16.hip"} <= set(SOURCES)
+
+
+def test_compiler_leaves_m0_to_the_copies():
+    for src, text in _compiled().items():
+        assert "global_load_lds_dwordx4" in text, src
+        assert _m0_outside_inline_asm(text) == [], src
+
+
+def test_detector_flags_compiler_m0_use():
+    text = "\n".join([
+        ";;#ASMSTART", "\ts_mov_b32 m0, s4", ";;#ASMEND",   # the copies' own write: allowed
+        "\ts_mov_b32 m0, -1",                                  # a compiler write: flagged
+        "\tv_movrels_b32 v0, v1 ; uses m0",                    # comment text is ignored
+    ])
+    assert _m0_outside_inline_asm(text) == ["s_mov_b32 m0, -1"]
+
+
+def test_no_write_hazards_around_asm_mfmas():
+    for src, text in _compiled().items():
+        assert "v_mfma_f32_32x32x16_bf16" in text, src
+        assert _mfma_hazards(text) == [], src
+
+
+def test_hazard_detector_flags_plain_cases():
+    text = "\n".join([
+        "_ZN2fa1kEv:",
+        "\tv_mov_b32_e32 v4, 0",                                    # writes an A operand register ...
+        ";;#ASMSTART", "\tv_mfma_f32_32x32x16_bf16 v[16:31], v[4:7], a[0:3], v[32:47]", ";;#ASMEND",
+        "\tv_add_u32_e32 v40, 1, v0",                              # ... and the accumulator input after
+        ";;#ASMSTART", "\ts_nop 1", "\tv_mfma_f32_32x32x16_bf16 v[48:63], v[8:11], a[4:7], 0", ";;#ASMEND",
+    ])
+    assert len(_mfma_hazards(text)) == 2
