@@ -295,7 +295,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       // the A operands of its first PF MFMAs, the -L*log2(e) rows its S chain
       // starts from, and the -Delta rows its dP chain starts from (FOLD) or the
       // Delta rows of the exp/dS half (dropout).
-      constexpr int PF = 6;
+#ifndef FA_DKDV_PF
+#define FA_DKDV_PF 6
+#endif
+      constexpr int PF = FA_DKDV_PF;
+      static_assert(PF < 8, "operand reads run ahead within a ring of 8");
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       struct SdpPre {
         bf16x8 op[PF];

@@ -61,7 +61,11 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
 #define FA_DQ_NP 4
 #endif
   constexpr int NP = FA_DQ_NP < NDQ ? FA_DQ_NP : NDQ;  // dQ MFMAs whose operands the preceding section reads
-  constexpr int PF = NDQ < 6 ? NDQ : 6;     // S/dP operand reads in flight
+#ifndef FA_DQ_PF
+#define FA_DQ_PF 6
+#endif
+  constexpr int PF = NDQ < FA_DQ_PF ? NDQ : FA_DQ_PF;  // S/dP operand reads in flight
+  static_assert(PF < 8, "operand reads run ahead within a ring of 8");
   constexpr int NC = 2 * NIW;               // copies per tile per wave
   constexpr int PER = NC / 4;               // copies per section
   // Mask staging (MASK): element r of a half is copied into sM right after the
