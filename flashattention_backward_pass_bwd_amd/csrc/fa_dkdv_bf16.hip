@@ -39,7 +39,10 @@
 
 namespace fa {
 
-template <int D, bool MASK, bool DROP>
+// MK: 0 no mask, 1 a mask of any strides, 2 a mask whose keys are contiguous and
+// whose 4-key groups are 16-byte aligned (staged with one 16-byte copy per lane
+// for 8 rows of the wave's 32 keys).
+template <int D, int MK, bool DROP>
 __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const __bf16* __restrict__ Q,
                                                            const __bf16* __restrict__ K,
                                                            const __bf16* __restrict__ V,
@@ -48,6 +51,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
                                                            const float* __restrict__ Dl,
                                                            __bf16* __restrict__ dK, __bf16* __restrict__ dV,
                                                            int nkb, int paired) {
+  constexpr bool MASK = MK != 0;
+  constexpr bool MVEC = MK == 2;
   constexpr int BQ = 64;
   constexpr int NCH = D / 8;                // 16-byte chunks per row
   constexpr int KS = D / 16;                // k-blocks of the head_dim contraction
@@ -146,6 +151,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     // row*msq*4 + key*msk*4; lanes fix the key (clamped) and the 4-row group.
     const uint32_t msq4 = MASK ? (uint32_t)a.msq * 4u : 0u;
     const uint32_t m_lvo = MASK ? ((uint32_t)min(jl, a.Sk - 1) * (uint32_t)a.msk + 4u * h2 * (uint32_t)a.msq) * 4u : 0u;
+    // MVEC: copy lane j fetches keys kw0 + 4*(j%8) .. +3 of row e + 4h (e = j/16,
+    // h = (j/8)%2) of an 8-row group; they land at byte 256e + 128h + 16*(j%8) of
+    // the group, so the reader lane (key k, half h2) finds element e at
+    // 256e + 128*h2 + 4k: one row per 32 banks, no conflicts.
+    const uint32_t m_lvv = MVEC ? (((uint32_t)(lane >> 4) + 4u * ((lane >> 3) & 1)) * (uint32_t)a.msq +
+                                   (uint32_t)(kw0 + 4 * (lane & 7))) * 4u
+                                : 0u;
     const uint32_t jg = (uint32_t)jl * 0x9E3779B9u;  // key part of the dropout draw
 
     int qb, qe;
@@ -215,6 +227,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       constexpr int MF = 2;
       constexpr int kMaskWait = 16 - (16 / NSD) * (MF + 1) + PER - 1;
       static_assert(kMaskWait >= 0, "mask staging wait");
+      // MVEC: group g (elements 4g .. 4g+3, 8 rows) is one copy, issued after its
+      // last element's slot; any element read MF slots ahead has at least 2 group
+      // copies and PER tile copies issued after its group's copy.
+      constexpr int SG = 4 / (16 / NSD);  // slots per group
+      constexpr int kMaskWaitV = 1 + PER;
+      constexpr int sl = (PER - 1) * (NSD / PER);  // section A's last tile copy slot
+      constexpr int kMaskLateA = MVEC ? (SG - 1 >= sl) + (2 * SG - 1 >= sl) + (3 * SG - 1 >= sl) + (4 * SG - 1 >= sl)
+                                      : 16 / PER;
+      constexpr int kMaskPerStep = MVEC ? 8 : 32;
       auto job_of = [&](const Cursor& c, int stage) {
         const uint32_t lim = (uint32_t)min(a.Sq - 1 - c.qt, BQ);
         return Job{Q + c.qoff, dO + c.qoff, lds_addr(&sT[stage][0][wave * NIW * RPI * D]), 2u * lim * (uint32_t)a.qss};
@@ -263,7 +284,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       // landed (the tile copies and the L/Delta copy of a step; with a mask, the 32
       // mask copies of a step too, and those of section A issued after its last
       // tile copy, 16 / PER of them).
-      constexpr int NMV = MASK ? 32 + 16 / PER : 0;
+      constexpr int NMV = MASK ? kMaskPerStep + kMaskLateA : 0;
       auto wait_prev = [&]() { wait_vmcnt<2 * NIW + NMV + 1>(); };
 
       // Instruction order inside a step is fixed by hand: one wave per SIMD means
@@ -410,9 +431,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         auto mask_rd = [&](int kk) {
           if constexpr (MASK && !FULL) {
             if (kk < NSD) {
-              wait_vmcnt<kMaskWait>();
+              wait_vmcnt<MVEC ? kMaskWaitV : kMaskWait>();
 #pragma unroll
-              for (int i = 0; i < 16 / NSD; ++i) mk[kk * (16 / NSD) + i] = sM[wave][kk * (16 / NSD) + i][lane];
+              for (int i = 0; i < 16 / NSD; ++i) {
+                const int r = kk * (16 / NSD) + i;
+                if constexpr (MVEC)
+                  mk[r] = (&sM[wave][0][0])[256 * (r >> 2) + 64 * (r & 3) + 32 * h2 + l32];
+                else
+                  mk[r] = sM[wave][r][lane];
+              }
             }
           }
         };
@@ -502,13 +529,27 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       auto mask_cp = [&](rsrc_t rs, uint32_t vb0, int r) {
         dma_buf4(rs, mad24(8 * (r >> 2) + (r & 3), msq4, vb0), lds_addr(&sM[wave][r][0]));
       };
+      // MVEC: group g of a half (rows 8g .. 8g+7 from vbv, the half's first row)
+      auto mask_cpv = [&](rsrc_t rs, uint32_t vbv, int g) {
+        dma_buf16(rs, mad24(8 * g, msq4, vbv), lds_addr(&sM[wave][4 * g][0]));
+      };
+      auto mask_vbv = [&](int qt, int half) { return m_lvv + (uint32_t)(qt + 32 * half) * msq4; };
+      // Slot hook of sections A and C: the copies refilling the elements (MVEC:
+      // the groups) whose last use was slot k.
+      auto mask_refill = [&](rsrc_t rs, int qt, int half, int k) {
+        if constexpr (MVEC) {
+          if (k % SG == SG - 1) mask_cpv(rs, mask_vbv(qt, half), k / SG);
+        } else if constexpr (MASK) {
+#pragma unroll
+          for (int i = 0; i < 16 / NSD; ++i) mask_cp(rs, mask_vb(qt, half), k * (16 / NSD) + i);
+        }
+      };
       // The cursor cm names tile it+1, whose half 0 section C of step it stages.
       Cursor cm = cursor0();
       if constexpr (MASK) {
         const rsrc_t rs = mask_src(0);
-        const uint32_t v0 = mask_vb(qb, 0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mask_cp(rs, v0, r);
+        for (int k = 0; k < NSD; ++k) mask_refill(rs, qb, 0, k);
         advance(cm);
       }
 
@@ -586,13 +627,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         // Each slot then stages the mask of half 1 of this tile in place of the
         // half-0 elements it used.
         const rsrc_t mrs_a = mask_src(g);
-        const uint32_t mvb_a = MASK ? mask_vb(qt, 1) : 0u;
         sec_sdp_ew(full_c, 1, stq, s1, dp1, pre, 0, stq, qt, s0, dp0, pm, ds, trp, [&](int k) {
           copies_at(pend, NC / 2 + PER, k, NSD);
-          if constexpr (MASK) {
-#pragma unroll
-            for (int i = 0; i < 16 / NSD; ++i) mask_cp(mrs_a, mvb_a, k * (16 / NSD) + i);
-          }
+          mask_refill(mrs_a, qt, 1, k);
         });
         wait_prev();  // tile it+1 landed everywhere once all waves pass the barrier
         barrier_only();
@@ -610,14 +647,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         // C: S/dP of half 0 of tile it+1 with exp/dS of half 1; each slot then
         // stages the mask of half 0 of tile it+1 in place of the elements it used
         const rsrc_t mrs_c = mask_src(cm.g);
-        const uint32_t mvb_c = MASK ? mask_vb(cm.qt, 0) : 0u;
         sec_sdp_ew(full_c, 0, stq1, s0, dp0, pre, 1, stq, qt, s1, dp1, pm, ds, trp, [&](int k) {
           copies_at(next, PER, k, NSD);
           if (k == 1) fix_wr(lst2);
-          if constexpr (MASK) {
-#pragma unroll
-            for (int i = 0; i < 16 / NSD; ++i) mask_cp(mrs_c, mvb_c, k * (16 / NSD) + i);
-          }
+          mask_refill(mrs_c, cm.qt, 0, k);
         });
         // D: dV/dK of half 1; prefetch for A of the next step
         sec_dkv(1, stq, trp, pm, ds, [&](int n) {
@@ -675,14 +708,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
   }
 }
 
-template <int D, bool MASK, bool DROP>
+template <int D, int MK, bool DROP>
 static hipError_t launch_t(const PrefillArgs& a, const void* Q, const void* K, const void* V, const void* dO,
                            const float* L, const float* delta, void* dK, void* dV, hipStream_t st) {
   const int nkb = (a.Sk + kDkdvKeysPerBlock - 1) / kDkdvKeysPerBlock;
   const int paired = (a.causal && a.window == 0 && nkb > 1) ? 1 : 0;
   const int nwi = paired ? (nkb + 1) / 2 : nkb;
   const unsigned grid = (unsigned)(nwi * a.B * a.Hkv);
-  hipLaunchKernelGGL((dkdv_bf16_kernel<D, MASK, DROP>), dim3(grid), dim3(256), 0, st, a,
+  hipLaunchKernelGGL((dkdv_bf16_kernel<D, MK, DROP>), dim3(grid), dim3(256), 0, st, a,
                      static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
                      static_cast<const __bf16*>(dO), L, delta, static_cast<__bf16*>(dK), static_cast<__bf16*>(dV),
                      nkb, paired);
@@ -692,12 +725,14 @@ static hipError_t launch_t(const PrefillArgs& a, const void* Q, const void* K, c
 template <int D>
 static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, const void* V, const void* dO,
                            const float* L, const float* delta, void* dK, void* dV, hipStream_t st) {
-  const bool mask = a.mask != nullptr;
   const bool drop = a.drop != 0;
-  if (mask && drop) return launch_t<D, true, true>(a, Q, K, V, dO, L, delta, dK, dV, st);
-  if (mask) return launch_t<D, true, false>(a, Q, K, V, dO, L, delta, dK, dV, st);
-  if (drop) return launch_t<D, false, true>(a, Q, K, V, dO, L, delta, dK, dV, st);
-  return launch_t<D, false, false>(a, Q, K, V, dO, L, delta, dK, dV, st);
+  const int mk = a.mask == nullptr ? 0 : (mask_keys_contiguous(a) ? 2 : 1);
+  if (mk == 2) return drop ? launch_t<D, 2, true>(a, Q, K, V, dO, L, delta, dK, dV, st)
+                           : launch_t<D, 2, false>(a, Q, K, V, dO, L, delta, dK, dV, st);
+  if (mk == 1) return drop ? launch_t<D, 1, true>(a, Q, K, V, dO, L, delta, dK, dV, st)
+                           : launch_t<D, 1, false>(a, Q, K, V, dO, L, delta, dK, dV, st);
+  return drop ? launch_t<D, 0, true>(a, Q, K, V, dO, L, delta, dK, dV, st)
+              : launch_t<D, 0, false>(a, Q, K, V, dO, L, delta, dK, dV, st);
 }
 
 hipError_t launch_dkdv_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V,

@@ -564,11 +564,7 @@ template <int D>
 static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, const void* V, const void* dO,
                            const float* L, const float* delta, void* dQ, hipStream_t st) {
   const bool drop = a.drop != 0;
-  // keys contiguous and every 4-key group 16-byte aligned: rows, heads and
-  // batches start on 16 bytes
-  const bool vec = a.mask != nullptr && a.msk == 1 && a.msq % 4 == 0 && a.msh % 4 == 0 && a.msb % 4 == 0 &&
-                   (reinterpret_cast<uintptr_t>(a.mask) & 15u) == 0;
-  const int mk = a.mask == nullptr ? 0 : (vec ? 2 : 1);
+  const int mk = a.mask == nullptr ? 0 : (mask_keys_contiguous(a) ? 2 : 1);
   if (mk == 2) return drop ? launch_t<D, 2, true>(a, Q, K, V, dO, L, delta, dQ, st)
                            : launch_t<D, 2, false>(a, Q, K, V, dO, L, delta, dQ, st);
   if (mk == 1) return drop ? launch_t<D, 1, true>(a, Q, K, V, dO, L, delta, dQ, st)

@@ -16,6 +16,14 @@ constexpr int kDqRowsPerWave = 32;
 constexpr int kDqWaves = 4;
 constexpr int kDqRowsPerBlock = kDqRowsPerWave * kDqWaves;
 
+// A mask whose keys are contiguous and whose 4-key groups start on 16 bytes
+// (rows, heads and batches on 16-byte strides, the base 16-byte aligned): the
+// tile kernels then stage it with 16-byte copies.
+inline bool mask_keys_contiguous(const PrefillArgs& a) {
+  return a.mask != nullptr && a.msk == 1 && a.msq % 4 == 0 && a.msh % 4 == 0 && a.msb % 4 == 0 &&
+         (reinterpret_cast<uintptr_t>(a.mask) & 15u) == 0;
+}
+
 struct DecodeArgs {
   int N, H, Hkv, D, len, g;
 };
