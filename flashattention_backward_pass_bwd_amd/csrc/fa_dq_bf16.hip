@@ -575,6 +575,10 @@ static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, c
 
 hipError_t launch_dq_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V,
                           const void* dO, const float* L, const float* delta, void* dQ, hipStream_t st) {
+  // Head dimension 128 without window, mask or dropout: two row blocks per wave
+  // (a window leaves its 256-row blocks more invisible key tiles than it saves).
+  if (D == 128 && a.window == 0 && a.mask == nullptr && a.drop == 0)
+    return launch_dq2_bf16(a, Q, K, V, dO, L, delta, dQ, st);
   return D == 64 ? launch_d<64>(a, Q, K, V, dO, L, delta, dQ, st) : launch_d<128>(a, Q, K, V, dO, L, delta, dQ, st);
 }
 

@@ -15,6 +15,9 @@ constexpr int kDkdvKeysPerBlock = kDkdvKeysPerWave * kDkdvWaves;
 constexpr int kDqRowsPerWave = 32;
 constexpr int kDqWaves = 4;
 constexpr int kDqRowsPerBlock = kDqRowsPerWave * kDqWaves;
+// The head-dimension-128 dQ kernel without window, mask or dropout: two 32-row blocks per wave.
+constexpr int kDq2RowsPerWave = 64;
+constexpr int kDq2RowsPerBlock = kDq2RowsPerWave * kDqWaves;
 
 // A mask whose keys are contiguous and whose 4-key groups start on 16 bytes
 // (rows, heads and batches on 16-byte strides, the base 16-byte aligned): the
@@ -38,6 +41,8 @@ hipError_t launch_dkdv_bf16(const PrefillArgs& a, int D, const void* Q, const vo
                             hipStream_t st);
 hipError_t launch_dq_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V,
                           const void* dO, const float* L, const float* delta, void* dQ, hipStream_t st);
+hipError_t launch_dq2_bf16(const PrefillArgs& a, const void* Q, const void* K, const void* V, const void* dO,
+                           const float* L, const float* delta, void* dQ, hipStream_t st);
 hipError_t launch_dq(const PrefillArgs& a, int dtype, int D, const void* Q, const void* K,
                      const void* V, const void* dO, const float* L, const float* delta, void* dQ,
                      hipStream_t st);

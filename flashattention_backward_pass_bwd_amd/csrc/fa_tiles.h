@@ -168,6 +168,12 @@ __device__ __forceinline__ void mfma_v_seed(f32x16& c, const bf16x8& a, const bf
   asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(c) : "v"(a), "a"(b), "v"(seed));
 }
 
+// The same with a seed block that stays unchanged for the whole kernel (no
+// VALU write right before the MFMA, so no wait states).
+__device__ __forceinline__ void mfma_v_cseed(f32x16& c, const bf16x8& a, const bf16x8& b, const f32x16& seed) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(c) : "v"(a), "a"(b), "v"(seed));
+}
+
 // Moves a value into accumulation registers once, so that later MFMAs read it
 // there as a B operand without a copy per use.
 __device__ __forceinline__ void to_agpr(bf16x8& v) { asm volatile("" : "+a"(v)); }
@@ -194,6 +200,10 @@ __device__ __forceinline__ void mfma_drain(f32x16& x, f32x16& y) {
 // MFMA, and passes the results through the asm so that no read of them moves
 // up next to the chain.
 __device__ __forceinline__ void mfma_settle(f32x16& x, f32x16& y) { asm volatile("s_nop 1" : "+v"(x), "+v"(y)); }
+// Eight wait states before instructions other than MFMAs read a result whose
+// chain ended a few instructions earlier: with at least four instructions
+// already in between, the twelve an XDL result needs are covered.
+__device__ __forceinline__ void mfma_result_wait(f32x16& x) { asm volatile("s_nop 7" : "+v"(x)); }
 template <int N>
 __device__ __forceinline__ void mfma_drain_acc(f32x16 (&x)[N], f32x16 (&y)[N]) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");

@@ -10,6 +10,10 @@
   and a register that an MFMA reads as its accumulator input (other than its
   own result) written within the ten instructions after it, while the MFMA
   may still read it.
+  A third: a VGPR result of an MFMA read or written by any instruction other
+  than the next MFMA of its own chain within the twelve wait states an XDL
+  result needs (the count the compiler itself inserts for
+  v_mfma_f32_32x32x16_bf16 on gfx950).
 """
 import concurrent.futures
 import os
@@ -135,6 +139,35 @@ def _mfma_hazards(text):
     return bad
 
 
+def _result_reads(text, need=12):
+    bad = []
+    seq = _instructions(text)
+    for i, (ins, inside) in enumerate(seq):
+        op = ins.split()[0]
+        if not (inside and op.startswith("v_mfma")):
+            continue
+        vd = _regs(ins[len(op):].split(",")[0])
+        if not vd or next(iter(vd))[0] != "v":
+            continue
+        ws = 0
+        for nins, _ in seq[i + 1:]:
+            if nins == "<kernel>" or ws >= need:
+                break
+            nop = nins.split()[0]
+            if nop == "s_nop":
+                ws += int(nins.split()[1], 0) + 1
+                continue
+            if nop.startswith("v_mfma"):
+                nparts = [p.strip() for p in nins[len(nop):].split(",")]
+                if _regs(nparts[0]) == vd and len(nparts) >= 4 and _regs(nparts[3]) == vd:
+                    break  # the chain's next MFMA (the hardware forwards the result)
+            if _regs(nins[len(nop):]) & vd:
+                bad.append(f"{ins} -> {nins} ({ws} wait states)")
+                break
+            ws += 1
+    return bad
+
+
 def test_copy_sources_found():
     assert {"fa_dkdv_bf16.hip", "fa_dq_bf16.hip"} <= set(SOURCES)
 
@@ -169,3 +202,23 @@ def test_hazard_detector_flags_plain_cases():
         ";;#ASMSTART", "\ts_nop 1", "\tv_mfma_f32_32x32x16_bf16 v[48:63], v[8:11], a[4:7], 0", ";;#ASMEND",
     ])
     assert len(_mfma_hazards(text)) == 2
+
+
+def test_mfma_results_read_after_their_wait_states():
+    for src, text in _compiled().items():
+        assert _result_reads(text) == [], src
+
+
+def test_result_read_detector_flags_plain_cases():
+    text = "\n".join([
+        "_ZN2fa1kEv:",
+        ";;#ASMSTART", "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[16:19], a[0:3], 0", ";;#ASMEND",
+        ";;#ASMSTART", "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[20:23], a[4:7], v[0:15]", ";;#ASMEND",  # chain: fine
+        ";;#ASMSTART", "\ts_nop 7", ";;#ASMEND",
+        "\tv_exp_f32_e32 v30, v3",                                                                  # 8 wait states: flagged
+        ";;#ASMSTART", "\tv_mfma_f32_32x32x16_bf16 v[32:47], v[16:19], a[0:3], 0", ";;#ASMEND",
+        ";;#ASMSTART", "\ts_nop 7", "\ts_nop 3", ";;#ASMEND",
+        "\tv_exp_f32_e32 v50, v40",                                                                 # 13 wait states: fine
+    ])
+    bad = _result_reads(text)
+    assert len(bad) == 1 and "v_exp_f32_e32 v30, v3" in bad[0]

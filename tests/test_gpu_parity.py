@@ -42,6 +42,14 @@ CASES = {
                                                           seq_k=150, window=1000, seed=18),
     "dropout_only_f32_d64": synth.CAUSAL_F32.resized(batch=2, num_heads=2, num_kv_heads=1, seq_q=129, seq_k=129,
                                                      dropout_p=0.3, dropout_seed=99, seed=19),
+    # head dimension 128 without window, mask or dropout (the 64-row-per-wave dQ
+    # kernel): Sq != Sk with an offset, and non-causal with Sq > Sk; with a window
+    "offset_bf16_d128": synth.LONG_BF16.resized(num_heads=6, num_kv_heads=2, seq_q=300, seq_k=520,
+                                                causal_offset=220, seed=21),
+    "offset_window_bf16_d128": synth.LONG_BF16.resized(num_heads=6, num_kv_heads=2, seq_q=300, seq_k=520,
+                                                       causal_offset=220, window=130, seed=23),
+    "noncausal_bf16_d128": synth.LONG_BF16.resized(batch=2, num_heads=4, num_kv_heads=2, seq_q=333, seq_k=190,
+                                                   causal=False, seed=22),
     "mask_noncausal_bf16": synth.EXTRAS_BF16.resized(batch=1, num_heads=4, num_kv_heads=4, seq_q=190, seq_k=260,
                                                      causal=False, window=0, mask_density=0.3, dropout_p=0.0,
                                                      seed=20),
