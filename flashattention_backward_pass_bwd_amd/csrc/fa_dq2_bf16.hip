@@ -251,6 +251,7 @@ __global__ __launch_bounds__(256, 1) void dq2_bf16_kernel(PrefillArgs a, const _
             else
               mfma_v(dp[rb], op, gr[rb][o - KS]);
           }
+          fence();  // the slot's other work follows its MFMA
           if (rb == 0) {
             if (o + PFO < NOP) {
               buf[(o + PFO) % NB] = rd_op(m, stq, o + PFO);
@@ -302,8 +303,11 @@ __global__ __launch_bounds__(256, 1) void dq2_bf16_kernel(PrefillArgs a, const _
         auto ew_ds = [&](int rb, int r) {
           dv[rb][r] = p[rb][r] * dp[rb][r];
           if (r & 1) {
-            dsn[rb][r >> 3][(r & 7) - 1] = (__bf16)dv[rb][r - 1];
-            dsn[rb][r >> 3][r & 7] = (__bf16)dv[rb][r];
+            // packed here, in this slot, not next to the packed vector's use
+            bf16x2 t = {(__bf16)dv[rb][r - 1], (__bf16)dv[rb][r]};
+            asm volatile("" : "+v"(t));
+            dsn[rb][r >> 3][(r & 7) - 1] = t[0];
+            dsn[rb][r >> 3][r & 7] = t[1];
           }
         };
         fence();
@@ -312,6 +316,7 @@ __global__ __launch_bounds__(256, 1) void dq2_bf16_kernel(PrefillArgs a, const _
           const int n = j >> 1, rb = j & 1;
           if constexpr (MF) {
             mfma_acc(accq[rb][n % DB], concat(tb[n % NBT][0], tb[n % NBT][1]), dsq[rb][n / DB]);
+            fence();
             if (rb == 0 && n + PFT < NTR) {
               tb[(n + PFT) % NBT][0] = rd_tr(mq, stqq, 2 * (n + PFT));
               tb[(n + PFT) % NBT][1] = rd_tr(mq, stqq, 2 * (n + PFT) + 1);
