@@ -184,14 +184,24 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         return Cursor{0, 0, qb, (int64_t)b * a.qsb + (int64_t)h0 * a.qsh + (int64_t)qb * a.qss,
                       ((int64_t)b * a.Hq + h0) * a.Sq + qb};
       };
-      auto advance = [&](Cursor& c) {  // next tile, else next head's first, else stay
-        const bool nx = c.t + 1 < ntq;
-        const bool ng = c.g + 1 < a.group;
-        c.qoff += nx ? inc_qt : (ng ? inc_qh : 0);
-        c.loff += nx ? (int64_t)BQ : (ng ? inc_lh : 0);
-        c.qt = nx ? c.qt + BQ : (ng ? qb : c.qt);
-        c.t = nx ? c.t + 1 : (ng ? 0 : c.t);
-        c.g = nx ? c.g : (ng ? c.g + 1 : c.g);
+      // Next tile, else next head's first, else stay: the conditions, then one
+      // field per part (parts 0..4), so that a step can spread the update over
+      // several pipeline slots.
+      struct Turn {
+        bool nx, ng;
+      };
+      auto turn_of = [&](const Cursor& c) { return Turn{c.t + 1 < ntq, c.g + 1 < a.group}; };
+      auto advance_part = [&](Cursor& c, const Turn& w, int part) {
+        if (part == 0) c.qoff += w.nx ? inc_qt : (w.ng ? inc_qh : 0);
+        if (part == 1) c.loff += w.nx ? (int64_t)BQ : (w.ng ? inc_lh : 0);
+        if (part == 2) c.qt = w.nx ? c.qt + BQ : (w.ng ? qb : c.qt);
+        if (part == 3) c.t = w.nx ? c.t + 1 : (w.ng ? 0 : c.t);
+        if (part == 4) c.g = w.nx ? c.g : (w.ng ? c.g + 1 : c.g);
+      };
+      auto advance = [&](Cursor& c) {
+        const Turn w = turn_of(c);
+#pragma unroll
+        for (int part = 0; part < 5; ++part) advance_part(c, w, part);
       };
       // Q and dO rows of a tile into a ring stage: copy u of this wave fills rows
       // (wave*NIW + u)*RPI + lane/NCH.  Rows past the end repeat the last row;
@@ -420,10 +430,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
             dv[r] = pr[r] * dpe[r];
           }
           if (r & 1) {
-            pmc[r >> 3][(r & 7) - 1] = (__bf16)pv[r - 1];
-            pmc[r >> 3][r & 7] = (__bf16)pv[r];
-            dsc[r >> 3][(r & 7) - 1] = (__bf16)dv[r - 1];
-            dsc[r >> 3][r & 7] = (__bf16)dv[r];
+            const bf16x2 tp = pack_here(pv[r - 1], pv[r]);
+            const bf16x2 td = pack_here(dv[r - 1], dv[r]);
+            pmc[r >> 3][(r & 7) - 1] = tp[0];
+            pmc[r >> 3][r & 7] = tp[1];
+            dsc[r >> 3][(r & 7) - 1] = td[0];
+            dsc[r >> 3][r & 7] = td[1];
           }
         };
         // Mask values of the half, read from this wave's LDS staging MF slots ahead
@@ -634,13 +646,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         wait_prev();  // tile it+1 landed everywhere once all waves pass the barrier
         barrier_only();
         const Cursor cl_now = cl;  // tile it+4: the copies' cursor of the next step
-        issue_ld(cl, lst4);
-        advance(cl);
-        fence();
-        const Job next = job_of(cq, stq3);
-        // B: dV/dK of half 0; prefetch for C (S/dP of half 0 of tile it+1, exp/dS of half 1)
+        Job next;
+        Turn turn;
+        // B: dV/dK of half 0; prefetch for C (S/dP of half 0 of tile it+1, exp/dS
+        // of half 1).  The cursors' bookkeeping is spread over its slots (not
+        // put between the barrier and its first MFMA), so its copies start one
+        // slot later.
+        constexpr int kLd = NDK >= 16 ? 2 : 1, kTurn = NDK >= 16 ? 3 : 1, kAdv = kTurn + 1;
+        static_assert(kAdv + 4 < NDK, "the cursor update fits section B");
         sec_dkv(0, stq, trp, pm, ds, [&](int n) {
-          copies_at(next, 0, n, NDK);
+          if (n == 0) next = job_of(cq, stq3);
+          if (n == kLd) issue_ld(cl, lst4);
+          if (n == kTurn) turn = turn_of(cl);
+          if (n >= kAdv && n < kAdv + 5) advance_part(cl, turn, n - kAdv);
+          if (n >= 1) copies_at(next, 0, n - 1, NDK);
           pre_at(n, 0, stq1, lst1, 1, lst);
           if (n == NDK / 2) fix_rd(lst2);  // L/Delta of tile it+2 (its copy landed before this step's barrier)
         });

@@ -303,9 +303,7 @@ __global__ __launch_bounds__(256, 1) void dq2_bf16_kernel(PrefillArgs a, const _
         auto ew_ds = [&](int rb, int r) {
           dv[rb][r] = p[rb][r] * dp[rb][r];
           if (r & 1) {
-            // packed here, in this slot, not next to the packed vector's use
-            bf16x2 t = {(__bf16)dv[rb][r - 1], (__bf16)dv[rb][r]};
-            asm volatile("" : "+v"(t));
+            const bf16x2 t = pack_here(dv[rb][r - 1], dv[rb][r]);
             dsn[rb][r >> 3][(r & 7) - 1] = t[0];
             dsn[rb][r >> 3][r & 7] = t[1];
           }

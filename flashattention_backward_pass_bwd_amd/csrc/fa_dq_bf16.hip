@@ -295,8 +295,9 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
             dv[r] = pv[r] * dpe[r];
           }
           if (r & 1) {
-            dsc[r >> 3][(r & 7) - 1] = (__bf16)dv[r - 1];
-            dsc[r >> 3][r & 7] = (__bf16)dv[r];
+            const bf16x2 t = pack_here(dv[r - 1], dv[r]);
+            dsc[r >> 3][(r & 7) - 1] = t[0];
+            dsc[r >> 3][r & 7] = t[1];
           }
         };
         // Mask values of the half, read from this wave's LDS staging MF slots ahead

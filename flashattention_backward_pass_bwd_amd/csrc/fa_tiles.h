@@ -174,6 +174,15 @@ __device__ __forceinline__ void mfma_v_cseed(f32x16& c, const bf16x8& a, const b
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3" : "=&v"(c) : "v"(a), "a"(b), "v"(seed));
 }
 
+// Two floats rounded to bf16 and packed into one register here: the asm keeps
+// the conversion where it is written (its pipeline slot) instead of letting it
+// sink next to the first use of the vector the pair goes into.
+__device__ __forceinline__ bf16x2 pack_here(float x, float y) {
+  bf16x2 t = {(__bf16)x, (__bf16)y};
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Moves a value into accumulation registers once, so that later MFMAs read it
 // there as a B operand without a copy per use.
 __device__ __forceinline__ void to_agpr(bf16x8& v) { asm volatile("" : "+a"(v)); }
