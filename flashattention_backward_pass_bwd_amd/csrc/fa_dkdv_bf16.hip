@@ -166,8 +166,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     const int ntiles = ntq * a.group;
 
     if (ntiles > 0) {
-      // Tiles are numbered it = g*ntq + t (query head g of the group, query
-      // tile t).  A cursor names the tile whose copies are issued next; past
+      // Steps are numbered it = (ntq-1-t)*group + g (query tile t, query head
+      // g of the group).  A cursor names the tile whose copies are issued next; past
       // the last tile it stays there, so the last copies repeat into stages
       // that are never read and every step runs the same straight-line code.
       // The cursor also carries the element offsets of the tile's first row in
@@ -176,27 +176,33 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         int g, t, qt;
         int64_t qoff, loff;
       };
-      const int64_t inc_qt = (int64_t)BQ * a.qss;                           // next tile
-      const int64_t inc_qh = a.qsh - (int64_t)(ntq - 1) * BQ * a.qss;       // next head's first tile
-      const int64_t inc_lh = (int64_t)a.Sq - (int64_t)(ntq - 1) * BQ;
+      // Order: query tiles from the last down to the first, and for each tile
+      // the group's query heads in turn.  The blocks of one KV head run side by
+      // side on one XCD and start on the same last tile, so they read the same
+      // Q/dO tiles at about the same time and share them in L2 (causal blocks
+      // differ only in where they stop).
+      const int64_t inc_qh = a.qsh;                                                    // next head, same tile
+      const int64_t inc_qt = -(int64_t)(a.group - 1) * a.qsh - (int64_t)BQ * a.qss;   // first head, tile below
+      const int64_t inc_lt = -(int64_t)(a.group - 1) * a.Sq - (int64_t)BQ;
       auto cursor0 = [&]() {
         const int h0 = kvh * a.group;
-        return Cursor{0, 0, qb, (int64_t)b * a.qsb + (int64_t)h0 * a.qsh + (int64_t)qb * a.qss,
-                      ((int64_t)b * a.Hq + h0) * a.Sq + qb};
+        const int qt = qb + (ntq - 1) * BQ;
+        return Cursor{0, ntq - 1, qt, (int64_t)b * a.qsb + (int64_t)h0 * a.qsh + (int64_t)qt * a.qss,
+                      ((int64_t)b * a.Hq + h0) * a.Sq + qt};
       };
-      // Next tile, else next head's first, else stay: the conditions, then one
-      // field per part (parts 0..4), so that a step can spread the update over
-      // several pipeline slots.
+      // Next head, else the first head of the tile below, else stay: the
+      // conditions, then one field per part (parts 0..4), so that a step can
+      // spread the update over several pipeline slots.
       struct Turn {
-        bool nx, ng;
+        bool ng, nt;
       };
-      auto turn_of = [&](const Cursor& c) { return Turn{c.t + 1 < ntq, c.g + 1 < a.group}; };
+      auto turn_of = [&](const Cursor& c) { return Turn{c.g + 1 < a.group, c.t > 0}; };
       auto advance_part = [&](Cursor& c, const Turn& w, int part) {
-        if (part == 0) c.qoff += w.nx ? inc_qt : (w.ng ? inc_qh : 0);
-        if (part == 1) c.loff += w.nx ? (int64_t)BQ : (w.ng ? inc_lh : 0);
-        if (part == 2) c.qt = w.nx ? c.qt + BQ : (w.ng ? qb : c.qt);
-        if (part == 3) c.t = w.nx ? c.t + 1 : (w.ng ? 0 : c.t);
-        if (part == 4) c.g = w.nx ? c.g : (w.ng ? c.g + 1 : c.g);
+        if (part == 0) c.qoff += w.ng ? inc_qh : (w.nt ? inc_qt : 0);
+        if (part == 1) c.loff += w.ng ? (int64_t)a.Sq : (w.nt ? inc_lt : 0);
+        if (part == 2) c.qt = w.ng ? c.qt : (w.nt ? c.qt - BQ : c.qt);
+        if (part == 3) c.t = w.ng ? c.t : (w.nt ? c.t - 1 : c.t);
+        if (part == 4) c.g = w.ng ? c.g + 1 : (w.nt ? 0 : c.g);
       };
       auto advance = [&](Cursor& c) {
         const Turn w = turn_of(c);
@@ -559,9 +565,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       // The cursor cm names tile it+1, whose half 0 section C of step it stages.
       Cursor cm = cursor0();
       if constexpr (MASK) {
-        const rsrc_t rs = mask_src(0);
+        const rsrc_t rs = mask_src(cm.g);  // the first step's tile
 #pragma unroll
-        for (int k = 0; k < NSD; ++k) mask_refill(rs, qb, 0, k);
+        for (int k = 0; k < NSD; ++k) mask_refill(rs, cm.qt, 0, k);
         advance(cm);
       }
 
@@ -684,24 +690,26 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
 
       const std::integral_constant<int, 1> kEdge;
       const std::integral_constant<int, 2> kInner;
-      for (int g = 0; g < a.group; ++g) {
-        // This wave's tiles of head g: [0,f0) boundary, [f0,f1) interior,
-        // [f1,ntq) boundary (the visible key interval moves monotonically with
-        // the query row, so the interior tiles are contiguous).  Boundary tiles
-        // include tiles this wave cannot see at all; the predicate zeroes them.
-        auto all = [&](int t) { return rect_all_visible(a, qb + t * BQ, qb + t * BQ + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1); };
-        int f0 = ntq, f1 = ntq;
-        if constexpr (!MASK) {
-          f0 = 0;
-          while (f0 < ntq && !all(f0)) ++f0;
-          f1 = f0;
-          while (f1 < ntq && all(f1)) ++f1;
-        }
-        int t = 0;
-        for (; t < f0; ++t) step(kEdge, g, t);
-        for (; t < f1; ++t) step(kInner, g, t);
-        for (; t < ntq; ++t) step(kEdge, g, t);
+      // This wave's tiles: [0,f0) boundary, [f0,f1) interior, [f1,ntq)
+      // boundary (the visible key interval moves monotonically with the query
+      // row, so the interior tiles are contiguous), walked from the last down,
+      // each for every query head of the group.  Boundary tiles include tiles
+      // this wave cannot see at all; the predicate zeroes them.
+      auto all = [&](int t) { return rect_all_visible(a, qb + t * BQ, qb + t * BQ + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1); };
+      int f0 = ntq, f1 = ntq;
+      if constexpr (!MASK) {
+        f0 = 0;
+        while (f0 < ntq && !all(f0)) ++f0;
+        f1 = f0;
+        while (f1 < ntq && all(f1)) ++f1;
       }
+      int t = ntq - 1;
+      for (; t >= f1; --t)
+        for (int g = 0; g < a.group; ++g) step(kEdge, g, t);
+      for (; t >= f0; --t)
+        for (int g = 0; g < a.group; ++g) step(kInner, g, t);
+      for (; t >= 0; --t)
+        for (int g = 0; g < a.group; ++g) step(kEdge, g, t);
       wait_vmcnt<0>();  // the repeated copies of the last steps have landed
       barrier_lds();    // every wave is done with the ring before the next pass refills it
     }
