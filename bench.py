@@ -43,7 +43,42 @@ def _args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long", choices=["long", "extras", "causal_f32", "decode", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip the calibration of the bf16 MFMA rate on N(0,1) operands (about 0.5 s)")
     return ap.parse_args()
+
+
+def _mfma_ceiling():
+    """TFLOP/s of back-to-back bf16 MFMAs on every SIMD with N(0,1) operand data.
+
+    The published dense peak assumes the full engine clock; under a sustained
+    MFMA load with random operand bits the chip holds a lower, power-limited
+    clock.  This runs the library's calibration kernel (fa_bwd_calib_mfma_bf16:
+    nothing but v_mfma_f32_32x32x16_bf16, operands rotating over registers as in
+    the tile kernels) for a few hundred milliseconds and reports its rate, the
+    ceiling the tile kernels can approach on this data.
+    """
+    import torch
+
+    from flashattention_backward_pass_bwd_amd import api
+
+    g = torch.Generator(device="cpu").manual_seed(1234)
+    ops = torch.randn(2048 * 8, generator=g).to(torch.bfloat16).cuda()
+    blocks = 4 * torch.cuda.get_device_properties(0).multi_processor_count  # four waves of one wave per SIMD
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    iters = 2000
+    for _ in range(20):
+        api.calib_mfma_bf16(ops, sink, blocks, iters)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 40
+    e0.record()
+    for _ in range(n):
+        api.calib_mfma_bf16(ops, sink, blocks, iters)
+    e1.record()
+    torch.cuda.synchronize()
+    flop = n * blocks * 4 * iters * 32 * 32768.0
+    return flop / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
 def _visible_pairs(w) -> int:
@@ -256,6 +291,13 @@ def bench_prefill(args, w):
                      "per_unit": "8*D FLOP per visible (b,h,i,j) pair", "units": pairs},
     }
     _log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+    if w.dtype == "bf16" and not args.no_mfma_ceiling:
+        ceiling = _mfma_ceiling()
+        out["roofline"]["mfma_ceiling"] = {
+            "value": round(ceiling, 1), "unit": "TFLOP/s", "frac": round(achieved / ceiling, 4),
+            "how": "back-to-back v_mfma_f32_32x32x16_bf16 on every SIMD, N(0,1) bf16 operands rotating "
+                   "over registers (fa_bwd_calib_mfma_bf16), after the timed steps"}
+        _log(f"MFMA ceiling on N(0,1) operands: {ceiling:.1f} TFLOP/s")
     if not args.no_cpu_baseline:
         _log("cpu baseline: oracle on one head")
         out["cpu_baseline"] = _cpu_baseline(w, q, k, v, o, do, lse)

@@ -35,6 +35,7 @@ EXPORTED = (
     "fa_bwd_status_string",
     "fa_bwd_debug_visibility",
     "fa_bwd_debug_dropout_keep",
+    "fa_bwd_calib_mfma_bf16",
 )
 
 
@@ -113,8 +114,9 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_status_string.restype = ctypes.c_char_p
     L.fa_bwd_debug_visibility.argtypes = [P, vp, vp]
     L.fa_bwd_debug_dropout_keep.argtypes = [P, vp, vp]
+    L.fa_bwd_calib_mfma_bf16.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, vp]
     for name in ("fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_decode",
-                 "fa_bwd_debug_visibility", "fa_bwd_debug_dropout_keep"):
+                 "fa_bwd_debug_visibility", "fa_bwd_debug_dropout_keep", "fa_bwd_calib_mfma_bf16"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L
     return L

@@ -156,3 +156,17 @@ def debug_dropout_keep(p: _lib.FaBwdParams, device) -> torch.Tensor:
     out = torch.empty((p.batch, p.num_heads, p.seq_q, p.seq_k), dtype=torch.uint8, device=device)
     _lib.check("fa_bwd_debug_dropout_keep", _lib.lib().fa_bwd_debug_dropout_keep(ctypes.byref(p), _vp(out), _stream()))
     return out
+
+
+def calib_mfma_bf16(operands: torch.Tensor, sink: torch.Tensor, blocks: int, iters: int) -> None:
+    """Enqueue the MFMA calibration kernel (see include/fa_bwd.h) on the current stream.
+
+    operands: bf16 device tensor of at least 2048 * 8 elements; sink: fp32 device
+    tensor of at least blocks * 256 elements.  Work: blocks * 4 * iters * 32 * 32768 FLOP.
+    """
+    if operands.dtype != torch.bfloat16 or operands.numel() < 2048 * 8 or not operands.is_contiguous():
+        raise ValueError("operands: contiguous bf16 tensor of at least 16384 elements")
+    if sink.dtype != torch.float32 or sink.numel() < blocks * 256:
+        raise ValueError("sink: fp32 tensor of at least blocks*256 elements")
+    _lib.check("fa_bwd_calib_mfma_bf16",
+               _lib.lib().fa_bwd_calib_mfma_bf16(_vp(operands), _vp(sink), blocks, iters, _stream()))

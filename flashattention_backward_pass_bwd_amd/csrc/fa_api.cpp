@@ -196,4 +196,12 @@ fa_status fa_bwd_debug_dropout_keep(const fa_bwd_params* p, uint8_t* out, fa_str
   return hip_status(fa::launch_debug_dropout(a, out, as_stream(stream)));
 }
 
+fa_status fa_bwd_calib_mfma_bf16(const void* operands, float* sink, int32_t blocks, int32_t iters,
+                                 fa_stream_t stream) {
+  if (operands == nullptr || sink == nullptr) return FA_ERR_NULL;
+  if (blocks <= 0 || iters <= 0) return FA_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(operands) & 15u) != 0) return FA_ERR_ALIGN;
+  return hip_status(fa::launch_calib_mfma(operands, sink, blocks, iters, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -1,7 +1,10 @@
 // Test hooks: materialise, for every (b, h, i, j), the counted-element
 // predicate and the dropout keep bit, using the same device functions the
 // backward kernels evaluate (visible, mask_at, drop_row_key, drop_keep).
+// And a calibration kernel for the MFMA roofline: the bf16 MFMA rate the chip
+// sustains on given operand data with every SIMD busy.
 #include "fa_internal.h"
+#include "fa_tiles.h"
 
 namespace fa {
 
@@ -31,6 +34,47 @@ __global__ __launch_bounds__(256) void debug_dropout_kernel(PrefillArgs a, uint8
     const int b = (int)(bh / a.Hq);
     out[e] = (!a.drop || drop_keep(drop_row_key(a, b, h, i), j, a.drop_thr)) ? 1 : 0;
   }
+}
+
+// Back-to-back v_mfma_f32_32x32x16_bf16 only: one wave per SIMD, four
+// independent accumulator chains, the A operand rotating over four VGPR blocks
+// and the B operand over four AGPR blocks (as in the tile kernels, no two
+// neighbouring MFMAs read the same registers), nothing else in the loop.
+// Thread t reads A block i from ops[t + 256 i] and B block i from
+// ops[1024 + t + 256 i] (2048 16-byte values).  A sum of the accumulators
+// goes to sink[block*256 + t] so the work cannot be dropped.
+__global__ __launch_bounds__(256, 1) void calib_mfma_kernel(const bf16x8* __restrict__ ops, float* __restrict__ sink,
+                                                            int iters) {
+  const int t = threadIdx.x;
+  bf16x8 av[4], bv[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    av[i] = ops[t + 256 * i];
+    bv[i] = ld16_agpr(ops + 1024 + t + 256 * i);  // straight into AGPRs (no VALU write before the MFMAs)
+  }
+  wait_all_vmem();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  f32x16 acc[4] = {};
+  // two wait states between the VALU zeroing of the accumulators and the first MFMA
+  asm volatile("s_nop 1" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc[j & 3]) : "v"(av[(j >> 2) & 3]), "a"(bv[(j >> 1) & 3]));
+  }
+  // wait states before the accumulators are read by VALU
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  sink[blockIdx.x * 256 + t] = s;
+}
+
+hipError_t launch_calib_mfma(const void* ops, float* sink, int blocks, int iters, hipStream_t st) {
+  hipLaunchKernelGGL(calib_mfma_kernel, dim3(blocks), dim3(256), 0, st, static_cast<const bf16x8*>(ops), sink, iters);
+  return hipGetLastError();
 }
 
 static unsigned grid_for(const PrefillArgs& a) {

@@ -52,5 +52,6 @@ hipError_t launch_decode(const DecodeArgs& a, const float* k_hist, const float* 
 int decode_max_history(int g);
 hipError_t launch_debug_visibility(const PrefillArgs& a, uint8_t* out, hipStream_t st);
 hipError_t launch_debug_dropout(const PrefillArgs& a, uint8_t* out, hipStream_t st);
+hipError_t launch_calib_mfma(const void* ops, float* sink, int blocks, int iters, hipStream_t st);
 
 }  // namespace fa

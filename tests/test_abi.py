@@ -155,6 +155,16 @@ def test_invalid_decode_arguments():
     assert L.fa_bwd_decode_max_history(ctypes.byref(dp(n_heads=30))) == 0
 
 
+def test_invalid_calibration_arguments():
+    L = _lib.lib()
+    f = L.fa_bwd_calib_mfma_bf16
+    assert f(None, FAKE, 4, 1, None) == _lib.FA_ERR_NULL
+    assert f(FAKE, None, 4, 1, None) == _lib.FA_ERR_NULL
+    assert f(FAKE, FAKE, 0, 1, None) == _lib.FA_ERR_ARG
+    assert f(FAKE, FAKE, 4, -1, None) == _lib.FA_ERR_ARG
+    assert f(ctypes.c_void_p(4096 + 4), FAKE, 4, 1, None) == _lib.FA_ERR_ALIGN
+
+
 def test_status_strings():
     for code in range(-6, 1):
         s = _lib.status_string(code)

@@ -91,3 +91,35 @@ def test_keep_mask_recovered_from_dv():
         nz = got["dv"][0, h][:, :S].T != 0.0  # [i, j]
         assert np.array_equal(nz, keep & vis), h
         say(f"  head {h}: {int((keep & vis).sum())} kept of {int(vis.sum())} visible")
+
+
+def test_mfma_calibration_kernel_sums():
+    """The MFMA calibration kernel does the products it claims.
+
+    With one iteration, the sum of every accumulator element of a wave equals
+    sum over its 32 MFMAs of sum_k (sum_m A[m,k]) (sum_n B[k,n]), where lane l
+    holds A[l%32][8(l/32) .. +7] and B[8(l/32) .. +7][l%32]; MFMA j uses A block
+    (j/4)%4 and B block (j/2)%4.  Checked per wave against fp64 on the host.
+    """
+    g = torch.Generator(device="cpu").manual_seed(3)
+    ops = torch.randn(2048 * 8, generator=g).to(torch.bfloat16)
+    blocks = 2
+    sink = torch.zeros(blocks * 256, dtype=torch.float32, device="cuda")
+    api.calib_mfma_bf16(ops.cuda(), sink, blocks, 1)
+    torch.cuda.synchronize()
+    got = sink.cpu().double().view(blocks, 4, 64).sum(dim=2)  # per (block, wave)
+    v = ops.double().view(2048, 8)
+    for w in range(4):
+        t = 64 * w + torch.arange(64)
+        kblk = (torch.arange(64) // 32)  # lane's 8-wide k block
+        want, mag = 0.0, 0.0
+        for j in range(32):
+            a = v[t + 256 * ((j >> 2) & 3)]          # [64 lanes, 8]
+            b = v[1024 + t + 256 * ((j >> 1) & 3)]
+            for kb in range(2):
+                sel = kblk == kb
+                terms = a[sel].sum(dim=0) * b[sel].sum(dim=0)
+                want += float(terms.sum())
+                mag += float(terms.abs().sum())
+        for blk in range(blocks):
+            assert abs(float(got[blk, w]) - want) <= 1e-4 * mag + 1e-3, (blk, w, float(got[blk, w]), want, mag)
