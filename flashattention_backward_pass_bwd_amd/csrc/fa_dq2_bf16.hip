@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256, 1) void dq2_bf16_kernel(PrefillArgs a, const _
         auto ew_exp = [&](int rb, int r) {
           float x = s[rb][r];
           if constexpr (!FULL) {
-            const bool ok = (uint32_t)(8 * (r >> 2) + (r & 3) - lb[rb]) < span[rb];
+            const bool ok = elem_visible(r, lb[rb], span[rb]);
             x = ok ? x : -__builtin_inff();
           }
           s[rb][r] = __builtin_amdgcn_exp2f(x);

@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         auto ew_exp = [&](int r) {
           float x = se[r];
           if constexpr (!FULL) {
-            bool ok = (uint32_t)(8 * (r >> 2) + (r & 3) - lb) < span;
+            bool ok = elem_visible(r, lb, span);
             if constexpr (MASK) {
               const float mv = mk[r];
               ok = ok && !(mv <= kMaskedSentinel);

@@ -183,6 +183,16 @@ __device__ __forceinline__ bf16x2 pack_here(float x, float y) {
   return t;
 }
 
+// Element r of a lane's C-layout block is visible iff c(r) - lb < span
+// (unsigned), c(r) = 8*(r/4) + r%4.  The difference is made opaque here, in
+// the element's own slot, so the compiler does not hoist the sixteen compares
+// out of the loop body as lane masks held in SGPRs (which then spill).
+__device__ __forceinline__ bool elem_visible(int r, int lb, uint32_t span) {
+  uint32_t d = (uint32_t)(8 * (r >> 2) + (r & 3) - lb);
+  asm volatile("" : "+v"(d));
+  return d < span;
+}
+
 // Moves a value into accumulation registers once, so that later MFMAs read it
 // there as a B operand without a copy per use.
 __device__ __forceinline__ void to_agpr(bf16x8& v) { asm volatile("" : "+a"(v)); }
