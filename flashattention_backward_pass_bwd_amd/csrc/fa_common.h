@@ -56,6 +56,48 @@ __device__ __forceinline__ bool drop_keep(uint32_t rk, int j, uint32_t thr) {
   return fmix32(rk ^ ((uint32_t)j * 0x9E3779B9u)) >= thr;
 }
 
+// Cross-lane sums in registers, without LDS traffic: DPP moves within 16-lane
+// rows, ds_swizzle across 16 lanes, v_permlane32_swap across 32.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float swizzle_xor16(float x) {  // lane ^ 16 within each 32-lane half
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
+__device__ __forceinline__ float halves_sum(float x) {  // x[lane] + x[lane ^ 32]
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+}
+// Sum over each aligned group of N consecutive lanes (N = 1, 2, 4, ..., 64), in
+// every lane of the group: quad_perm swaps lanes 1 and 2 apart, the half-row
+// mirror pairs the two quads of an 8-lane half, the row mirror the two halves
+// of a 16-lane row.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp_mov<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x += dpp_mov<0x140>(x); // row_mirror
+  if constexpr (N >= 32) x += swizzle_xor16(x);
+  if constexpr (N >= 64) x = halves_sum(x);
+  return x;
+}
+// Sum over the lanes congruent to this one modulo M (M = 1, 2, 4, ..., 64), in
+// every such lane: row rotations by M, 2M, .., 8 within 16-lane rows, then
+// across 16 and 32.
+template <int M>
+__device__ __forceinline__ float strided_sum(float x) {
+  if constexpr (M <= 1) x += dpp_mov<0x121>(x);  // row_ror:1
+  if constexpr (M <= 2) x += dpp_mov<0x122>(x);  // row_ror:2
+  if constexpr (M <= 4) x += dpp_mov<0x124>(x);  // row_ror:4
+  if constexpr (M <= 8) x += dpp_mov<0x128>(x);  // row_ror:8
+  if constexpr (M <= 16) x += swizzle_xor16(x);
+  if constexpr (M <= 32) x = halves_sum(x);
+  return x;
+}
+
 // Geometric visibility (ferrotensor-backend flash_attention_v2_backward.wgsl, fab2_visible).
 __device__ __forceinline__ bool visible(const PrefillArgs& a, int i, int j) {
   if (i >= a.Sq || j >= a.Sk || i < 0 || j < 0) return false;

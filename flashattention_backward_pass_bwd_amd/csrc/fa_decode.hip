@@ -84,8 +84,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a, co
       }
 #pragma unroll
       for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int m = LPR / 2; m > 0; m >>= 1) acc[g] += __shfl_xor(acc[g], m, LPR);
+        acc[g] = group_sum<LPR>(acc[g]);
       if (j < len && lr < G) {
         float val = acc[0];
 #pragma unroll
@@ -105,8 +104,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a, co
     for (int g = 0; g < G; ++g) part[g] += pr[(int64_t)g * len + j] * smem[j * G + g];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-#pragma unroll
-    for (int m = 32; m > 0; m >>= 1) part[g] += __shfl_xor(part[g], m, 64);
+    part[g] = group_sum<64>(part[g]);
   }
   if (lane == 0)
 #pragma unroll
@@ -165,10 +163,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a, co
     for (int c = 0; c < NV4; ++c)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float x = acc[g][c][e];
-#pragma unroll
-        for (int m = LPR; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
-        acc[g][c][e] = x;
+        acc[g][c][e] = strided_sum<LPR>(acc[g][c][e]);
       }
   __syncthreads();  // every wave is done reading d_scores from smem
   // ... then over the 16 waves through LDS: smem[wave][g][d].

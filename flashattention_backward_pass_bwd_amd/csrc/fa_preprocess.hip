@@ -3,7 +3,7 @@
 // ferrotensor-backend flash_attention_v2_backward.wgsl, pass-1 Delta).
 //
 // HBM-bound: each row is read once as 16-byte chunks by a group of lanes,
-// multiplied in fp32 and reduced across the group with butterfly shuffles.
+// multiplied in fp32 and reduced across the group with DPP lane moves.
 #include "fa_internal.h"
 
 namespace fa {
@@ -30,8 +30,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PrefillArgs a, const T*
 #pragma unroll
     for (int e = 0; e < CH; ++e) acc += to_f32(g[e]) * to_f32(o[e]);
   }
-#pragma unroll
-  for (int s = LPR / 2; s > 0; s >>= 1) acc += __shfl_xor(acc, s, LPR);
+  acc = group_sum<LPR>(acc);
   if (row < rows && lane_in_row == 0) delta[row] = acc;
 }
 
