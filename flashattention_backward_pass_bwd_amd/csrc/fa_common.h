@@ -65,10 +65,16 @@ __device__ __forceinline__ float dpp_mov(float x) {
 __device__ __forceinline__ float swizzle_xor16(float x) {  // lane ^ 16 within each 32-lane half
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
 }
+// v_permlane32_swap_b32 a, b exchanges a's lanes 32-63 with b's lanes 0-31;
+// with a = b = x, a then holds x's lanes 0-31 twice and b its lanes 32-63
+// twice, so a + b = x[lane] + x[lane ^ 32] in every lane.  Inline assembly:
+// this compiler's builtin for it adds one of its two results to itself when
+// both inputs are the same value.  Two wait states separate the VALU copies
+// from the permute.
 __device__ __forceinline__ float halves_sum(float x) {  // x[lane] + x[lane ^ 32]
-  const unsigned u = __builtin_bit_cast(unsigned, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return a + b;
 }
 // Sum over each aligned group of N consecutive lanes (N = 1, 2, 4, ..., 64), in
 // every lane of the group: quad_perm swaps lanes 1 and 2 apart, the half-row

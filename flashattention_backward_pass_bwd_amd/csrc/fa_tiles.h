@@ -63,16 +63,26 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 // dynamically indexed register arrays or messages), which
 // tests/test_asm_checks.py checks on the generated assembly.  One wait state
 // separates the M0 write from the copy.
+// The base is wave-uniform by contract; it is read into SGPRs explicitly
+// (readfirstlane, free when the compiler already holds it there), because an
+// "s" operand the compiler happens to keep in VGPRs is not moved for the asm.
+__device__ __forceinline__ uint64_t sgpr_ptr(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)));
+               : "v"(voff), "s"(sgpr_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)));
 }
 
 __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                :
-               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds)));
+               : "v"(voff), "s"(sgpr_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)));
 }
 
 // Buffer descriptor of a raw fp32 range of `bytes` bytes at base: a read at a

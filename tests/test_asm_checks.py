@@ -168,6 +168,19 @@ def _result_reads(text, need=12):
     return bad
 
 
+def test_sources_assemble():
+    # The checks below read the compiler's assembly text (-S), which is emitted
+    # even when an inline-asm operand is invalid; assembling catches that.
+    def obj(src):
+        with tempfile.TemporaryDirectory() as d:
+            cmd = [build._hipcc(), *build.COMMON_FLAGS, *build.EXTRA_FLAGS.get(src, []), "--cuda-device-only", "-x", "hip",
+                   "-c", os.path.join(build.CSRC, src), "-o", os.path.join(d, src + ".o")]
+            return src, subprocess.run(cmd, capture_output=True, text=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        for src, res in ex.map(obj, SOURCES):
+            assert res.returncode == 0, (src, res.stderr[-2000:])
+
+
 def test_copy_sources_found():
     assert {"fa_dkdv_bf16.hip", "fa_dq_bf16.hip"} <= set(SOURCES)
 
