@@ -30,6 +30,9 @@ EXPORTED = (
     "fa_bwd_preprocess",
     "fa_bwd_dkdv",
     "fa_bwd_dq",
+    "fa_bwd_ds_workspace_size",
+    "fa_bwd_dkdv_ds",
+    "fa_bwd_dq_ds",
     "fa_bwd_decode",
     "fa_bwd_decode_max_history",
     "fa_bwd_status_string",
@@ -107,6 +110,10 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_preprocess.argtypes = [P, vp, vp, vp, vp]
     L.fa_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.fa_bwd_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
+    u64 = ctypes.c_uint64
+    L.fa_bwd_ds_workspace_size.argtypes = [P, ctypes.POINTER(u64)]
+    L.fa_bwd_dkdv_ds.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, u64, vp]
+    L.fa_bwd_dq_ds.argtypes = [P, vp, vp, u64, vp, vp]
     L.fa_bwd_decode.argtypes = [DP, vp, vp, vp, vp, vp, vp, vp]
     L.fa_bwd_decode_max_history.argtypes = [DP]
     L.fa_bwd_decode_max_history.restype = ctypes.c_int32
@@ -115,7 +122,8 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_debug_visibility.argtypes = [P, vp, vp]
     L.fa_bwd_debug_dropout_keep.argtypes = [P, vp, vp]
     L.fa_bwd_calib_mfma_bf16.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, vp]
-    for name in ("fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_decode",
+    for name in ("fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_ds_workspace_size",
+                 "fa_bwd_dkdv_ds", "fa_bwd_dq_ds", "fa_bwd_decode",
                  "fa_bwd_debug_visibility", "fa_bwd_debug_dropout_keep", "fa_bwd_calib_mfma_bf16"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L

@@ -113,15 +113,57 @@ def dq(p: _lib.FaBwdParams, q, k, v, do, lse, delta, dq_out=None):
     return dq_out
 
 
+def ds_workspace_bytes(p: _lib.FaBwdParams) -> int:
+    """Bytes of dS workspace fa_bwd_dkdv_ds / fa_bwd_dq_ds need for these parameters."""
+    n = ctypes.c_uint64(0)
+    _lib.check("fa_bwd_ds_workspace_size", _lib.lib().fa_bwd_ds_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return int(n.value)
+
+
+def ds_workspace(p: _lib.FaBwdParams, device) -> torch.Tensor:
+    """A workspace tensor of the size the dS entry points need (at least 16 bytes)."""
+    return torch.empty(max(ds_workspace_bytes(p), 16), dtype=torch.uint8, device=device)
+
+
+def dkdv_ds(p: _lib.FaBwdParams, q, k, v, do, lse, delta, ws, dk=None, dv=None):
+    """dK/dV pass that also stores dS into the workspace ws (uint8 device tensor)."""
+    _same_layout(q, do)
+    _same_layout(k, v)
+    dk = _like(k) if dk is None else dk
+    dv = _like(v) if dv is None else dv
+    _same_layout(k, dk, dv)
+    _lib.check("fa_bwd_dkdv_ds", _lib.lib().fa_bwd_dkdv_ds(
+        ctypes.byref(p), _vp(q), _vp(k), _vp(v), _vp(do), _vp(lse), _vp(delta), _vp(dk), _vp(dv),
+        _vp(ws), ws.numel() * ws.element_size(), _stream()))
+    return dk, dv
+
+
+def dq_ds(p: _lib.FaBwdParams, q, k, ws, dq_out=None):
+    """dQ from the dS that dkdv_ds stored in ws (q gives dQ's shape and layout only)."""
+    dq_out = _like(q) if dq_out is None else dq_out
+    _same_layout(q, dq_out)
+    _lib.check("fa_bwd_dq_ds", _lib.lib().fa_bwd_dq_ds(
+        ctypes.byref(p), _vp(k), _vp(ws), ws.numel() * ws.element_size(), _vp(dq_out), _stream()))
+    return dq_out
+
+
 def backward(q, k, v, o, do, lse, *, scale, causal=False, causal_offset=0, window=0, dropout_p=0.0,
-             seed=0, mask=None):
-    """Delta preprocess, then the dK/dV and dQ passes; returns (dq, dk, dv, delta)."""
+             seed=0, mask=None, share_ds=False):
+    """Delta preprocess, then the dK/dV and dQ passes; returns (dq, dk, dv, delta).
+
+    share_ds (bf16): the dK/dV pass stores dS in a workspace and the dQ pass
+    reads it (fa_bwd_dkdv_ds, fa_bwd_dq_ds) instead of recomputing it."""
     p = make_params(q, k, scale=scale, causal=causal, causal_offset=causal_offset, window=window,
                     dropout_p=dropout_p, seed=seed, mask=mask)
     _same_layout(q, o, do)
     delta = preprocess(p, o, do)
-    dk_, dv_ = dkdv(p, q, k, v, do, lse, delta)
-    dq_ = dq(p, q, k, v, do, lse, delta)
+    if share_ds:
+        ws = ds_workspace(p, q.device)
+        dk_, dv_ = dkdv_ds(p, q, k, v, do, lse, delta, ws)
+        dq_ = dq_ds(p, q, k, ws)
+    else:
+        dk_, dv_ = dkdv(p, q, k, v, do, lse, delta)
+        dq_ = dq(p, q, k, v, do, lse, delta)
     return dq_, dk_, dv_, delta
 
 

@@ -27,6 +27,7 @@ SOURCES = [
     "fa_dq.hip",
     "fa_dq_bf16.hip",
     "fa_dq2_bf16.hip",
+    "fa_dqs_bf16.hip",
     "fa_decode.hip",
     "fa_debug.hip",
     "fa_api.cpp",

@@ -95,6 +95,26 @@ fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
 
 fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// dS workspace of the workspace entry points: bf16 only; fills in the tiles
+// per (b, h) and the bytes needed (layout in fa_common.h).
+fa_status check_ws(const fa_bwd_params* p, PrefillArgs* a, uint64_t* bytes) {
+  fa_status s = check_prefill(p, a);
+  if (s != FA_OK) return s;
+  if (p->dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  const int nkb = (p->seq_k + fa::kWsKeys - 1) / fa::kWsKeys;
+  const int64_t nqt = (p->seq_q + fa::kWsRows - 1) / fa::kWsRows;
+  if (nqt * ((a->group + 3) / 4) * p->batch * p->num_kv_heads >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
+  int64_t tiles = 0;
+  for (int kb = 0; kb < nkb; ++kb) {
+    int ql, n;
+    fa::ws_run(*a, kb, ql, n);
+    tiles += n;
+  }
+  a->ws_tiles = tiles;
+  *bytes = (uint64_t)tiles * (uint64_t)p->batch * (uint64_t)p->num_heads * (uint64_t)fa::kWsTileBytes;
+  return FA_OK;
+}
+
 hipStream_t as_stream(fa_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
@@ -139,6 +159,42 @@ fa_status fa_bwd_dq(const fa_bwd_params* p, const void* Q, const void* K, const 
       (reinterpret_cast<uintptr_t>(L) & 3u) || (reinterpret_cast<uintptr_t>(delta) & 3u))
     return FA_ERR_ALIGN;
   return hip_status(fa::launch_dq(a, p->dtype, p->head_dim, Q, K, V, dO, L, delta, dQ, as_stream(stream)));
+}
+
+fa_status fa_bwd_ds_workspace_size(const fa_bwd_params* p, uint64_t* bytes) {
+  PrefillArgs a;
+  if (p == nullptr || bytes == nullptr) return FA_ERR_NULL;
+  return check_ws(p, &a, bytes);
+}
+
+fa_status fa_bwd_dkdv_ds(const fa_bwd_params* p, const void* Q, const void* K, const void* V, const void* dO,
+                         const float* L, const float* delta, void* dK, void* dV, void* ds_ws, uint64_t ws_bytes,
+                         fa_stream_t stream) {
+  PrefillArgs a;
+  uint64_t need = 0;
+  if (p == nullptr || Q == nullptr || K == nullptr || V == nullptr || dO == nullptr || L == nullptr ||
+      delta == nullptr || dK == nullptr || dV == nullptr || ds_ws == nullptr)
+    return FA_ERR_NULL;
+  fa_status s = check_ws(p, &a, &need);
+  if (s != FA_OK) return s;
+  if (ws_bytes < need) return FA_ERR_ARG;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(dK) || !aligned16(dV) ||
+      !aligned16(ds_ws) || (reinterpret_cast<uintptr_t>(L) & 3u) || (reinterpret_cast<uintptr_t>(delta) & 3u))
+    return FA_ERR_ALIGN;
+  return hip_status(
+      fa::launch_dkdv_bf16_ws(a, p->head_dim, Q, K, V, dO, L, delta, dK, dV, ds_ws, as_stream(stream)));
+}
+
+fa_status fa_bwd_dq_ds(const fa_bwd_params* p, const void* K, const void* ds_ws, uint64_t ws_bytes, void* dQ,
+                       fa_stream_t stream) {
+  PrefillArgs a;
+  uint64_t need = 0;
+  if (p == nullptr || K == nullptr || ds_ws == nullptr || dQ == nullptr) return FA_ERR_NULL;
+  fa_status s = check_ws(p, &a, &need);
+  if (s != FA_OK) return s;
+  if (ws_bytes < need) return FA_ERR_ARG;
+  if (!aligned16(K) || !aligned16(ds_ws) || !aligned16(dQ)) return FA_ERR_ALIGN;
+  return hip_status(fa::launch_dqs_bf16(a, p->head_dim, K, ds_ws, dQ, as_stream(stream)));
 }
 
 int32_t fa_bwd_decode_max_history(const fa_decode_params* p) {

@@ -33,6 +33,7 @@ struct PrefillArgs {
   const float* mask;
   int64_t msb, msh, msq, msk;
   uint32_t mask_rec;  // bytes of one (b, h) slice of the mask: ((Sq-1)*msq + (Sk-1)*msk + 1)*4 (bf16 path)
+  int64_t ws_tiles;   // dS workspace tiles per (b, h) (workspace entry points only)
 };
 
 // MurmurHash3 32-bit finaliser (Appleby, public domain).
@@ -178,16 +179,42 @@ __device__ __forceinline__ void key_range(const PrefillArgs& a, int q0, int q1, 
   end = (int)max(e, bg);
 }
 
-// Queries [begin, end) that can see any key in [k0, k1].
-__device__ __forceinline__ void query_range(const PrefillArgs& a, int k0, int k1, int& begin, int& end) {
+// Queries [begin, end) that can see any key in [k0, k1] (also used by the host
+// to size the dS workspace, so written without device-only helpers).
+__host__ __device__ __forceinline__ void query_range(const PrefillArgs& a, int k0, int k1, int& begin, int& end) {
   long bg = 0, e = a.Sq;
-  if (a.causal) bg = max(0L, (long)k0 - a.offset);
+  if (a.causal) bg = (long)k0 - a.offset > 0 ? (long)k0 - a.offset : 0L;
   if (a.window > 0) {
-    e = min(e, max(0L, (long)k1 + a.window - a.offset));
-    if (!a.causal) bg = max(bg, (long)k0 - a.window - a.offset + 1);
+    const long top = (long)k1 + a.window - a.offset;
+    e = e < top ? e : (top > 0 ? top : 0L);
+    if (!a.causal) {
+      const long lo = (long)k0 - a.window - a.offset + 1;
+      bg = bg > lo ? bg : lo;
+    }
   }
-  begin = (int)min(bg, (long)a.Sq);
-  end = (int)max(e, (long)begin);
+  begin = (int)(bg < (long)a.Sq ? bg : (long)a.Sq);
+  end = (int)(e > (long)begin ? e : (long)begin);
+}
+
+// The dS workspace (filled by the dK/dV pass in its workspace mode, read by
+// the dQ pass over stored dS).  Its unit is a tile of 64 query rows x 128 keys
+// (one key block of the dK/dV pass), 16 KB of bf16: [row half m][32-key group
+// w][row group t (16 rows)][key k][row half h (8 rows)][8 rows], the rows of a
+// half in the order the MFMA result registers hold them (within each 16 rows,
+// quads 1 and 2 swapped); (w, t) is one 1 KB store of the dK/dV pass's wave w
+// and keys 64j .. 64j+63 of a row half are 4 KB in one piece.  Per (b, h) the tiles follow
+// key block by key block; key block kb stores query tiles qlo .. qlo+n-1, the
+// 64-row tiles that meet the rows query_range gives for its keys.
+constexpr int kWsRows = 64;
+constexpr int kWsKeys = 128;
+constexpr int kWsTileBytes = kWsRows * kWsKeys * 2;
+__host__ __device__ __forceinline__ void ws_run(const PrefillArgs& a, int kb, int& qlo, int& n) {
+  const int k0 = kb * kWsKeys;
+  const int k1 = k0 + kWsKeys - 1 < a.Sk - 1 ? k0 + kWsKeys - 1 : a.Sk - 1;
+  int qb, qe;
+  query_range(a, k0, k1, qb, qe);
+  qlo = qb / kWsRows;
+  n = qe > qb ? (qe - 1) / kWsRows - qlo + 1 : 0;
 }
 
 // ----------------------------------------------------------------------------

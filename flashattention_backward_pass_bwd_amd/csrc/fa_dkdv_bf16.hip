@@ -32,6 +32,12 @@
 // single exp2; without dropout the dP chain starts from -Delta and yields
 // dP - Delta directly.  For causal attention without a window, block i
 // also takes key block nkb-1-i, so every block carries the same work.
+//
+// Workspace mode (WS): the pass also stores every tile's dS, as the bf16 values
+// its dK contraction used, into the dS workspace (layout in fa_common.h) for
+// the dQ pass over stored dS.  Query tiles then start on a multiple of 64
+// rows (the rows added below the first visible one are invisible), and each
+// dV/dK section stores the dS of its half with two 16-byte stores per lane.
 #include <type_traits>
 
 #include "fa_internal.h"
@@ -42,7 +48,7 @@ namespace fa {
 // MK: 0 no mask, 1 a mask of any strides, 2 a mask whose keys are contiguous and
 // whose 4-key groups are 16-byte aligned (staged with one 16-byte copy per lane
 // for 8 rows of the wave's 32 keys).
-template <int D, int MK, bool DROP>
+template <int D, int MK, bool DROP, bool WS>
 __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const __bf16* __restrict__ Q,
                                                            const __bf16* __restrict__ K,
                                                            const __bf16* __restrict__ V,
@@ -50,7 +56,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
                                                            const float* __restrict__ L,
                                                            const float* __restrict__ Dl,
                                                            __bf16* __restrict__ dK, __bf16* __restrict__ dV,
-                                                           int nkb, int paired) {
+                                                           unsigned char* __restrict__ ws, int nkb, int paired) {
   constexpr bool MASK = MK != 0;
   constexpr bool MVEC = MK == 2;
   constexpr int BQ = 64;
@@ -162,6 +168,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
 
     int qb, qe;
     query_range(a, k0, min(k0 + kDkdvKeysPerBlock, a.Sk) - 1, qb, qe);
+    static_assert(!WS || (BQ == kWsRows && kDkdvKeysPerBlock == kWsKeys), "workspace tiles are the pass's tiles");
+    int64_t ws_p = 0;  // WS: workspace tiles of the key blocks before this one, per (b, h)
+    if constexpr (WS) {
+      qb -= qb % BQ;
+      for (int k = 0; k < kb; ++k) {
+        int ql, n;
+        ws_run(a, k, ql, n);
+        ws_p += n;
+      }
+    }
     const int ntq = (qe - qb + BQ - 1) / BQ;
     const int ntiles = ntq * a.group;
 
@@ -301,7 +317,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       // mask copies of a step too, and those of section A issued after its last
       // tile copy, 16 / PER of them).
       constexpr int NMV = MASK ? kMaskPerStep + kMaskLateA : 0;
-      auto wait_prev = [&]() { wait_vmcnt<2 * NIW + NMV + 1>(); };
+      // WS: the dS stores of the previous step's sections B and D come after
+      // those copies too.
+      constexpr int NWS = WS ? 4 : 0;
+      auto wait_prev = [&]() { wait_vmcnt<2 * NIW + NMV + 1 + NWS>(); };
+      // WS: lane l stores the dS of its key (32*wave + l%32) for rows 16t + 8*h2
+      // .. +7 (register order) of half m at m*8192 + 2048*wave + 1024t + 32*(l%32)
+      // + 16*h2 bytes of the tile: each store writes 1 KB in one piece.
+      const uint32_t ws_lane = (uint32_t)(2048 * wave + 32 * l32 + 16 * h2);
 
       // Instruction order inside a step is fixed by hand: one wave per SIMD means
       // the MFMAs overlap only the VALU and LDS work placed between them, so every
@@ -449,7 +472,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         auto mask_rd = [&](int kk) {
           if constexpr (MASK && !FULL) {
             if (kk < NSD) {
-              wait_vmcnt<MVEC ? kMaskWaitV : kMaskWait>();
+              // (WS: the two dS stores of the dV/dK section in between count too)
+              wait_vmcnt<(MVEC ? kMaskWaitV : kMaskWait) + (WS ? 2 : 0)>();
 #pragma unroll
               for (int i = 0; i < 16 / NSD; ++i) {
                 const int r = kk * (16 / NSD) + i;
@@ -629,6 +653,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         const int lst4 = (it + 4) & (NSL - 1);
         const int qt = qb + t * BQ;
         const int h = kvh * a.group + g;
+        unsigned char* wsb = nullptr;  // WS: this step's workspace tile
+        if constexpr (WS) wsb = ws + ((int64_t)(b * a.Hq + h) * a.ws_tiles + ws_p + t) * kWsTileBytes;
+        auto store_ds = [&](int n, int half, const bf16x8 (&d)[2]) {
+          if constexpr (WS) {
+            if (n == NDK - 2) st16_nt(wsb, ws_lane + 8192u * half, d[0]);
+            if (n == NDK - 1) st16_nt(wsb, ws_lane + 8192u * half + 1024u, d[1]);
+          }
+        };
         bf16x8 pm[2], ds[2];
         bf16x4 trp[2 * NP];
         f32x16 s1, dp1;
@@ -668,6 +700,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           if (n >= 1) copies_at(next, 0, n - 1, NDK);
           pre_at(n, 0, stq1, lst1, 1, lst);
           if (n == NDK / 2) fix_rd(lst2);  // L/Delta of tile it+2 (its copy landed before this step's barrier)
+          store_ds(n, 0, ds);
         });
         // C: S/dP of half 0 of tile it+1 with exp/dS of half 1; each slot then
         // stages the mask of half 0 of tile it+1 in place of the elements it used
@@ -681,6 +714,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         sec_dkv(1, stq, trp, pm, ds, [&](int n) {
           copies_at(next, 2 * PER, n, NDK);
           pre_at(n, 1, stq1, lst1, 0, lst1);
+          store_ds(n, 1, ds);
         });
         pend = next;
         cq = cl_now;
@@ -735,38 +769,45 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
   }
 }
 
-template <int D, int MK, bool DROP>
+template <int D, int MK, bool DROP, bool WS>
 static hipError_t launch_t(const PrefillArgs& a, const void* Q, const void* K, const void* V, const void* dO,
-                           const float* L, const float* delta, void* dK, void* dV, hipStream_t st) {
+                           const float* L, const float* delta, void* dK, void* dV, void* ws, hipStream_t st) {
   const int nkb = (a.Sk + kDkdvKeysPerBlock - 1) / kDkdvKeysPerBlock;
   const int paired = (a.causal && a.window == 0 && nkb > 1) ? 1 : 0;
   const int nwi = paired ? (nkb + 1) / 2 : nkb;
   const unsigned grid = (unsigned)(nwi * a.B * a.Hkv);
-  hipLaunchKernelGGL((dkdv_bf16_kernel<D, MK, DROP>), dim3(grid), dim3(256), 0, st, a,
+  hipLaunchKernelGGL((dkdv_bf16_kernel<D, MK, DROP, WS>), dim3(grid), dim3(256), 0, st, a,
                      static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
                      static_cast<const __bf16*>(dO), L, delta, static_cast<__bf16*>(dK), static_cast<__bf16*>(dV),
-                     nkb, paired);
+                     static_cast<unsigned char*>(ws), nkb, paired);
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool WS>
 static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, const void* V, const void* dO,
-                           const float* L, const float* delta, void* dK, void* dV, hipStream_t st) {
+                           const float* L, const float* delta, void* dK, void* dV, void* ws, hipStream_t st) {
   const bool drop = a.drop != 0;
   const int mk = a.mask == nullptr ? 0 : (mask_keys_contiguous(a) ? 2 : 1);
-  if (mk == 2) return drop ? launch_t<D, 2, true>(a, Q, K, V, dO, L, delta, dK, dV, st)
-                           : launch_t<D, 2, false>(a, Q, K, V, dO, L, delta, dK, dV, st);
-  if (mk == 1) return drop ? launch_t<D, 1, true>(a, Q, K, V, dO, L, delta, dK, dV, st)
-                           : launch_t<D, 1, false>(a, Q, K, V, dO, L, delta, dK, dV, st);
-  return drop ? launch_t<D, 0, true>(a, Q, K, V, dO, L, delta, dK, dV, st)
-              : launch_t<D, 0, false>(a, Q, K, V, dO, L, delta, dK, dV, st);
+  if (mk == 2) return drop ? launch_t<D, 2, true, WS>(a, Q, K, V, dO, L, delta, dK, dV, ws, st)
+                           : launch_t<D, 2, false, WS>(a, Q, K, V, dO, L, delta, dK, dV, ws, st);
+  if (mk == 1) return drop ? launch_t<D, 1, true, WS>(a, Q, K, V, dO, L, delta, dK, dV, ws, st)
+                           : launch_t<D, 1, false, WS>(a, Q, K, V, dO, L, delta, dK, dV, ws, st);
+  return drop ? launch_t<D, 0, true, WS>(a, Q, K, V, dO, L, delta, dK, dV, ws, st)
+              : launch_t<D, 0, false, WS>(a, Q, K, V, dO, L, delta, dK, dV, ws, st);
 }
 
 hipError_t launch_dkdv_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V,
                             const void* dO, const float* L, const float* delta, void* dK, void* dV,
                             hipStream_t st) {
-  return D == 64 ? launch_d<64>(a, Q, K, V, dO, L, delta, dK, dV, st)
-                 : launch_d<128>(a, Q, K, V, dO, L, delta, dK, dV, st);
+  return D == 64 ? launch_d<64, false>(a, Q, K, V, dO, L, delta, dK, dV, nullptr, st)
+                 : launch_d<128, false>(a, Q, K, V, dO, L, delta, dK, dV, nullptr, st);
+}
+
+hipError_t launch_dkdv_bf16_ws(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V,
+                               const void* dO, const float* L, const float* delta, void* dK, void* dV, void* ws,
+                               hipStream_t st) {
+  return D == 64 ? launch_d<64, true>(a, Q, K, V, dO, L, delta, dK, dV, ws, st)
+                 : launch_d<128, true>(a, Q, K, V, dO, L, delta, dK, dV, ws, st);
 }
 
 }  // namespace fa

@@ -57,12 +57,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 // as LDS writes and does not wait for every copy in flight before each later
 // LDS read, which would serialise the copy ring.  Callers order them with
 // wait_vmcnt (every wave waits for its own copies) and a block barrier.
+// The base (and M0's value) reach the asm in SGPRs, which the compiler may
+// have just written with VALU (v_readfirstlane_b32); gfx9 needs five wait
+// states between such a write and a vector memory instruction reading the
+// SGPR, and the compiler does not insert them in front of an asm statement, so
+// every copy and store here issues them itself (s_nop 4; with the M0 write,
+// six).  tests/test_asm_checks.py checks the generated assembly for it.
 // M0 holds the LDS address for the copy.  It is written without being saved:
 // the compiler itself never reads or writes M0 in the kernels that use these
 // copies (gfx9 LDS instructions do not need it, and these kernels have no
 // dynamically indexed register arrays or messages), which
 // tests/test_asm_checks.py checks on the generated assembly.  One wait state
-// separates the M0 write from the copy.
+// separates the M0 write from the copy (covered by the five above).
 // The base is wave-uniform by contract; it is read into SGPRs explicitly
 // (readfirstlane, free when the compiler already holds it there), because an
 // "s" operand the compiler happens to keep in VGPRs is not moved for the asm.
@@ -74,15 +80,38 @@ __device__ __forceinline__ uint64_t sgpr_ptr(const void* p) {
 }
 
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sgpr_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)));
 }
 
 __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dword %0, %1"
                :
                : "v"(voff), "s"(sgpr_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)));
+}
+
+// The same copy with the streaming cache policy (nt), for data read once.
+__device__ __forceinline__ void dma16_nt(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+               :
+               : "v"(voff), "s"(sgpr_ptr(sbase)), "s"(__builtin_amdgcn_readfirstlane(lds)));
+}
+
+// 16-byte store of a lane's register block at a wave-uniform base + 32-bit
+// lane offset, with the streaming cache policy (nt: written once, read by a
+// later kernel).  Inline assembly like the copies: the compiler places no
+// waits for it.  Stores count in vmcnt like loads (completing in issue
+// order), so callers' manual waits include the stores issued after the
+// accesses they wait for.  Its data registers are next written many
+// instructions later (more than the one wait state a store of more than 8
+// bytes needs).
+#ifndef FA_WS_STORE_POLICY
+#define FA_WS_STORE_POLICY " nt"
+#endif
+__device__ __forceinline__ void st16_nt(void* sbase, uint32_t voff, const bf16x8& v) {
+  asm volatile("s_nop 4\n\tglobal_store_dwordx4 %0, %1, %2" FA_WS_STORE_POLICY
+               : : "v"(voff), "v"(v), "s"(sgpr_ptr(sbase)));
 }
 
 // Buffer descriptor of a raw fp32 range of `bytes` bytes at base: a read at a
@@ -97,7 +126,7 @@ __device__ __forceinline__ rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
 // range).  Inline assembly like dma16, with M0 likewise; ordered after the
 // reads of the LDS it overwrites.
 __device__ __forceinline__ void dma_buf4(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tbuffer_load_dword %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");
@@ -106,7 +135,7 @@ __device__ __forceinline__ void dma_buf4(rsrc_t rsrc, uint32_t voff, uint32_t ld
 // The same for four consecutive fp32 per lane (16 bytes, 16-byte aligned):
 // lane l's values land at lds + 16*l.
 __device__ __forceinline__ void dma_buf16(rsrc_t rsrc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
                : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory");

@@ -142,6 +142,33 @@ fa_status fa_bwd_dq(const fa_bwd_params* p, const void* Q, const void* K, const 
                     fa_stream_t stream);
 
 /*
+ * The same two passes sharing dS through a caller-owned workspace (bf16 only):
+ * fa_bwd_dkdv_ds computes exactly what fa_bwd_dkdv does and also stores every
+ * visible tile's dS_ij ([wgsl-fa2] flash_bwd_dk_dv: the dS it forms for dK),
+ * rounded to bf16 as its dK contraction uses it; fa_bwd_dq_ds then computes
+ * dQ_i = scale * sum_j dS_ij K_j ([wgsl-fa2] flash_bwd_dq; [metal-dq] dQ sum)
+ * from the stored dS instead of recomputing S, P, dP and dS.  Run
+ * fa_bwd_dkdv_ds, then fa_bwd_dq_ds, on one stream (or order them); the
+ * workspace's contents between the two calls are opaque.
+ *
+ * fa_bwd_ds_workspace_size: bytes of workspace the two calls need for *p:
+ * batch * num_heads * T * 16384, T = the 64-row x 128-key tiles any element
+ * of which is visible (about seq_q * seq_k / 8192 for a full matrix, half of
+ * that when causal).  ds_ws: device memory, 16-byte aligned, at least that
+ * many bytes (ws_bytes); the library keeps no pointer to it.
+ * Errors as fa_bwd_dkdv, plus: FA_ERR_NULL (ds_ws or bytes NULL),
+ * FA_ERR_UNSUPPORTED (dtype fp32), FA_ERR_ARG (ws_bytes too small),
+ * FA_ERR_ALIGN (ds_ws not 16-byte aligned).  fa_bwd_dq_ds reads K and the
+ * workspace only; it writes every element of dQ.
+ */
+fa_status fa_bwd_ds_workspace_size(const fa_bwd_params* p, uint64_t* bytes);
+fa_status fa_bwd_dkdv_ds(const fa_bwd_params* p, const void* Q, const void* K, const void* V,
+                         const void* dO, const float* L, const float* delta, void* dK, void* dV,
+                         void* ds_ws, uint64_t ws_bytes, fa_stream_t stream);
+fa_status fa_bwd_dq_ds(const fa_bwd_params* p, const void* K, const void* ds_ws, uint64_t ws_bytes,
+                       void* dQ, fa_stream_t stream);
+
+/*
  * Decode-step backward, pass 1 ([wgsl-dec]): one query per head, unscaled
  * scores, probs supplied.  For each sequence n and head h (KV head
  * h / heads_per_kv):

@@ -59,7 +59,7 @@ def forward_inputs(w, inp):
     return round_out(o, w.dtype), lse.astype(np.float32)
 
 
-def gpu_backward(w, inp, o, lse, mask_dev=None):
+def gpu_backward(w, inp, o, lse, mask_dev=None, share_ds=False):
     """Run preprocess + dK/dV + dQ through the C ABI; returns numpy logical arrays."""
     q = dev(inp["q"], w.layout, w.dtype)
     k = dev(inp["k"], w.layout, w.dtype)
@@ -71,7 +71,8 @@ def gpu_backward(w, inp, o, lse, mask_dev=None):
         mask_dev = torch.from_numpy(inp["mask"]).cuda()
     dq, dk, dv, delta = api.backward(q, k, v, od, do, L, scale=w.scale, causal=w.causal,
                                      causal_offset=w.causal_offset, window=w.window,
-                                     dropout_p=w.dropout_p, seed=w.dropout_seed, mask=mask_dev)
+                                     dropout_p=w.dropout_p, seed=w.dropout_seed, mask=mask_dev,
+                                     share_ds=share_ds)
     torch.cuda.synchronize()
     return {"dq": logical(dq), "dk": logical(dk), "dv": logical(dv),
             "delta": delta.cpu().numpy().astype(np.float64)}

@@ -108,6 +108,8 @@ def test_invalid_prefill_arguments(field, value, code):
     assert L.fa_bwd_dq(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
     assert L.fa_bwd_debug_visibility(P, FAKE, None) == code
     assert L.fa_bwd_debug_dropout_keep(P, FAKE, None) == code
+    assert L.fa_bwd_dkdv_ds(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == code
+    assert L.fa_bwd_dq_ds(P, FAKE, FAKE, 1 << 40, FAKE, None) == code
 
 
 def test_null_and_misaligned_pointers():
@@ -153,6 +155,75 @@ def test_invalid_decode_arguments():
     assert call(dp(), None, FAKE, FAKE, FAKE, FAKE, FAKE) == _lib.FA_ERR_NULL
     assert call(dp(), FAKE, ctypes.c_void_p(4100), FAKE, FAKE, FAKE, FAKE) == _lib.FA_ERR_ALIGN
     assert L.fa_bwd_decode_max_history(ctypes.byref(dp(n_heads=30))) == 0
+
+
+def _ws_bytes(L, p):
+    n = ctypes.c_uint64(0)
+    assert L.fa_bwd_ds_workspace_size(ctypes.byref(p), ctypes.byref(n)) == _lib.FA_OK
+    return n.value
+
+
+def test_invalid_workspace_arguments():
+    L = _lib.lib()
+    p = _valid()
+    P = ctypes.byref(p)
+    need = _ws_bytes(L, p)
+    assert need > 0
+    odd = ctypes.c_void_p(4096 + 8)
+    assert L.fa_bwd_ds_workspace_size(None, None) == _lib.FA_ERR_NULL
+    assert L.fa_bwd_ds_workspace_size(P, None) == _lib.FA_ERR_NULL
+    dkdv = lambda ws, nb: L.fa_bwd_dkdv_ds(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, nb, None)
+    assert dkdv(None, need) == _lib.FA_ERR_NULL
+    assert dkdv(FAKE, need - 1) == _lib.FA_ERR_ARG
+    assert dkdv(odd, need) == _lib.FA_ERR_ALIGN
+    assert L.fa_bwd_dq_ds(P, FAKE, None, need, FAKE, None) == _lib.FA_ERR_NULL
+    assert L.fa_bwd_dq_ds(P, FAKE, FAKE, need, None, None) == _lib.FA_ERR_NULL
+    assert L.fa_bwd_dq_ds(P, FAKE, FAKE, need - 1, FAKE, None) == _lib.FA_ERR_ARG
+    assert L.fa_bwd_dq_ds(P, FAKE, odd, need, FAKE, None) == _lib.FA_ERR_ALIGN
+    assert L.fa_bwd_dq_ds(P, odd, FAKE, need, FAKE, None) == _lib.FA_ERR_ALIGN
+    p.dtype = _lib.FA_DTYPE_F32  # the shared-dS passes are bf16 only
+    n = ctypes.c_uint64(0)
+    assert L.fa_bwd_ds_workspace_size(P, ctypes.byref(n)) == _lib.FA_ERR_UNSUPPORTED
+    assert dkdv(FAKE, 1 << 40) == _lib.FA_ERR_UNSUPPORTED
+    assert L.fa_bwd_dq_ds(P, FAKE, FAKE, 1 << 40, FAKE, None) == _lib.FA_ERR_UNSUPPORTED
+
+
+# (seq_q, seq_k, causal, causal_offset, window): full, causal, offsets that
+# leave key blocks' first rows off the 64-row grid, windows with and without
+# causal, rows or keys nobody sees, and the extras workload's geometry.
+WS_GEOMS = [
+    (100, 120, 0, 0, 0),
+    (1100, 1100, 1, 0, 0),
+    (300, 520, 1, 220, 130),
+    (260, 400, 1, 157, 0),
+    (300, 150, 0, 0, 20),
+    (200, 190, 0, 5, 33),
+    (80, 300, 1, 0, 0),
+    (70, 70, 1, 0, 1),
+    (2048, 2048, 1, 0, 512),
+]
+
+
+@pytest.mark.parametrize("geom", WS_GEOMS)
+def test_ds_workspace_counts_visible_tiles(geom):
+    """The workspace holds one 16 KB tile per (b, h) and 64-row x 128-key block
+    with at least one visible element: checked against the oracle's own
+    visibility rule, counted by brute force."""
+    import numpy as np
+    import oracle
+    from oracle.attention import visible
+    sq, sk, causal, off, win = geom
+    L = _lib.lib()
+    p = _valid()
+    p.seq_q, p.seq_k, p.causal, p.causal_offset, p.window = sq, sk, causal, off, win
+    p.q_stride_b, p.kv_stride_b = sq * 8 * 128, sk * 2 * 128
+    vis = visible(np.arange(sq), np.arange(sk), sq, sk,
+                  oracle.Spec(scale=0.1, causal=bool(causal), causal_offset=off, window=win))
+    nt, nk = -(-sq // 64), -(-sk // 128)
+    pad = np.zeros((nt * 64, nk * 128), dtype=bool)
+    pad[:sq, :sk] = vis
+    tiles = int(pad.reshape(nt, 64, nk, 128).any(axis=(1, 3)).sum())
+    assert _ws_bytes(L, p) == p.batch * p.num_heads * tiles * 16384
 
 
 def test_invalid_calibration_arguments():

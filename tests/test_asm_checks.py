@@ -200,6 +200,76 @@ def test_detector_flags_compiler_m0_use():
     assert _m0_outside_inline_asm(text) == ["s_mov_b32 m0, -1"]
 
 
+_SREG = re.compile(r"^(s\[(\d+):(\d+)\]|s(\d+)|vcc)$")
+
+
+def _sregs(op):
+    m = _SREG.match(op.strip())
+    if not m:
+        return set()
+    if m.group(1) == "vcc":
+        return {"vcc"}
+    if m.group(2):
+        return {f"s{r}" for r in range(int(m.group(2)), int(m.group(3)) + 1)}
+    return {f"s{m.group(4)}"}
+
+
+def _vmem_sgpr_hazards(text):
+    """VMEM instructions (global_, buffer_, flat_, scratch_) reading an SGPR that a
+    VALU instruction (v_readfirstlane, a compare or carry-out into SGPRs) wrote
+    fewer than five wait states earlier.  gfx9 needs those five; the compiler
+    inserts them for its own instructions, but not in front of an inline-asm
+    statement whose SGPR input it just produced with VALU.  Straight-line code
+    (a label does not reset the count, which only undercounts across loop
+    back edges)."""
+    bad, since = [], {}
+    for line in text.splitlines():
+        s = line.split(";")[0].strip()
+        if re.match(r"^_Z\w*:", s):
+            since = {}
+            continue
+        if not s or s.startswith(".") or s.endswith(":"):
+            continue
+        mn, _, rest = s.partition(" ")
+        ops = [o.strip() for o in re.split(r",\s*", rest)] if rest else []
+        if re.match(r"^(global|buffer|flat|scratch)_", mn):
+            near = sorted(r for o in ops for r in _sregs(o.split(" ")[0]) if since.get(r, 99) < 5)
+            if near:
+                bad.append(f"{s}  ({', '.join(near)} written by VALU {min(since[r] for r in near)} wait states before)")
+        m = re.match(r"^s_nop\s+(\d+)$", s)
+        step = int(m.group(1)) + 1 if m else 1
+        for r in since:
+            since[r] += step
+        if mn.startswith("v_") and ops:
+            written = _sregs(ops[0])
+            if len(ops) > 1 and re.search(r"_co_|div_scale|mad_u64_u32|mad_i64_i32", mn):
+                written |= _sregs(ops[1])
+            for r in written:
+                since[r] = 0
+    return bad
+
+
+def test_vmem_sgpr_operands_after_valu_writes():
+    for src, text in _compiled().items():
+        assert _vmem_sgpr_hazards(text) == [], src
+
+
+def test_vmem_sgpr_detector_flags_plain_cases():
+    text = "\n".join([
+        "_ZN2fa1kEv:",
+        "\tv_readfirstlane_b32 s59, v151",
+        "\tv_readfirstlane_b32 s58, v150",
+        ";;#ASMSTART", "\tglobal_store_dwordx4 v160, v[4:7], s[58:59] nt", ";;#ASMEND",     # flagged
+        "\tv_readfirstlane_b32 s4, v1",
+        ";;#ASMSTART", "\ts_mov_b32 m0, s4", "\ts_nop 4", "\tglobal_load_lds_dwordx4 v3, s[4:5]", ";;#ASMEND",
+        "\tv_cmp_gt_i32_e64 s[6:7], v1, v2",
+        "\tbuffer_load_dword v1, v2, s[8:11], 0 offen",                                    # other SGPRs: fine
+        "\tglobal_load_dword v1, v2, s[6:7]",                                             # flagged
+    ])
+    bad = _vmem_sgpr_hazards(text)
+    assert len(bad) == 2 and "s[58:59]" in bad[0] and "s[6:7]" in bad[1], bad
+
+
 def test_no_write_hazards_around_asm_mfmas():
     for src, text in _compiled().items():
         assert "v_mfma_f32_32x32x16_bf16" in text, src

@@ -71,6 +71,41 @@ def test_prefill_parity(name):
     assert_close(got["dv"], dv, w.dtype, "dv")
 
 
+# The dS-sharing path (bf16): every bf16 case above, plus geometries whose first
+# visible row of a key block is not a multiple of 64 (the dK/dV pass then
+# aligns its tiles down), a query tile no key sees, and a group of 8 heads
+# (two wave chunks per query tile in the dQ pass) and of 1 (spare waves).
+DS_CASES = {n: w for n, w in CASES.items() if w.dtype == "bf16"}
+DS_CASES.update({
+    "ds_offset_unaligned_d128": synth.LONG_BF16.resized(num_heads=4, num_kv_heads=2, seq_q=260, seq_k=400,
+                                                        causal_offset=157, seed=31),
+    "ds_rows_nobody_sees_d64": synth.LONG_BF16.resized(head_dim=64, num_heads=2, num_kv_heads=1, seq_q=300,
+                                                       seq_k=150, causal=False, causal_offset=0, window=20,
+                                                       seed=32),
+    "ds_group8_window_mask_drop": synth.EXTRAS_BF16.resized(batch=1, num_heads=16, num_kv_heads=2, seq_q=333,
+                                                            seq_k=333, window=70, seed=33),
+    "ds_mha_noncausal_d64": synth.LONG_BF16.resized(head_dim=64, batch=2, num_heads=3, num_kv_heads=3,
+                                                    seq_q=190, seq_k=260, causal=False, seed=34),
+})
+
+
+@pytest.mark.parametrize("name", sorted(DS_CASES))
+def test_prefill_parity_shared_ds(name):
+    w = DS_CASES[name]
+    say(f"[parity shared dS] {name}: {w}")
+    inp = synth.prefill_inputs(w)
+    o, lse = forward_inputs(w, inp)
+    got = gpu_backward(w, inp, o, lse, share_ds=True)
+    delta, dq, dk, dv = oracle.backward(inp["q"], inp["k"], inp["v"], o, inp["do"], lse,
+                                        _spec(w), inp["mask"])
+    assert_close(got["dq"], dq, w.dtype, "dq")
+    assert_close(got["dk"], dk, w.dtype, "dk")
+    assert_close(got["dv"], dv, w.dtype, "dv")
+    again = gpu_backward(w, inp, o, lse, share_ds=True)
+    for k in ("dq", "dk", "dv"):
+        assert np.array_equal(got[k], again[k]), k  # no atomics: bitwise repeatable
+
+
 def _spec(w):
     from fa_testlib import spec_of
     return spec_of(w)
