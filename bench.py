@@ -42,6 +42,8 @@ def _args():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long", choices=["long", "extras", "causal_f32", "decode", "copy"])
+    ap.add_argument("--path", default="shared_ds", choices=["shared_ds", "recompute"],
+                    help="bf16: the dQ pass reads the dS the dK/dV pass stored (shared_ds) or recomputes it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mfma-ceiling", action="store_true",
                     help="skip the calibration of the bf16 MFMA rate on N(0,1) operands (about 0.5 s)")
@@ -223,6 +225,11 @@ def bench_prefill(args, w):
     dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=dev)
     dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=dev)
     dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=dev)
+    # bf16: the dK/dV pass stores dS and the dQ pass reads it (the workspace is
+    # allocated here, outside the timed steps); fp32: both passes recompute.
+    shared = w.dtype == "bf16" and args.path == "shared_ds"
+    ws = api.ds_workspace(p, dev) if shared else None
+    ws_bytes = api.ds_workspace_bytes(p) if shared else 0
 
     def step(ev=None):
         if ev is not None:
@@ -230,10 +237,16 @@ def bench_prefill(args, w):
         api.preprocess(p, o, do, delta)
         if ev is not None:
             ev[1].record()
-        api.dkdv(p, q, k, v, do, lse, delta, dk, dv)
+        if shared:
+            api.dkdv_ds(p, q, k, v, do, lse, delta, ws, dk, dv)
+        else:
+            api.dkdv(p, q, k, v, do, lse, delta, dk, dv)
         if ev is not None:
             ev[2].record()
-        api.dq(p, q, k, v, do, lse, delta, dq)
+        if shared:
+            api.dq_ds(p, q, k, ws, dq)
+        else:
+            api.dq(p, q, k, v, do, lse, delta, dq)
         if ev is not None:
             ev[3].record()
 
@@ -282,6 +295,7 @@ def bench_prefill(args, w):
                    "seq_q": w.seq_q, "seq_k": w.seq_k, "head_dim": w.head_dim, "layout": w.layout,
                    "causal": w.causal, "window": w.window, "mask_density": w.mask_density,
                    "dropout_p": w.dropout_p, "nominal_gflop": round(nominal / 1e9, 3),
+                   "path": "shared_ds" if shared else "recompute", "ds_workspace_bytes": ws_bytes,
                    "window_aware_gflop": round(10.0 * w.head_dim * pairs / 1e9, 3)},
         "kernels_ms": {"preprocess": round(t_pre, 4), "dkdv": round(t_dkdv, 4), "dq": round(t_dq, 4)},
         "roofline": {"kernel": "dkdv_kernel", "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
@@ -290,6 +304,16 @@ def bench_prefill(args, w):
                      "traffic_unit": "bytes per launch (HBM, FETCH_SIZE+WRITE_SIZE scaled by the copy calibration)",
                      "per_unit": "8*D FLOP per visible (b,h,i,j) pair", "units": pairs},
     }
+    if shared:
+        # the dQ pass over stored dS streams the workspace once: HBM-bound
+        esz = 2
+        dq_bytes = ws_bytes + (w.batch * w.num_kv_heads * w.seq_k * w.head_dim +
+                               w.batch * w.num_heads * w.seq_q * w.head_dim) * esz
+        gbs = dq_bytes / (t_dq * 1e-3) / 1e9
+        out["roofline_dq"] = {"kernel": "dqs_kernel", "bound": "hbm", "achieved": round(gbs, 1),
+                              "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                              "per_unit": "the stored dS (16 KB per visible 64x128 tile) + K read, dQ written",
+                              "algorithmic_bytes": dq_bytes}
     _log(f"timed {args.steps} steps: {ms:.3f} ms/step")
     if w.dtype == "bf16" and not args.no_mfma_ceiling:
         ceiling = _mfma_ceiling()
