@@ -46,6 +46,18 @@ __host__ __device__ __forceinline__ uint32_t fmix32(uint32_t x) {
   return x;
 }
 
+// fmix32's first step, x ^ (x >> 16), distributes over xor: fmix32(r ^ k) =
+// fmix32_tail(xs16(r) ^ xs16(k)).  The tile kernels apply xs16 once per row key
+// and once per key, and the rest per element.
+__host__ __device__ __forceinline__ uint32_t xs16(uint32_t x) { return x ^ (x >> 16); }
+__host__ __device__ __forceinline__ uint32_t fmix32_tail(uint32_t x) {
+  x *= 0x85EBCA6Bu;
+  x ^= x >> 13;
+  x *= 0xC2B2AE35u;
+  x ^= x >> 16;
+  return x;
+}
+
 // Per-row part of the dropout draw: fmix32(((b*Hq + h)*Sq + i) + fmix32(seed)), mod 2^32.
 __device__ __forceinline__ uint32_t drop_row_key(const PrefillArgs& a, int b, int h, int i) {
   uint32_t row = ((uint32_t)b * (uint32_t)a.Hq + (uint32_t)h) * (uint32_t)a.Sq + (uint32_t)i;

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     const uint32_t m_lvv = MVEC ? (((uint32_t)(lane >> 4) + 4u * ((lane >> 3) & 1)) * (uint32_t)a.msq +
                                    (uint32_t)(kw0 + 4 * (lane & 7))) * 4u
                                 : 0u;
-    const uint32_t jg = (uint32_t)jl * 0x9E3779B9u;  // key part of the dropout draw
+    const uint32_t jg = xs16((uint32_t)jl * 0x9E3779B9u);  // key part of the dropout draw, first xorshift applied
 
     int qb, qe;
     query_range(a, k0, min(k0 + kDkdvKeysPerBlock, a.Sk) - 1, qb, qe);
@@ -289,7 +289,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       };
       // L (wave 0) and Delta (wave 1) of a tile into an L ring stage (rows past
       // the end repeat the last row; waves 2 and 3 make the same copy into sDum),
-      // and the tile's dropout row keys (lanes 0-15 of each wave, 16 rows per wave).
+      // and the tile's dropout row keys, first xorshift applied (lanes 0-15 of each
+      // wave, 16 rows per wave).
       const float* const ld_src = (wave & 1) ? Dl : L;
       const uint32_t ld_dst = lds_addr(wave == 0 ? &sL[0][0] : (wave == 1 ? &sDel[0][0] : &sDum[wave & 1][0]));
       const uint32_t ld_stride = wave < 2 ? 4u * BQ : 0u;  // bytes per ring stage
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         if constexpr (DROP) {
           // the row's global index ((b*Hq + h)*Sq + i) mod 2^32 (drop_row_key)
           uint32_t* rp = lane < 16 ? &sRK[lst][16 * wave + lane] : reinterpret_cast<uint32_t*>(&sDum[1][lane]);
-          *rp = fmix32((uint32_t)c.loff + (uint32_t)(16 * wave + lane) + a.seed_mix);
+          *rp = xs16(fmix32((uint32_t)c.loff + (uint32_t)(16 * wave + lane) + a.seed_mix));
         }
       };
       // Once a stage's L/Delta landed and a barrier passed, each wave rewrites 16
@@ -435,23 +436,20 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         float mk[16];  // mask values of the half (MASK), read ahead from sM
         // exp of element r (C-layout register r of half me); se holds
         // S*scale*log2(e) - L*log2(e).
+        // A mask value at or below the -1e30 sentinel excludes the element: added
+        // in the exponent it makes exp2 exactly 0 (|S - L| is far below 1e29), so
+        // it needs no compare of its own, and interior tiles with a mask take
+        // the same path without the visibility test.
         auto ew_exp = [&](int r) {
           float x = se[r];
-          if constexpr (!FULL) {
-            bool ok = elem_visible(r, lb, span);
-            if constexpr (MASK) {
-              const float mv = mk[r];
-              ok = ok && !(mv <= kMaskedSentinel);
-              x = __builtin_fmaf(mv, kLog2e, x);
-            }
-            x = ok ? x : -__builtin_inff();
-          }
+          if constexpr (MASK) x = __builtin_fmaf(mk[r], kLog2e, x);
+          if constexpr (!FULL) x = elem_visible(r, lb, span) ? x : -__builtin_inff();
           pr[r] = __builtin_amdgcn_exp2f(x);
         };
         // P and dS of element r, one slot after its exp; odd r packs the pair.
         auto ew_ds = [&](int r) {
           if constexpr (DROP) {
-            const float mm = fmix32(pre.rk[r >> 2][r & 3] ^ jg) >= a.drop_thr ? a.drop_inv : 0.f;
+            const float mm = fmix32_tail(pre.rk[r >> 2][r & 3] ^ jg) >= a.drop_thr ? a.drop_inv : 0.f;
             pv[r] = pr[r] * mm;
             dv[r] = pr[r] * (dpe[r] * mm - pre.dl[r >> 2][r & 3]);
           } else {
@@ -470,7 +468,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         // Mask values of the half, read from this wave's LDS staging MF slots ahead
         // of their use, each once its copy (issued two sections earlier) landed.
         auto mask_rd = [&](int kk) {
-          if constexpr (MASK && !FULL) {
+          if constexpr (MASK) {
             if (kk < NSD) {
               // (WS: the two dS stores of the dV/dK section in between count too)
               wait_vmcnt<(MVEC ? kMaskWaitV : kMaskWait) + (WS ? 2 : 0)>();
@@ -730,13 +728,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       // each for every query head of the group.  Boundary tiles include tiles
       // this wave cannot see at all; the predicate zeroes them.
       auto all = [&](int t) { return rect_all_visible(a, qb + t * BQ, qb + t * BQ + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1); };
-      int f0 = ntq, f1 = ntq;
-      if constexpr (!MASK) {
-        f0 = 0;
-        while (f0 < ntq && !all(f0)) ++f0;
-        f1 = f0;
-        while (f1 < ntq && all(f1)) ++f1;
-      }
+      int f0 = 0;
+      while (f0 < ntq && !all(f0)) ++f0;
+      int f1 = f0;
+      while (f1 < ntq && all(f1)) ++f1;
       int t = ntq - 1;
       for (; t >= f1; --t)
         for (int g = 0; g < a.group; ++g) step(kEdge, g, t);
