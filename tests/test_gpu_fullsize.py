@@ -1,5 +1,6 @@
 """Full-size parity of the bf16 prefill workloads, in the launch configuration
-bench.py times, on outputs the oracle can compute one by one.
+bench.py times (dS shared through the workspace) and with dS recomputed, on
+outputs the oracle can compute one by one.
 
 All heads get seeded N(0,1) Q, K, V.  A few "checked" query heads get a real
 dO and O, L from the fp64 oracle forward; every other head gets dO = 0 and
@@ -38,31 +39,38 @@ def _run_checked(w, checked, rows, keys):
             lse[b, h, r] = lb
         say(f"  oracle forward done for head {(b, h)}")
     o = round_out(o, w.dtype)
-    mask_dev = torch.from_numpy(inp["mask"]).cuda() if inp["mask"] is not None else None
-    q, k, v = (dev(inp[n], w.layout, w.dtype) for n in ("q", "k", "v"))
-    dq, dk, dv, _ = api.backward(q, k, v, dev(o, w.layout, w.dtype), dev(do, w.layout, w.dtype),
-                                 torch.from_numpy(lse).cuda(), scale=w.scale, causal=w.causal,
-                                 causal_offset=w.causal_offset, window=w.window, dropout_p=w.dropout_p,
-                                 seed=w.dropout_seed, mask=mask_dev)
-    torch.cuda.synchronize()
-    gdq, gdk, gdv = logical(dq), logical(dk), logical(dv)
-    say("  gpu backward done")
     checked_q = set(checked)
     checked_kv = {(b, h // g) for (b, h) in checked}
-    for b in range(B):
-        for h in range(Hq):
-            if (b, h) not in checked_q:
-                assert np.all(gdq[b, h] == 0.0), (b, h)
-        for kvh in range(w.num_kv_heads):
-            if (b, kvh) not in checked_kv:
-                assert np.all(gdk[b, kvh] == 0.0) and np.all(gdv[b, kvh] == 0.0), (b, kvh)
-    for (b, h) in checked:
-        ref = oracle.backward_dq_rows(inp["q"], inp["k"], inp["v"], o, do, lse, spec, inp["mask"], b, h, rows)
-        assert_close(gdq[b, h, rows], ref, w.dtype, f"dq rows (b={b}, h={h})")
-    for (b, kvh) in sorted(checked_kv):
-        rk, rv = oracle.backward_dkdv_keys(inp["q"], inp["k"], inp["v"], o, do, lse, spec, inp["mask"], b, kvh, keys)
-        assert_close(gdk[b, kvh, keys], rk, w.dtype, f"dk keys (b={b}, kvh={kvh})")
-        assert_close(gdv[b, kvh, keys], rv, w.dtype, f"dv keys (b={b}, kvh={kvh})")
+    ref_dq = {bh: oracle.backward_dq_rows(inp["q"], inp["k"], inp["v"], o, do, lse, spec, inp["mask"], *bh, rows)
+              for bh in checked}
+    ref_dkdv = {bk: oracle.backward_dkdv_keys(inp["q"], inp["k"], inp["v"], o, do, lse, spec, inp["mask"], *bk, keys)
+                for bk in sorted(checked_kv)}
+    say("  oracle references done")
+    mask_dev = torch.from_numpy(inp["mask"]).cuda() if inp["mask"] is not None else None
+    q, k, v = (dev(inp[n], w.layout, w.dtype) for n in ("q", "k", "v"))
+    # both bf16 paths: dS shared through the workspace (what bench.py times) and recomputed
+    for share in (True, False):
+        dq, dk, dv, _ = api.backward(q, k, v, dev(o, w.layout, w.dtype), dev(do, w.layout, w.dtype),
+                                     torch.from_numpy(lse).cuda(), scale=w.scale, causal=w.causal,
+                                     causal_offset=w.causal_offset, window=w.window, dropout_p=w.dropout_p,
+                                     seed=w.dropout_seed, mask=mask_dev, share_ds=share)
+        torch.cuda.synchronize()
+        gdq, gdk, gdv = logical(dq), logical(dk), logical(dv)
+        del dq, dk, dv
+        torch.cuda.empty_cache()
+        say(f"  gpu backward done (shared dS: {share})")
+        for b in range(B):
+            for h in range(Hq):
+                if (b, h) not in checked_q:
+                    assert np.all(gdq[b, h] == 0.0), (b, h)
+            for kvh in range(w.num_kv_heads):
+                if (b, kvh) not in checked_kv:
+                    assert np.all(gdk[b, kvh] == 0.0) and np.all(gdv[b, kvh] == 0.0), (b, kvh)
+        for (b, h), ref in ref_dq.items():
+            assert_close(gdq[b, h, rows], ref, w.dtype, f"dq rows (b={b}, h={h})")
+        for (b, kvh), (rk, rv) in ref_dkdv.items():
+            assert_close(gdk[b, kvh, keys], rk, w.dtype, f"dk keys (b={b}, kvh={kvh})")
+            assert_close(gdv[b, kvh, keys], rv, w.dtype, f"dv keys (b={b}, kvh={kvh})")
 
 
 def test_extras_workload_full_size():
