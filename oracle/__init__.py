@@ -43,4 +43,5 @@ from .attention import (  # noqa: F401
     backward_dkdv_keys,
     decode_probs,
     decode_backward,
+    decode_dkdv,
 )

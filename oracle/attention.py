@@ -332,3 +332,23 @@ def decode_backward(k_hist, v_hist, probs, d_out, heads_per_kv: int):
             d_scores[n, h] = ds
             d_q[n, h] = ds @ k_hist[n, :, kv, :].astype(np.float64)
     return d_scores, d_q
+
+
+def decode_dkdv(q, probs, d_scores, d_out, heads_per_kv: int):
+    """Decode-step backward, pass 2 (named after pass 1 on the rullama page;
+    its code is not shown there): the history gradients, summed over the
+    query heads sharing a KV head.  With scores s_hj = q_h . K_j (unscaled) and
+    out_h = sum_j probs_hj V_j:
+      dK_j = sum_h d_scores_hj q_h,   dV_j = sum_h probs_hj d_out_h.
+    Returns dk_hist, dv_hist [N, L, Hkv, D], fp64."""
+    N, H, L = probs.shape
+    D = q.shape[2]
+    Hkv = H // heads_per_kv
+    dk = np.zeros((N, L, Hkv, D), dtype=np.float64)
+    dv = np.zeros((N, L, Hkv, D), dtype=np.float64)
+    for n in range(N):
+        for h in range(H):
+            kv = h // heads_per_kv
+            dk[n, :, kv, :] += np.outer(d_scores[n, h].astype(np.float64), q[n, h].astype(np.float64))
+            dv[n, :, kv, :] += np.outer(probs[n, h].astype(np.float64), d_out[n, h].astype(np.float64))
+    return dk, dv
