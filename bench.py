@@ -370,6 +370,21 @@ def bench_decode(args):
     ms = start.elapsed_time(stop) / args.steps
     nbytes = 4 * (2 * N * L * Hkv * D + 2 * N * H * L + 2 * N * H * D)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    # pass 2 (history dK, dV from pass 1's d_scores), timed on its own after pass 1
+    dk_hist = torch.empty_like(k_hist)
+    dv_hist = torch.empty_like(v_hist)
+    for _ in range(args.warmup):
+        api.decode_dkdv(q, d_out, probs, d_scores, Hkv, dk_hist, dv_hist)
+    torch.cuda.synchronize()
+    s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s2.record()
+    for _ in range(args.steps):
+        api.decode_dkdv(q, d_out, probs, d_scores, Hkv, dk_hist, dv_hist)
+    e2.record()
+    torch.cuda.synchronize()
+    ms2 = s2.elapsed_time(e2) / args.steps
+    nbytes2 = 4 * (2 * N * L * Hkv * D + 2 * N * H * L + 2 * N * H * D)
+    gbs2 = nbytes2 / (ms2 * 1e-3) / 1e9
     return {
         "metric": "decode-step attention-backward HBM GB/s, 1 GPU",
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -380,6 +395,10 @@ def bench_decode(args):
         "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                      "per_unit": "bytes of K,V rows + probs/d_scores + d_out/d_q", "units": nbytes},
+        "pass2": {"kernel": "decode_kv_kernel", "what": "history dK, dV (fa_bwd_decode_dkdv)", "bound": "hbm",
+                  "ms": round(ms2, 4), "achieved": round(gbs2, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                  "frac": round(gbs2 / PEAK_HBM_GBS, 4),
+                  "per_unit": "dK,dV rows written + probs/d_scores + q/d_out read", "units": nbytes2},
     }
 
 

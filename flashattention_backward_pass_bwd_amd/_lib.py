@@ -34,6 +34,7 @@ EXPORTED = (
     "fa_bwd_dkdv_ds",
     "fa_bwd_dq_ds",
     "fa_bwd_decode",
+    "fa_bwd_decode_dkdv",
     "fa_bwd_decode_max_history",
     "fa_bwd_status_string",
     "fa_bwd_debug_visibility",
@@ -115,6 +116,7 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_dkdv_ds.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, u64, vp]
     L.fa_bwd_dq_ds.argtypes = [P, vp, vp, u64, vp, vp]
     L.fa_bwd_decode.argtypes = [DP, vp, vp, vp, vp, vp, vp, vp]
+    L.fa_bwd_decode_dkdv.argtypes = [DP, vp, vp, vp, vp, vp, vp, vp]
     L.fa_bwd_decode_max_history.argtypes = [DP]
     L.fa_bwd_decode_max_history.restype = ctypes.c_int32
     L.fa_bwd_status_string.argtypes = [ctypes.c_int]
@@ -123,7 +125,7 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_debug_dropout_keep.argtypes = [P, vp, vp]
     L.fa_bwd_calib_mfma_bf16.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, vp]
     for name in ("fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_ds_workspace_size",
-                 "fa_bwd_dkdv_ds", "fa_bwd_dq_ds", "fa_bwd_decode",
+                 "fa_bwd_dkdv_ds", "fa_bwd_dq_ds", "fa_bwd_decode", "fa_bwd_decode_dkdv",
                  "fa_bwd_debug_visibility", "fa_bwd_debug_dropout_keep", "fa_bwd_calib_mfma_bf16"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L

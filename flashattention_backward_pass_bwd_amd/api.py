@@ -188,6 +188,23 @@ def decode_backward(k_hist, v_hist, probs, d_out, d_scores=None, d_q=None):
     return d_scores, d_q
 
 
+def decode_dkdv(q, d_out, probs, d_scores, n_kv_heads: int, dk_hist=None, dv_hist=None):
+    """Decode-step backward pass 2: history dK, dV [N, len, Hkv, D] from q, d_out
+    [N, H, D] and probs, d_scores [N, H, len]; fp32 contiguous tensors."""
+    for t in (q, d_out, probs, d_scores):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("decode tensors must be contiguous float32")
+    N, H, D = q.shape
+    L = probs.shape[2]
+    p = _lib.FaDecodeParams(num_seqs=N, n_heads=H, n_kv_heads=n_kv_heads, head_dim=D, history_len=L)
+    shape = (N, L, n_kv_heads, D)
+    dk_hist = torch.empty(shape, dtype=torch.float32, device=q.device) if dk_hist is None else dk_hist
+    dv_hist = torch.empty(shape, dtype=torch.float32, device=q.device) if dv_hist is None else dv_hist
+    _lib.check("fa_bwd_decode_dkdv", _lib.lib().fa_bwd_decode_dkdv(
+        ctypes.byref(p), _vp(q), _vp(d_out), _vp(probs), _vp(d_scores), _vp(dk_hist), _vp(dv_hist), _stream()))
+    return dk_hist, dv_hist
+
+
 def debug_visibility(p: _lib.FaBwdParams, device) -> torch.Tensor:
     out = torch.empty((p.batch, p.num_heads, p.seq_q, p.seq_k), dtype=torch.uint8, device=device)
     _lib.check("fa_bwd_debug_visibility", _lib.lib().fa_bwd_debug_visibility(ctypes.byref(p), _vp(out), _stream()))

@@ -223,6 +223,26 @@ fa_status fa_bwd_decode(const fa_decode_params* p, const float* k_hist, const fl
   return hip_status(fa::launch_decode(a, k_hist, v_hist, probs, d_out, d_scores, d_q, as_stream(stream)));
 }
 
+fa_status fa_bwd_decode_dkdv(const fa_decode_params* p, const float* q, const float* d_out, const float* probs,
+                             const float* d_scores, float* dk_hist, float* dv_hist, fa_stream_t stream) {
+  if (p == nullptr || q == nullptr || d_out == nullptr || probs == nullptr || d_scores == nullptr ||
+      dk_hist == nullptr || dv_hist == nullptr)
+    return FA_ERR_NULL;
+  if (p->num_seqs <= 0 || p->n_heads <= 0 || p->n_kv_heads <= 0 || p->head_dim <= 0 || p->history_len <= 0)
+    return FA_ERR_SHAPE;
+  if (p->n_heads % p->n_kv_heads != 0) return FA_ERR_SHAPE;
+  const int g = p->n_heads / p->n_kv_heads;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return FA_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) return FA_ERR_UNSUPPORTED;
+  const int64_t nblk = (p->history_len + fa::decode_kv_rows_per_block() - 1) / fa::decode_kv_rows_per_block();
+  if ((int64_t)p->num_seqs * p->n_kv_heads * nblk >= (int64_t(1) << 31)) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(d_out) || !aligned16(dk_hist) || !aligned16(dv_hist) ||
+      (reinterpret_cast<uintptr_t>(probs) & 3u) || (reinterpret_cast<uintptr_t>(d_scores) & 3u))
+    return FA_ERR_ALIGN;
+  fa::DecodeArgs a{p->num_seqs, p->n_heads, p->n_kv_heads, p->head_dim, p->history_len, g};
+  return hip_status(fa::launch_decode_kv(a, q, d_out, probs, d_scores, dk_hist, dv_hist, as_stream(stream)));
+}
+
 const char* fa_bwd_status_string(fa_status s) {
   switch (s) {
     case FA_OK: return "FA_OK";

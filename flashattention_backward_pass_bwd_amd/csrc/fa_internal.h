@@ -54,6 +54,9 @@ hipError_t launch_decode(const DecodeArgs& a, const float* k_hist, const float* 
                          const float* probs, const float* d_out, float* d_scores, float* d_q,
                          hipStream_t st);
 int decode_max_history(int g);
+hipError_t launch_decode_kv(const DecodeArgs& a, const float* q, const float* dout, const float* probs,
+                            const float* dscores, float* dk, float* dv, hipStream_t st);
+int decode_kv_rows_per_block();
 hipError_t launch_debug_visibility(const PrefillArgs& a, uint8_t* out, hipStream_t st);
 hipError_t launch_debug_dropout(const PrefillArgs& a, uint8_t* out, hipStream_t st);
 hipError_t launch_calib_mfma(const void* ops, float* sink, int blocks, int iters, hipStream_t st);

@@ -192,6 +192,25 @@ fa_status fa_bwd_decode(const fa_decode_params* p, const float* k_hist, const fl
                         const float* probs, const float* d_out, float* d_scores, float* d_q,
                         fa_stream_t stream);
 
+/*
+ * Decode-step backward, pass 2 ([wgsl-dec] header: the pass after the one
+ * producing d_scores, named there, its code not on the page): the history
+ * gradients, summed over the query heads h of each KV head kv = h / heads_per_kv,
+ *   dk_hist[n, j, kv] = sum_h d_scores[n, h, j] q[n, h],
+ *   dv_hist[n, j, kv] = sum_h probs[n, h, j] d_out[n, h]
+ * (scores are the unscaled q . K_j of fa_bwd_decode).  fp32, contiguous:
+ * q, d_out [num_seqs, n_heads, head_dim]; probs, d_scores [num_seqs, n_heads,
+ * history_len] (d_scores as fa_bwd_decode writes it); dk_hist, dv_hist
+ * [num_seqs, history_len, n_kv_heads, head_dim], every element written.
+ * head_dim in {64, 128, 256}; n_heads / n_kv_heads in {1, 2, 4, 8}; no limit on
+ * history_len beyond 32-bit grid sizes.  Errors: FA_ERR_NULL, FA_ERR_SHAPE,
+ * FA_ERR_UNSUPPORTED, FA_ERR_ALIGN (q, d_out, dk_hist, dv_hist not 16-byte
+ * aligned; probs or d_scores not 4-byte aligned), FA_ERR_HIP.
+ */
+fa_status fa_bwd_decode_dkdv(const fa_decode_params* p, const float* q, const float* d_out,
+                             const float* probs, const float* d_scores, float* dk_hist,
+                             float* dv_hist, fa_stream_t stream);
+
 /* Longest history fa_bwd_decode accepts for p's head grouping (0 if the grouping is unsupported). */
 int32_t fa_bwd_decode_max_history(const fa_decode_params* p);
 

@@ -226,6 +226,26 @@ def test_ds_workspace_counts_visible_tiles(geom):
     assert _ws_bytes(L, p) == p.batch * p.num_heads * tiles * 16384
 
 
+def test_invalid_decode_pass2_arguments():
+    L = _lib.lib()
+    def dp(**kw):
+        p = _lib.FaDecodeParams(num_seqs=2, n_heads=8, n_kv_heads=2, head_dim=128, history_len=100)
+        for k, v in kw.items():
+            setattr(p, k, v)
+        return ctypes.byref(p)
+    f = L.fa_bwd_decode_dkdv
+    odd = ctypes.c_void_p(4096 + 8)
+    assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_NULL
+    assert f(dp(), FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.FA_ERR_NULL
+    assert f(dp(history_len=0), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_SHAPE
+    assert f(dp(n_kv_heads=3), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_SHAPE
+    assert f(dp(n_heads=24, n_kv_heads=2), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_UNSUPPORTED
+    assert f(dp(head_dim=96), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_UNSUPPORTED
+    assert f(dp(), odd, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_ALIGN
+    assert f(dp(), FAKE, FAKE, FAKE, FAKE, FAKE, odd, None) == _lib.FA_ERR_ALIGN
+    assert f(dp(), FAKE, FAKE, ctypes.c_void_p(4096 + 2), FAKE, FAKE, FAKE, None) == _lib.FA_ERR_ALIGN
+
+
 def test_invalid_calibration_arguments():
     L = _lib.lib()
     f = L.fa_bwd_calib_mfma_bf16

@@ -3,6 +3,9 @@
 Covers the workload's own shapes (32 heads over 8 KV heads, head_dim 256,
 history 4096) at a few sequences, other head dims / groupings / ragged
 history lengths, and the full 64-sequence workload (every output compared).
+Pass 2 (history dK, dV from the GPU's d_scores) is compared with the oracle's
+pass 2 on the oracle's d_scores: every output on the small cases, three
+sequences of the full workload.
 """
 import numpy as np
 import pytest
@@ -25,7 +28,20 @@ def _run(w, seqs=None):
     d_scores, d_q = api.decode_backward(t["k_hist"], t["v_hist"], pd, t["d_out"])
     torch.cuda.synchronize()
     ref_s, ref_q = oracle.decode_backward(inp["k_hist"], inp["v_hist"], probs, inp["d_out"], g)
-    return d_scores.cpu().numpy(), d_q.cpu().numpy(), ref_s, ref_q
+    dk, dv = api.decode_dkdv(t["q"], t["d_out"], pd, d_scores, w.n_kv_heads)
+    torch.cuda.synchronize()
+    return d_scores.cpu().numpy(), d_q.cpu().numpy(), ref_s, ref_q, (dk, dv, inp, probs)
+
+
+def _check_pass2(res, g, seqs):
+    dk, dv, inp, probs = res
+    sl = slice(None) if seqs is None else list(seqs)
+    ref_s, _ = oracle.decode_backward(inp["k_hist"][sl], inp["v_hist"][sl], probs[sl], inp["d_out"][sl], g)
+    rk, rv = oracle.decode_dkdv(inp["q"][sl], probs[sl], ref_s, inp["d_out"][sl], g)
+    gk = dk.cpu().numpy()[sl] if seqs is None else dk[list(seqs)].cpu().numpy()
+    gv = dv.cpu().numpy()[sl] if seqs is None else dv[list(seqs)].cpu().numpy()
+    assert_close(gk, rk, "f32", "dk_hist")
+    assert_close(gv, rv, "f32", "dv_hist")
 
 
 CASES = {
@@ -44,16 +60,18 @@ CASES = {
 def test_decode_parity(name):
     w = CASES[name]
     say(f"[decode] {name}: {w}")
-    ds, dq, ref_s, ref_q = _run(w)
+    ds, dq, ref_s, ref_q, res = _run(w)
     assert_close(ds, ref_s, "f32", "d_scores")
     assert_close(dq, ref_q, "f32", "d_q")
     # probs sum to one, so each head's score gradients sum to zero
     assert np.abs(ds.sum(-1)).max() < 1e-5 * max(1.0, np.abs(ds).max() * w.history_len)
+    _check_pass2(res, w.n_heads // w.n_kv_heads, None)
 
 
 def test_decode_full_workload():
     w = synth.DECODE_F32
     say(f"[decode] full workload {w.name}")
-    ds, dq, ref_s, ref_q = _run(w)
+    ds, dq, ref_s, ref_q, res = _run(w)
     assert_close(ds, ref_s, "f32", "d_scores")
     assert_close(dq, ref_q, "f32", "d_q")
+    _check_pass2(res, w.n_heads // w.n_kv_heads, [0, 17, w.num_seqs - 1])
