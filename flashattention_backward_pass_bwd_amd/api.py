@@ -81,6 +81,17 @@ def _like(t: torch.Tensor) -> torch.Tensor:
     return torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
 
 
+def forward(p: _lib.FaBwdParams, q, k, v, o=None, lse=None):
+    """Forward pass (bf16): O (q's shape and layout) and L fp32 [B, Hq, Sq]."""
+    _same_layout(k, v)
+    o = _like(q) if o is None else o
+    _same_layout(q, o)
+    if lse is None:
+        lse = torch.empty((p.batch, p.num_heads, p.seq_q), dtype=torch.float32, device=q.device)
+    _lib.check("fa_fwd", _lib.lib().fa_fwd(ctypes.byref(p), _vp(q), _vp(k), _vp(v), _vp(o), _vp(lse), _stream()))
+    return o, lse
+
+
 def preprocess(p: _lib.FaBwdParams, o: torch.Tensor, do: torch.Tensor, delta: torch.Tensor | None = None):
     _same_layout(o, do)
     if delta is None:

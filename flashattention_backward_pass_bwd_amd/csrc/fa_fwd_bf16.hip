@@ -1,0 +1,205 @@
+// Forward pass producing O and L with the backward's conventions, bf16 storage,
+// bf16 MFMA with fp32 accumulation (ferrotensor-backend
+// flash_attention_v2_backward.wgsl: the forward whose O and L the backward
+// takes -- its file is referenced there, not shown -- and the online
+// log-sum-exp of its dQ pass's first sweep; rustytorch
+// flash_attention_backward_dq.metal takes L as an input):
+//   S_ij = scale * Q_i.K_j + mask_ij on visible, unmasked elements,
+//   L_i = log sum_j exp(S_ij)  (natural log; +inf when no element counts),
+//   O_i = sum_j exp(S_ij - L_i) M_ij V_j   (M the dropout multiplier).
+//
+// Block: 4 waves own 128 consecutive query rows of one (b, h); wave w keeps its
+// 32 rows of Q as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so
+// every lane column is one query row: the row's running maximum and sum are
+// per-lane values (the two half-waves, which hold different keys of the same
+// rows, agree on the maximum through v_permlane32_swap and add their sums at
+// the end).  Per 64-key tile: K and V rows go into LDS (swizzled, see
+// fa_tiles.h); per 32-key half, S^T (A operand: K rows), the exponent in fp32
+// (scale applied to the fp32 product, so L keeps fp32 accuracy), the online
+// rescale of O^T, and O^T += V^T (P.M)^T with V^T through ds_read_b64_tr_b16
+// and (P.M)^T straight from the C registers of S^T.  The MFMAs are compiler
+// builtins, so the compiler keeps their wait states; two blocks share a CU.
+#include "fa_internal.h"
+#include "fa_tiles.h"
+
+namespace fa {
+
+constexpr int kFwdRowsPerBlock = 128;
+
+// Maximum of x over lanes l and l ^ 32 (the two half-waves).
+__device__ __forceinline__ float halves_max(float x) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
+
+template <int D, bool MASK, bool DROP>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const __bf16* __restrict__ Q,
+                                                          const __bf16* __restrict__ K,
+                                                          const __bf16* __restrict__ V, __bf16* __restrict__ O,
+                                                          float* __restrict__ Lout) {
+  constexpr int BK = 64;
+  constexpr int NCH = D / 8;  // 16-byte chunks per row
+  constexpr int KS = D / 16;  // k-blocks of the head_dim contraction
+  constexpr int DB = D / 32;  // 32-row blocks of O^T
+  __shared__ __attribute__((aligned(16))) __bf16 sK[BK * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[BK * D];
+
+  const int nqb = (a.Sq + kFwdRowsPerBlock - 1) / kFwdRowsPerBlock;
+  const int qbi = blockIdx.x % nqb;
+  const int bh = blockIdx.x / nqb;
+  const int h = bh % a.Hq;
+  const int b = bh / a.Hq;
+  const int kvh = h / a.group;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int h2 = lane >> 5;
+  const int l32 = lane & 31;
+  const int q0 = qbi * kFwdRowsPerBlock;
+  const int i = q0 + 32 * wave + l32;  // this lane's query row
+  const int ic = min(i, a.Sq - 1);
+
+  // Q row i as the B operand: k-block ks holds d = 16ks + 8*h2 .. +7.
+  bf16x8 qr[KS];
+  const __bf16* qrow = Q + (int64_t)b * a.qsb + (int64_t)ic * a.qss + (int64_t)h * a.qsh;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) qr[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * h2);
+
+  int kb, ke;
+  key_range(a, q0, min(q0 + kFwdRowsPerBlock, a.Sq) - 1, kb, ke);
+  const DiagBounds vb = diag_bounds(a);
+  const uint32_t rkey = DROP ? drop_row_key(a, b, h, ic) : 0u;
+  const float* mrow = MASK ? a.mask + (int64_t)b * a.msb + (int64_t)h * a.msh + (int64_t)ic * a.msq : nullptr;
+
+  int tr_lo[DB], tr_hi[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) {
+    tr_lo[d] = tr_lane_off<D>(lane, d, 0);
+    tr_hi[d] = tr_lane_off<D>(lane, d, 8);
+  }
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int d = 0; d < DB; ++d) acc[d] = f32x16{};
+  float m = -__builtin_inff();  // running maximum of the exponent (log2 units), shared by both half-waves
+  float l = 0.f;                // this lane's part of the running sum
+  const __bf16* kbase = K + (int64_t)b * a.ksb + (int64_t)kvh * a.ksh;
+  const __bf16* vbase = V + (int64_t)b * a.ksb + (int64_t)kvh * a.ksh;
+
+  for (int kt = kb; kt < ke; kt += BK) {
+    __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+    for (int u = 0; u < BK * NCH / 256; ++u) {
+      const int c = tid + 256 * u, r = c / NCH, ch = c % NCH;
+      const int64_t off = (int64_t)min(kt + r, a.Sk - 1) * a.kss + 8 * ch;  // rows past the end repeat the last
+      *reinterpret_cast<bf16x8*>(&sK[tile_off<D>(r, ch)]) = *reinterpret_cast<const bf16x8*>(kbase + off);
+      *reinterpret_cast<bf16x8*>(&sV[tile_off<D>(r, ch)]) = *reinterpret_cast<const bf16x8*>(vbase + off);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // S^T: row 32*half + l32 of the tile is the A operand's key.
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kr = lds_read_b128(&sK[tile_off<D>(32 * half + l32, 2 * ks + h2)]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qr[ks], s, 0, 0, 0);
+      }
+      // Element r: key j = kt + 32*half + 8*(r/4) + 4*h2 + r%4 of row i.
+      float x[16];
+      float tmax = -__builtin_inff();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = kt + 32 * half + 8 * (r >> 2) + 4 * h2 + (r & 3);
+        const int dd = j - i;
+        bool ok = i < a.Sq && j < a.Sk && dd > vb.dlo && dd < vb.dhi;
+        float v = s[r] * a.scale_log2;
+        if constexpr (MASK) {
+          const float mv = ok ? mrow[(int64_t)j * a.msk] : 0.f;
+          ok = ok && !(mv <= kMaskedSentinel);
+          v = __builtin_fmaf(mv, kLog2e, v);
+        }
+        x[r] = ok ? v : -__builtin_inff();
+        tmax = fmaxf(tmax, x[r]);
+      }
+      const float mnew = fmaxf(m, halves_max(tmax));
+      const float mref = mnew == -__builtin_inff() ? 0.f : mnew;  // nothing counted yet: every term is 0
+      const float alpha = __builtin_amdgcn_exp2f(m - mref);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+      bf16x8 pm[2];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float p0 = __builtin_amdgcn_exp2f(x[r] - mref), p1 = __builtin_amdgcn_exp2f(x[r + 1] - mref);
+        l += p0 + p1;
+        if constexpr (DROP) {
+          const int j = kt + 32 * half + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          p0 = drop_keep(rkey, j, a.drop_thr) ? p0 * a.drop_inv : 0.f;
+          p1 = drop_keep(rkey, j + 1, a.drop_thr) ? p1 * a.drop_inv : 0.f;
+        }
+        pm[r >> 3][r & 7] = (__bf16)p0;
+        pm[r >> 3][(r & 7) + 1] = (__bf16)p1;
+      }
+      // O^T += V^T (P.M)^T: k-step t covers keys 32*half + 16t .. +15.
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          const __bf16* base = &sV[(32 * half + 16 * t) * D];
+          const bf16x8 vt = concat(lds_read_tr(base + tr_lo[d]), lds_read_tr(base + tr_hi[d]));
+          acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pm[t], acc[d], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  const float lsum = halves_sum(l);
+  if (i < a.Sq) {
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    __bf16* orow = O + (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[d][4 * r4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * r4 + 4 * h2) = o4;
+      }
+    }
+    if (h2 == 0)
+      Lout[((int64_t)b * a.Hq + h) * a.Sq + i] =
+          lsum > 0.f ? (m + __builtin_log2f(lsum)) * 0.6931471805599453f : __builtin_inff();
+  }
+}
+
+template <int D, bool MASK, bool DROP>
+static hipError_t launch_t(const PrefillArgs& a, const void* Q, const void* K, const void* V, void* O, float* L,
+                           hipStream_t st) {
+  const int nqb = (a.Sq + kFwdRowsPerBlock - 1) / kFwdRowsPerBlock;
+  const unsigned grid = (unsigned)((int64_t)nqb * a.B * a.Hq);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, DROP>), dim3(grid), dim3(256), 0, st, a,
+                     static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
+                     static_cast<__bf16*>(O), L);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, const void* V, void* O, float* L,
+                           hipStream_t st) {
+  const bool mk = a.mask != nullptr, dr = a.drop != 0;
+  if (mk) return dr ? launch_t<D, true, true>(a, Q, K, V, O, L, st) : launch_t<D, true, false>(a, Q, K, V, O, L, st);
+  return dr ? launch_t<D, false, true>(a, Q, K, V, O, L, st) : launch_t<D, false, false>(a, Q, K, V, O, L, st);
+}
+
+hipError_t launch_fwd_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V, void* O,
+                           float* L, hipStream_t st) {
+  return D == 64 ? launch_d<64>(a, Q, K, V, O, L, st) : launch_d<128>(a, Q, K, V, O, L, st);
+}
+
+}  // namespace fa

@@ -113,6 +113,21 @@ typedef struct fa_bwd_params {
 } fa_bwd_params;
 
 /*
+ * Forward pass with the same conventions, bf16 only: the O and L the backward
+ * takes ([wgsl-fa2] header: the forward whose outputs the two passes read,
+ * its online log-sum-exp sweep; [metal-dq] L as an input).  With S_ij =
+ * scale * Q_i.K_j + mask_ij on counted (visible, unmasked) elements:
+ *   L_i = ln sum_j exp(S_ij)  (+inf when no element of row i counts),
+ *   O_i = sum_j exp(S_ij - L_i) M_ij V_j  (M the dropout multiplier; 0 rows
+ *   when nothing counts).
+ * Q, K, V, O as in fa_bwd_params (O shares Q's strides); L fp32, contiguous
+ * [batch, num_heads, seq_q].  Errors as fa_bwd_dq, plus FA_ERR_UNSUPPORTED
+ * for fp32.
+ */
+fa_status fa_fwd(const fa_bwd_params* p, const void* Q, const void* K, const void* V, void* O, float* L,
+                 fa_stream_t stream);
+
+/*
  * Delta_i = sum_d dO_id * O_id per (b, h, i), fp32 accumulation
  * ([metal-dq] D = rowsum(dO * O); [wgsl-fa2] pass-1 Delta).
  * O, dO: query-side tensors (dtype); delta: fp32 [batch, num_heads, seq_q].

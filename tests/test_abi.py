@@ -22,7 +22,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libfa
 
 def _declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:fa_status|int32_t|const char\*)\s+(fa_bwd_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:fa_status|int32_t|const char\*)\s+(fa_\w+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_binding_surface():
@@ -104,6 +104,7 @@ def test_invalid_prefill_arguments(field, value, code):
     setattr(p, field, value)
     P = ctypes.byref(p)
     assert L.fa_bwd_preprocess(P, FAKE, FAKE, FAKE, None) == code
+    assert L.fa_fwd(P, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
     assert L.fa_bwd_dkdv(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
     assert L.fa_bwd_dq(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
     assert L.fa_bwd_debug_visibility(P, FAKE, None) == code
@@ -224,6 +225,19 @@ def test_ds_workspace_counts_visible_tiles(geom):
     pad[:sq, :sk] = vis
     tiles = int(pad.reshape(nt, 64, nk, 128).any(axis=(1, 3)).sum())
     assert _ws_bytes(L, p) == p.batch * p.num_heads * tiles * 16384
+
+
+def test_invalid_forward_arguments():
+    L = _lib.lib()
+    p = _valid()
+    P = ctypes.byref(p)
+    odd = ctypes.c_void_p(4096 + 8)
+    assert L.fa_fwd(P, None, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_NULL
+    assert L.fa_fwd(P, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.FA_ERR_NULL
+    assert L.fa_fwd(P, FAKE, FAKE, FAKE, odd, FAKE, None) == _lib.FA_ERR_ALIGN
+    assert L.fa_fwd(P, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(4096 + 2), None) == _lib.FA_ERR_ALIGN
+    p.dtype = _lib.FA_DTYPE_F32
+    assert L.fa_fwd(P, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_UNSUPPORTED
 
 
 def test_invalid_decode_pass2_arguments():

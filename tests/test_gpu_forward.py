@@ -1,0 +1,81 @@
+"""GPU parity of the forward pass (O, L) against the fp64 oracle forward.
+
+O (bf16) to the bf16 bar (relative Frobenius error 2e-2).  L is fp32 computed
+from fp32 MFMA sums of exact bf16 products and the hardware exp2/log2, so it
+must agree to 1e-4 * max(1, |L|) on every finite row, and be +inf exactly on
+the rows where no element counts.  Every bf16 case of the backward parity
+tests, plus rows with every key masked.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from flashattention_backward_pass_bwd_amd import api, synth
+
+from fa_testlib import assert_close, dev, logical, say, spec_of
+from test_gpu_parity import CASES
+
+pytestmark = pytest.mark.gpu
+
+FWD_CASES = {n: w for n, w in CASES.items() if w.dtype == "bf16"}
+
+
+def _check(w, inp):
+    spec = spec_of(w)
+    ref_o, ref_l = oracle.forward(inp["q"], inp["k"], inp["v"], spec, inp["mask"])
+    q, k, v = (dev(inp[n], w.layout, w.dtype) for n in ("q", "k", "v"))
+    mask = torch.from_numpy(inp["mask"]).cuda() if inp["mask"] is not None else None
+    p = api.make_params(q, k, scale=w.scale, causal=w.causal, causal_offset=w.causal_offset, window=w.window,
+                        dropout_p=w.dropout_p, seed=w.dropout_seed, mask=mask)
+    o, lse = api.forward(p, q, k, v)
+    torch.cuda.synchronize()
+    got_l = lse.cpu().numpy().astype(np.float64)
+    inf = np.isinf(ref_l)
+    assert np.array_equal(np.isinf(got_l), inf) and np.all(got_l[inf] > 0), "rows with nothing counted"
+    err = np.abs(got_l[~inf] - ref_l[~inf]) / np.maximum(1.0, np.abs(ref_l[~inf]))
+    say(f"  L: max err {err.max() if err.size else 0.0:.2e} (tol 1e-4)")
+    assert err.size == 0 or err.max() <= 1e-4
+    assert_close(logical(o), ref_o, "bf16", "o")
+    return logical(o), got_l
+
+
+@pytest.mark.parametrize("name", sorted(FWD_CASES))
+def test_forward_parity(name):
+    w = FWD_CASES[name]
+    say(f"[forward] {name}: {w}")
+    _check(w, synth.prefill_inputs(w))
+
+
+def test_forward_fully_masked_rows():
+    w = synth.EXTRAS_BF16.resized(batch=2, num_heads=4, num_kv_heads=2, seq_q=96, seq_k=96, window=8,
+                                  mask_density=0.05, seed=41)
+    inp = synth.prefill_inputs(w)
+    inp["mask"][1, 0, 0, 0] = np.float32(-1e30)  # row 0 of batch 1 sees only key 0, now excluded
+    inp["mask"][0, 0, 5, :] = np.float32(-1e30)  # row 5 of batch 0: every key excluded
+    o, lse = _check(w, inp)
+    assert np.isinf(lse[1, :, 0]).all() and np.isinf(lse[0, :, 5]).all()
+    assert np.all(o[1, :, 0] == 0.0) and np.all(o[0, :, 5] == 0.0)
+
+
+@pytest.mark.parametrize("which", ["extras", "long"])
+def test_forward_full_size_sampled(which):
+    """The full-size bf16 workloads: sampled rows of a few heads against the oracle's rows."""
+    w = synth.EXTRAS_BF16 if which == "extras" else synth.LONG_BF16
+    inp = synth.prefill_inputs(w)
+    spec = spec_of(w)
+    q, k, v = (dev(inp[n], w.layout, w.dtype) for n in ("q", "k", "v"))
+    mask = torch.from_numpy(inp["mask"]).cuda() if inp["mask"] is not None else None
+    p = api.make_params(q, k, scale=w.scale, causal=w.causal, causal_offset=w.causal_offset, window=w.window,
+                        dropout_p=w.dropout_p, seed=w.dropout_seed, mask=mask)
+    o, lse = api.forward(p, q, k, v)
+    torch.cuda.synchronize()
+    go, gl = logical(o), lse.cpu().numpy().astype(np.float64)
+    S = w.seq_q
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, S // 2, S - 2, S - 1], rng.integers(0, S, 41)]))
+    for (b, h) in [(0, 0), (w.batch - 1, w.num_heads - 1), (w.batch // 2, w.num_heads // 2 + 1)]:
+        ro, rl = oracle.forward_rows(inp["q"], inp["k"], inp["v"], spec, inp["mask"], b, h, rows)
+        assert_close(go[b, h, rows], ro, "bf16", f"o rows (b={b}, h={h})")
+        err = np.abs(gl[b, h, rows] - rl) / np.maximum(1.0, np.abs(rl))
+        assert err.max() <= 1e-4, err.max()
