@@ -28,6 +28,7 @@ FA_DTYPE_BF16 = 1
 # Every function include/fa_bwd.h declares.
 EXPORTED = (
     "fa_fwd",
+    "fa_bwd_lse",
     "fa_bwd_preprocess",
     "fa_bwd_dkdv",
     "fa_bwd_dq",
@@ -110,6 +111,7 @@ def lib() -> ctypes.CDLL:
     DP = ctypes.POINTER(FaDecodeParams)
     vp = ctypes.c_void_p
     L.fa_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.fa_bwd_lse.argtypes = [P, vp, vp, vp, vp]
     L.fa_bwd_preprocess.argtypes = [P, vp, vp, vp, vp]
     L.fa_bwd_dkdv.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.fa_bwd_dq.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -126,7 +128,7 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_debug_visibility.argtypes = [P, vp, vp]
     L.fa_bwd_debug_dropout_keep.argtypes = [P, vp, vp]
     L.fa_bwd_calib_mfma_bf16.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, vp]
-    for name in ("fa_fwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_ds_workspace_size",
+    for name in ("fa_fwd", "fa_bwd_lse", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_ds_workspace_size",
                  "fa_bwd_dkdv_ds", "fa_bwd_dq_ds", "fa_bwd_decode", "fa_bwd_decode_dkdv",
                  "fa_bwd_debug_visibility", "fa_bwd_debug_dropout_keep", "fa_bwd_calib_mfma_bf16"):
         getattr(L, name).restype = ctypes.c_int

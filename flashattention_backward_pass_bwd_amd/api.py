@@ -92,6 +92,14 @@ def forward(p: _lib.FaBwdParams, q, k, v, o=None, lse=None):
     return o, lse
 
 
+def lse(p: _lib.FaBwdParams, q, k, out=None):
+    """L fp32 [B, Hq, Sq] alone (bf16), for a caller whose forward did not keep it."""
+    if out is None:
+        out = torch.empty((p.batch, p.num_heads, p.seq_q), dtype=torch.float32, device=q.device)
+    _lib.check("fa_bwd_lse", _lib.lib().fa_bwd_lse(ctypes.byref(p), _vp(q), _vp(k), _vp(out), _stream()))
+    return out
+
+
 def preprocess(p: _lib.FaBwdParams, o: torch.Tensor, do: torch.Tensor, delta: torch.Tensor | None = None):
     _same_layout(o, do)
     if delta is None:

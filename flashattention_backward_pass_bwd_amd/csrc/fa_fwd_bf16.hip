@@ -19,6 +19,8 @@
 // rescale of O^T, and O^T += V^T (P.M)^T with V^T through ds_read_b64_tr_b16
 // and (P.M)^T straight from the C registers of S^T.  The MFMAs are compiler
 // builtins, so the compiler keeps their wait states; two blocks share a CU.
+// With WO false the kernel computes L alone (no V, no O): the log-sum-exp
+// sweep for a caller whose forward did not keep L.
 #include "fa_internal.h"
 #include "fa_tiles.h"
 
@@ -33,7 +35,7 @@ __device__ __forceinline__ float halves_max(float x) {
   return fmaxf(a, b);
 }
 
-template <int D, bool MASK, bool DROP>
+template <int D, bool MASK, bool DROP, bool WO>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const __bf16* __restrict__ Q,
                                                           const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
@@ -94,7 +96,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
       const int c = tid + 256 * u, r = c / NCH, ch = c % NCH;
       const int64_t off = (int64_t)min(kt + r, a.Sk - 1) * a.kss + 8 * ch;  // rows past the end repeat the last
       *reinterpret_cast<bf16x8*>(&sK[tile_off<D>(r, ch)]) = *reinterpret_cast<const bf16x8*>(kbase + off);
-      *reinterpret_cast<bf16x8*>(&sV[tile_off<D>(r, ch)]) = *reinterpret_cast<const bf16x8*>(vbase + off);
+      if constexpr (WO)
+        *reinterpret_cast<bf16x8*>(&sV[tile_off<D>(r, ch)]) = *reinterpret_cast<const bf16x8*>(vbase + off);
     }
     __syncthreads();
 #pragma unroll
@@ -128,16 +131,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
       const float alpha = __builtin_amdgcn_exp2f(m - mref);
       m = mnew;
       l *= alpha;
+      if constexpr (WO) {
 #pragma unroll
-      for (int d = 0; d < DB; ++d)
+        for (int d = 0; d < DB; ++d)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+          for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+      }
       bf16x8 pm[2];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float p0 = __builtin_amdgcn_exp2f(x[r] - mref), p1 = __builtin_amdgcn_exp2f(x[r + 1] - mref);
         l += p0 + p1;
-        if constexpr (DROP) {
+        if constexpr (DROP && WO) {
           const int j = kt + 32 * half + 8 * (r >> 2) + 4 * h2 + (r & 3);
           p0 = drop_keep(rkey, j, a.drop_thr) ? p0 * a.drop_inv : 0.f;
           p1 = drop_keep(rkey, j + 1, a.drop_thr) ? p1 * a.drop_inv : 0.f;
@@ -147,7 +152,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
       }
       // O^T += V^T (P.M)^T: k-step t covers keys 32*half + 16t .. +15.
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < (WO ? 2 : 0); ++t) {
 #pragma unroll
         for (int d = 0; d < DB; ++d) {
           const __bf16* base = &sV[(32 * half + 16 * t) * D];
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     __bf16* orow = O + (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh;
 #pragma unroll
-    for (int d = 0; d < DB; ++d) {
+    for (int d = 0; d < (WO ? DB : 0); ++d) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         bf16x4 o4;
@@ -178,12 +183,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
   }
 }
 
-template <int D, bool MASK, bool DROP>
+template <int D, bool MASK, bool DROP, bool WO>
 static hipError_t launch_t(const PrefillArgs& a, const void* Q, const void* K, const void* V, void* O, float* L,
                            hipStream_t st) {
   const int nqb = (a.Sq + kFwdRowsPerBlock - 1) / kFwdRowsPerBlock;
   const unsigned grid = (unsigned)((int64_t)nqb * a.B * a.Hq);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, DROP>), dim3(grid), dim3(256), 0, st, a,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, DROP, WO>), dim3(grid), dim3(256), 0, st, a,
                      static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
                      static_cast<__bf16*>(O), L);
   return hipGetLastError();
@@ -193,10 +198,14 @@ template <int D>
 static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, const void* V, void* O, float* L,
                            hipStream_t st) {
   const bool mk = a.mask != nullptr, dr = a.drop != 0;
-  if (mk) return dr ? launch_t<D, true, true>(a, Q, K, V, O, L, st) : launch_t<D, true, false>(a, Q, K, V, O, L, st);
-  return dr ? launch_t<D, false, true>(a, Q, K, V, O, L, st) : launch_t<D, false, false>(a, Q, K, V, O, L, st);
+  if (O == nullptr)  // L alone: dropout does not enter it
+    return mk ? launch_t<D, true, false, false>(a, Q, K, V, O, L, st) : launch_t<D, false, false, false>(a, Q, K, V, O, L, st);
+  if (mk)
+    return dr ? launch_t<D, true, true, true>(a, Q, K, V, O, L, st) : launch_t<D, true, false, true>(a, Q, K, V, O, L, st);
+  return dr ? launch_t<D, false, true, true>(a, Q, K, V, O, L, st) : launch_t<D, false, false, true>(a, Q, K, V, O, L, st);
 }
 
+// O == nullptr: L alone (V is not read).
 hipError_t launch_fwd_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V, void* O,
                            float* L, hipStream_t st) {
   return D == 64 ? launch_d<64>(a, Q, K, V, O, L, st) : launch_d<128>(a, Q, K, V, O, L, st);

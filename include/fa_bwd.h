@@ -128,6 +128,14 @@ fa_status fa_fwd(const fa_bwd_params* p, const void* Q, const void* K, const voi
                  fa_stream_t stream);
 
 /*
+ * L alone, for a caller whose forward did not keep it ([wgsl-fa2] the dQ
+ * pass's first sweep: the online log-sum-exp of the scores): the L of fa_fwd
+ * (dropout does not enter it), without reading V or writing O.  bf16 only;
+ * errors as fa_fwd.
+ */
+fa_status fa_bwd_lse(const fa_bwd_params* p, const void* Q, const void* K, float* L, fa_stream_t stream);
+
+/*
  * Delta_i = sum_d dO_id * O_id per (b, h, i), fp32 accumulation
  * ([metal-dq] D = rowsum(dO * O); [wgsl-fa2] pass-1 Delta).
  * O, dO: query-side tensors (dtype); delta: fp32 [batch, num_heads, seq_q].

@@ -105,6 +105,7 @@ def test_invalid_prefill_arguments(field, value, code):
     P = ctypes.byref(p)
     assert L.fa_bwd_preprocess(P, FAKE, FAKE, FAKE, None) == code
     assert L.fa_fwd(P, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
+    assert L.fa_bwd_lse(P, FAKE, FAKE, FAKE, None) == code
     assert L.fa_bwd_dkdv(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
     assert L.fa_bwd_dq(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
     assert L.fa_bwd_debug_visibility(P, FAKE, None) == code
@@ -236,8 +237,11 @@ def test_invalid_forward_arguments():
     assert L.fa_fwd(P, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.FA_ERR_NULL
     assert L.fa_fwd(P, FAKE, FAKE, FAKE, odd, FAKE, None) == _lib.FA_ERR_ALIGN
     assert L.fa_fwd(P, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(4096 + 2), None) == _lib.FA_ERR_ALIGN
+    assert L.fa_bwd_lse(P, FAKE, None, FAKE, None) == _lib.FA_ERR_NULL
+    assert L.fa_bwd_lse(P, FAKE, odd, FAKE, None) == _lib.FA_ERR_ALIGN
     p.dtype = _lib.FA_DTYPE_F32
     assert L.fa_fwd(P, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_UNSUPPORTED
+    assert L.fa_bwd_lse(P, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_UNSUPPORTED
 
 
 def test_invalid_decode_pass2_arguments():

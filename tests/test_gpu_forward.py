@@ -4,7 +4,8 @@ O (bf16) to the bf16 bar (relative Frobenius error 2e-2).  L is fp32 computed
 from fp32 MFMA sums of exact bf16 products and the hardware exp2/log2, so it
 must agree to 1e-4 * max(1, |L|) on every finite row, and be +inf exactly on
 the rows where no element counts.  Every bf16 case of the backward parity
-tests, plus rows with every key masked.
+tests, plus rows with every key masked.  fa_bwd_lse (L alone) must give the
+forward's L.
 """
 import numpy as np
 import pytest
@@ -37,6 +38,8 @@ def _check(w, inp):
     say(f"  L: max err {err.max() if err.size else 0.0:.2e} (tol 1e-4)")
     assert err.size == 0 or err.max() <= 1e-4
     assert_close(logical(o), ref_o, "bf16", "o")
+    lonly = api.lse(p, q, k).cpu().numpy().astype(np.float64)  # the L-only sweep: the same values
+    assert np.array_equal(np.isinf(lonly), inf) and np.abs(lonly[~inf] - got_l[~inf]).max(initial=0.0) <= 1e-5 * max(1.0, np.abs(got_l[~inf]).max(initial=1.0))
     return logical(o), got_l
 
 
