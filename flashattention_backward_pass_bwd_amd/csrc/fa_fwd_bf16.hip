@@ -13,8 +13,9 @@
 // every lane column is one query row: the row's running maximum and sum are
 // per-lane values (the two half-waves, which hold different keys of the same
 // rows, agree on the maximum through v_permlane32_swap and add their sums at
-// the end).  Per 64-key tile: K and V rows go into LDS (swizzled, see
-// fa_tiles.h); per 32-key half, S^T (A operand: K rows), the exponent in fp32
+// the end).  Per 64-key tile: K and V rows go into a 2-stage LDS ring
+// (swizzled, see fa_tiles.h) by direct global->LDS copies one tile ahead; per
+// 32-key half, S^T (A operand: K rows), the exponent in fp32
 // (scale applied to the fp32 product, so L keeps fp32 accuracy), the online
 // rescale of O^T, and O^T += V^T (P.M)^T with V^T through ds_read_b64_tr_b16
 // and (P.M)^T straight from the C registers of S^T.  The MFMAs are compiler
@@ -44,8 +45,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
   constexpr int NCH = D / 8;  // 16-byte chunks per row
   constexpr int KS = D / 16;  // k-blocks of the head_dim contraction
   constexpr int DB = D / 32;  // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) __bf16 sK[BK * D];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[BK * D];
+  constexpr int RPI = 1024 / (2 * D);  // tile rows per 1 KB copy
+  constexpr int NIW = BK / RPI / 4;    // copies per wave per tile per tensor
+  constexpr int NC = (WO ? 2 : 1) * NIW;
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][BK * D];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[WO ? 2 : 1][BK * D];
 
   const int nqb = (a.Sq + kFwdRowsPerBlock - 1) / kFwdRowsPerBlock;
   const int qbi = blockIdx.x % nqb;
@@ -89,24 +93,47 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
   const __bf16* kbase = K + (int64_t)b * a.ksb + (int64_t)kvh * a.ksh;
   const __bf16* vbase = V + (int64_t)b * a.ksb + (int64_t)kvh * a.ksh;
 
-  for (int kt = kb; kt < ke; kt += BK) {
-    __syncthreads();  // every wave is done with the previous tile
+  // Copy u of this wave fills tile rows (wave*NIW + u)*RPI + lane/NCH, lane l
+  // landing in physical chunk l%NCH (so it fetches the logical chunk stored
+  // there); rows past the last key repeat it.
+  uint32_t cp_off[NIW], cp_chk[NIW];
 #pragma unroll
-    for (int u = 0; u < BK * NCH / 256; ++u) {
-      const int c = tid + 256 * u, r = c / NCH, ch = c % NCH;
-      const int64_t off = (int64_t)min(kt + r, a.Sk - 1) * a.kss + 8 * ch;  // rows past the end repeat the last
-      *reinterpret_cast<bf16x8*>(&sK[tile_off<D>(r, ch)]) = *reinterpret_cast<const bf16x8*>(kbase + off);
-      if constexpr (WO)
-        *reinterpret_cast<bf16x8*>(&sV[tile_off<D>(r, ch)]) = *reinterpret_cast<const bf16x8*>(vbase + off);
+  for (int u = 0; u < NIW; ++u) {
+    const int r = (wave * NIW + u) * RPI + lane / NCH;
+    cp_chk[u] = 16u * (uint32_t)((lane % NCH) ^ swz<D>(r));
+    cp_off[u] = 2u * (uint32_t)r * (uint32_t)a.kss + cp_chk[u];
+  }
+  auto issue = [&](int kt, int st) {  // the copies of the tile at key kt into stage st
+    const int kc = min(kt, a.Sk - 1);
+    const uint32_t lim2 = 2u * (uint32_t)min(a.Sk - 1 - kc, BK) * (uint32_t)a.kss;
+#pragma unroll
+    for (int u = 0; u < NIW; ++u) {
+      const uint32_t off = min(cp_off[u], lim2 + cp_chk[u]);
+      dma16(kbase + (int64_t)kc * a.kss, off, lds_addr(&sK[st][(wave * NIW + u) * RPI * D]));
+      if constexpr (WO) dma16(vbase + (int64_t)kc * a.kss, off, lds_addr(&sV[st][(wave * NIW + u) * RPI * D]));
     }
-    __syncthreads();
+  };
+  if (kb < ke) issue(kb, 0);
+  int st = 0;
+  for (int kt = kb; kt < ke; kt += BK, st ^= 1) {
+    barrier_lds();  // every wave is done with the tile before, whose stage the next copies refill
+    if (kt + BK < ke) {
+      issue(kt + BK, st ^ 1);
+      wait_vmcnt<NC>();  // this wave's copies of tile kt landed (the next tile's are in flight)
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_lds();  // ... and every wave's
+    // every element of the block's rows and the tile's keys visible, no mask:
+    // no per-element test (block-uniform)
+    const bool full = !MASK && rect_all_visible(a, q0, q0 + kFwdRowsPerBlock - 1, kt, kt + BK - 1);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       // S^T: row 32*half + l32 of the tile is the A operand's key.
       f32x16 s = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kr = lds_read_b128(&sK[tile_off<D>(32 * half + l32, 2 * ks + h2)]);
+        const bf16x8 kr = lds_read_b128(&sK[st][tile_off<D>(32 * half + l32, 2 * ks + h2)]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qr[ks], s, 0, 0, 0);
       }
       // Element r: key j = kt + 32*half + 8*(r/4) + 4*h2 + r%4 of row i.
@@ -116,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
       for (int r = 0; r < 16; ++r) {
         const int j = kt + 32 * half + 8 * (r >> 2) + 4 * h2 + (r & 3);
         const int dd = j - i;
-        bool ok = i < a.Sq && j < a.Sk && dd > vb.dlo && dd < vb.dhi;
+        bool ok = full || (i < a.Sq && j < a.Sk && dd > vb.dlo && dd < vb.dhi);
         float v = s[r] * a.scale_log2;
         if constexpr (MASK) {
           const float mv = ok ? mrow[(int64_t)j * a.msk] : 0.f;
@@ -128,15 +155,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
       }
       const float mnew = fmaxf(m, halves_max(tmax));
       const float mref = mnew == -__builtin_inff() ? 0.f : mnew;  // nothing counted yet: every term is 0
-      const float alpha = __builtin_amdgcn_exp2f(m - mref);
-      m = mnew;
-      l *= alpha;
-      if constexpr (WO) {
+      // Rescale only when some row's maximum grew (the other rows' factor is 1);
+      // after the first tiles of a row that is rare.
+      if (__builtin_amdgcn_ballot_w64(mnew > m) != 0) {
+        const float alpha = __builtin_amdgcn_exp2f(m - mref);
+        l *= alpha;
+        if constexpr (WO) {
 #pragma unroll
-        for (int d = 0; d < DB; ++d)
+          for (int d = 0; d < DB; ++d)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+            for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+        }
       }
+      m = mnew;
       bf16x8 pm[2];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
@@ -155,7 +186,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
       for (int t = 0; t < (WO ? 2 : 0); ++t) {
 #pragma unroll
         for (int d = 0; d < DB; ++d) {
-          const __bf16* base = &sV[(32 * half + 16 * t) * D];
+          const __bf16* base = &sV[WO ? st : 0][(32 * half + 16 * t) * D];
           const bf16x8 vt = concat(lds_read_tr(base + tr_lo[d]), lds_read_tr(base + tr_hi[d]));
           acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pm[t], acc[d], 0, 0, 0);
         }
