@@ -127,15 +127,22 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
     // every element of the block's rows and the tile's keys visible, no mask:
     // no per-element test (block-uniform)
     const bool full = !MASK && rect_all_visible(a, q0, q0 + kFwdRowsPerBlock - 1, kt, kt + BK - 1);
+    // S^T of both 32-key halves first (row 32*half + l32 of the tile is the A
+    // operand's key): the second chain runs on the matrix cores while the
+    // first half's exponents are computed.
+    f32x16 sh[2];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      // S^T: row 32*half + l32 of the tile is the A operand's key.
-      f32x16 s = f32x16{};
+      sh[half] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 kr = lds_read_b128(&sK[st][tile_off<D>(32 * half + l32, 2 * ks + h2)]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qr[ks], s, 0, 0, 0);
+        sh[half] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qr[ks], sh[half], 0, 0, 0);
       }
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const f32x16& s = sh[half];
       // Element r: key j = kt + 32*half + 8*(r/4) + 4*h2 + r%4 of row i.
       float x[16];
       float tmax = -__builtin_inff();
