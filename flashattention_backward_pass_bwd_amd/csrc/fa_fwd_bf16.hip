@@ -36,7 +36,9 @@ __device__ __forceinline__ float halves_max(float x) {
   return fmaxf(a, b);
 }
 
-template <int D, bool MASK, bool DROP, bool WO>
+// MV: a mask whose keys are contiguous and 16-byte aligned in groups of 4
+// (mask_keys_contiguous): each lane reads its 4 consecutive keys at once.
+template <int D, bool MASK, bool DROP, bool WO, bool MV>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const __bf16* __restrict__ Q,
                                                           const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V, __bf16* __restrict__ O,
@@ -74,6 +76,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
 
   int kb, ke;
   key_range(a, q0, min(q0 + kFwdRowsPerBlock, a.Sq) - 1, kb, ke);
+  if constexpr (MV) kb -= kb % BK;  // tiles on 64-key boundaries (the keys added are invisible)
   const DiagBounds vb = diag_bounds(a);
   const uint32_t rkey = DROP ? drop_row_key(a, b, h, ic) : 0u;
   const float* mrow = MASK ? a.mask + (int64_t)b * a.msb + (int64_t)h * a.msh + (int64_t)ic * a.msq : nullptr;
@@ -146,6 +149,22 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
       // Element r: key j = kt + 32*half + 8*(r/4) + 4*h2 + r%4 of row i.
       float x[16];
       float tmax = -__builtin_inff();
+      f32x4 mq[4];  // MV: the mask values of keys kt + 32*half + 8g + 4*h2 .. +3
+      if constexpr (MASK && MV) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int j0 = kt + 32 * half + 8 * g + 4 * h2;
+          mq[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (i < a.Sq && j0 + 3 - i > vb.dlo && j0 - i < vb.dhi) {
+            if (j0 + 3 < a.Sk) {  // the whole group in range: one 16-byte load
+              mq[g] = *reinterpret_cast<const f32x4*>(mrow + j0);
+            } else {              // the last keys: one by one, none past Sk - 1
+#pragma unroll
+              for (int e = 0; e < 4; ++e) mq[g][e] = j0 + e < a.Sk ? mrow[j0 + e] : 0.f;
+            }
+          }
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = kt + 32 * half + 8 * (r >> 2) + 4 * h2 + (r & 3);
@@ -153,7 +172,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
         bool ok = full || (i < a.Sq && j < a.Sk && dd > vb.dlo && dd < vb.dhi);
         float v = s[r] * a.scale_log2;
         if constexpr (MASK) {
-          const float mv = ok ? mrow[(int64_t)j * a.msk] : 0.f;
+          float mv;
+          if constexpr (MV) mv = mq[r >> 2][r & 3];
+          else mv = ok ? mrow[(int64_t)j * a.msk] : 0.f;
           ok = ok && !(mv <= kMaskedSentinel);
           v = __builtin_fmaf(mv, kLog2e, v);
         }
@@ -221,12 +242,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
   }
 }
 
-template <int D, bool MASK, bool DROP, bool WO>
+template <int D, bool MASK, bool DROP, bool WO, bool MV = false>
 static hipError_t launch_t(const PrefillArgs& a, const void* Q, const void* K, const void* V, void* O, float* L,
                            hipStream_t st) {
   const int nqb = (a.Sq + kFwdRowsPerBlock - 1) / kFwdRowsPerBlock;
   const unsigned grid = (unsigned)((int64_t)nqb * a.B * a.Hq);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, DROP, WO>), dim3(grid), dim3(256), 0, st, a,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, MASK, DROP, WO, MV>), dim3(grid), dim3(256), 0, st, a,
                      static_cast<const __bf16*>(Q), static_cast<const __bf16*>(K), static_cast<const __bf16*>(V),
                      static_cast<__bf16*>(O), L);
   return hipGetLastError();
@@ -238,6 +259,9 @@ static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, c
   const bool mk = a.mask != nullptr, dr = a.drop != 0;
   if (O == nullptr)  // L alone: dropout does not enter it
     return mk ? launch_t<D, true, false, false>(a, Q, K, V, O, L, st) : launch_t<D, false, false, false>(a, Q, K, V, O, L, st);
+  if (mk && mask_keys_contiguous(a))
+    return dr ? launch_t<D, true, true, true, true>(a, Q, K, V, O, L, st)
+              : launch_t<D, true, false, true, true>(a, Q, K, V, O, L, st);
   if (mk)
     return dr ? launch_t<D, true, true, true>(a, Q, K, V, O, L, st) : launch_t<D, true, false, true>(a, Q, K, V, O, L, st);
   return dr ? launch_t<D, false, true, true>(a, Q, K, V, O, L, st) : launch_t<D, false, false, true>(a, Q, K, V, O, L, st);

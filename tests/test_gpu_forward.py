@@ -22,11 +22,12 @@ pytestmark = pytest.mark.gpu
 FWD_CASES = {n: w for n, w in CASES.items() if w.dtype == "bf16"}
 
 
-def _check(w, inp):
+def _check(w, inp, mask_dev=None):
     spec = spec_of(w)
     ref_o, ref_l = oracle.forward(inp["q"], inp["k"], inp["v"], spec, inp["mask"])
     q, k, v = (dev(inp[n], w.layout, w.dtype) for n in ("q", "k", "v"))
-    mask = torch.from_numpy(inp["mask"]).cuda() if inp["mask"] is not None else None
+    mask = mask_dev if mask_dev is not None else (
+        torch.from_numpy(inp["mask"]).cuda() if inp["mask"] is not None else None)
     p = api.make_params(q, k, scale=w.scale, causal=w.causal, causal_offset=w.causal_offset, window=w.window,
                         dropout_p=w.dropout_p, seed=w.dropout_seed, mask=mask)
     o, lse = api.forward(p, q, k, v)
@@ -82,3 +83,30 @@ def test_forward_full_size_sampled(which):
         assert_close(go[b, h, rows], ro, "bf16", f"o rows (b={b}, h={h})")
         err = np.abs(gl[b, h, rows] - rl) / np.maximum(1.0, np.abs(rl))
         assert err.max() <= 1e-4, err.max()
+
+
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("layout", ["per_head", "key_major", "key_padding"])
+def test_forward_mask_layouts(layout, head_dim):
+    """The mask layouts of the backward's tests (one mask per head with finite
+    values, a key-major copy, a key-padding row broadcast over queries) with a
+    window, dropout and a key count that is not a multiple of 4."""
+    w = synth.EXTRAS_BF16.resized(batch=2, num_heads=4, num_kv_heads=2, head_dim=head_dim, seq_q=197,
+                                  seq_k=230, window=90, causal_offset=40, seed=61 + head_dim)
+    inp = synth.prefill_inputs(w)
+    rng = np.random.default_rng(200 + head_dim)
+    B, H, Sq, Sk = w.batch, w.num_heads, w.seq_q, w.seq_k
+    if layout == "per_head":
+        m = np.where(rng.random((B, H, Sq, Sk)) < 0.1, -1e30, rng.normal(0.0, 0.5, (B, H, Sq, Sk)))
+        inp["mask"] = m.astype(np.float32)
+        mask_dev = torch.from_numpy(inp["mask"]).cuda()
+    elif layout == "key_major":
+        m = np.where(rng.random((B, 1, Sq, Sk)) < 0.1, -1e30, 0.0).astype(np.float32)
+        inp["mask"] = m
+        mask_dev = torch.from_numpy(np.ascontiguousarray(m.transpose(0, 1, 3, 2))).cuda().transpose(2, 3)
+    else:
+        m = np.where(rng.random((B, 1, 1, Sk)) < 0.15, -1e30, 0.0).astype(np.float32)
+        inp["mask"] = m
+        mask_dev = torch.from_numpy(m).cuda()
+    say(f"[forward mask layout] {layout} D={head_dim}")
+    _check(w, inp, mask_dev)
