@@ -130,6 +130,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
     // every element of the block's rows and the tile's keys visible, no mask:
     // no per-element test (block-uniform)
     const bool full = !MASK && rect_all_visible(a, q0, q0 + kFwdRowsPerBlock - 1, kt, kt + BK - 1);
+    // Row i sees the keys [jlo, jhi): j - i in (dlo, dhi), j < Sk (none past
+    // the last row); element key j is visible iff j - jlo < span (unsigned).
+    const int jlo = max(i + vb.dlo + 1, 0);
+    const int jhi = i < a.Sq ? min(i + vb.dhi, a.Sk) : 0;
+    const uint32_t span = (uint32_t)max(jhi - jlo, 0);
     // S^T of both 32-key halves first (row 32*half + l32 of the tile is the A
     // operand's key): the second chain runs on the matrix cores while the
     // first half's exponents are computed.
@@ -168,8 +173,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = kt + 32 * half + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        const int dd = j - i;
-        bool ok = full || (i < a.Sq && j < a.Sk && dd > vb.dlo && dd < vb.dhi);
+        bool ok = full || (uint32_t)(j - jlo) < span;
         float v = s[r] * a.scale_log2;
         if constexpr (MASK) {
           float mv;
