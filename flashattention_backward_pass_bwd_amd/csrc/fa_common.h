@@ -89,6 +89,11 @@ __device__ __forceinline__ float halves_sum(float x) {  // x[lane] + x[lane ^ 32
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   return a + b;
 }
+__device__ __forceinline__ float halves_max(float x) {  // max(x[lane], x[lane ^ 32]), the same way
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return fmaxf(a, b);
+}
 // Sum over each aligned group of N consecutive lanes (N = 1, 2, 4, ..., 64), in
 // every lane of the group: quad_perm swaps lanes 1 and 2 apart, the half-row
 // mirror pairs the two quads of an 8-lane half, the row mirror the two halves

@@ -29,13 +29,6 @@ namespace fa {
 
 constexpr int kFwdRowsPerBlock = 128;
 
-// Maximum of x over lanes l and l ^ 32 (the two half-waves).
-__device__ __forceinline__ float halves_max(float x) {
-  float a = x, b = x;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-  return fmaxf(a, b);
-}
-
 // MV: a mask whose keys are contiguous and 16-byte aligned in groups of 4
 // (mask_keys_contiguous): each lane reads its 4 consecutive keys at once.
 template <int D, bool MASK, bool DROP, bool WO, bool MV>
@@ -94,7 +87,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
   float m = -__builtin_inff();  // running maximum of the exponent (log2 units), shared by both half-waves
   float l = 0.f;                // this lane's part of the running sum
   const __bf16* kbase = K + (int64_t)b * a.ksb + (int64_t)kvh * a.ksh;
-  const __bf16* vbase = V + (int64_t)b * a.ksb + (int64_t)kvh * a.ksh;
+  const __bf16* vbase = WO ? V + (int64_t)b * a.ksb + (int64_t)kvh * a.ksh : nullptr;  // V is NULL for L alone
 
   // Copy u of this wave fills tile rows (wave*NIW + u)*RPI + lane/NCH, lane l
   // landing in physical chunk l%NCH (so it fetches the logical chunk stored
@@ -229,7 +222,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
   const float lsum = halves_sum(l);
   if (i < a.Sq) {
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    __bf16* orow = O + (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh;
+    __bf16* orow = WO ? O + (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh : nullptr;  // O is NULL for L alone
 #pragma unroll
     for (int d = 0; d < (WO ? DB : 0); ++d) {
 #pragma unroll
