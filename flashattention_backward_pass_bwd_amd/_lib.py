@@ -21,6 +21,10 @@ FA_ERR_UNSUPPORTED = -3
 FA_ERR_ALIGN = -4
 FA_ERR_ARG = -5
 FA_ERR_HIP = -6
+FA_ERR_SCRATCH = -7
+
+# Size of the library-owned dS workspace of fa_bwd_dkdv_dq_noalloc (FA_BWD_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
@@ -35,6 +39,7 @@ EXPORTED = (
     "fa_bwd_ds_workspace_size",
     "fa_bwd_dkdv_ds",
     "fa_bwd_dq_ds",
+    "fa_bwd_dkdv_dq_noalloc",
     "fa_bwd_decode",
     "fa_bwd_decode_dkdv",
     "fa_bwd_decode_max_history",
@@ -119,6 +124,7 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_ds_workspace_size.argtypes = [P, ctypes.POINTER(u64)]
     L.fa_bwd_dkdv_ds.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, u64, vp]
     L.fa_bwd_dq_ds.argtypes = [P, vp, vp, u64, vp, vp]
+    L.fa_bwd_dkdv_dq_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.fa_bwd_decode.argtypes = [DP, vp, vp, vp, vp, vp, vp, vp]
     L.fa_bwd_decode_dkdv.argtypes = [DP, vp, vp, vp, vp, vp, vp, vp]
     L.fa_bwd_decode_max_history.argtypes = [DP]
@@ -129,7 +135,7 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_debug_dropout_keep.argtypes = [P, vp, vp]
     L.fa_bwd_calib_mfma_bf16.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int32, vp]
     for name in ("fa_fwd", "fa_bwd_lse", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_ds_workspace_size",
-                 "fa_bwd_dkdv_ds", "fa_bwd_dq_ds", "fa_bwd_decode", "fa_bwd_decode_dkdv",
+                 "fa_bwd_dkdv_ds", "fa_bwd_dq_ds", "fa_bwd_dkdv_dq_noalloc", "fa_bwd_decode", "fa_bwd_decode_dkdv",
                  "fa_bwd_debug_visibility", "fa_bwd_debug_dropout_keep", "fa_bwd_calib_mfma_bf16"):
         getattr(L, name).restype = ctypes.c_int
     _LIB = L

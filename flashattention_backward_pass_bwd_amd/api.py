@@ -166,6 +166,22 @@ def dq_ds(p: _lib.FaBwdParams, q, k, ws, dq_out=None):
     return dq_out
 
 
+def dkdv_dq_noalloc(p: _lib.FaBwdParams, q, k, v, do, lse, delta, dq_out=None, dk=None, dv=None):
+    """Both passes of the shared-dS pair with the library-owned dS workspace
+    (fa_bwd_dkdv_dq_noalloc: no device allocation in the library); returns (dq, dk, dv)."""
+    _same_layout(q, do)
+    _same_layout(k, v)
+    dq_out = _like(q) if dq_out is None else dq_out
+    dk = _like(k) if dk is None else dk
+    dv = _like(v) if dv is None else dv
+    _same_layout(q, dq_out)
+    _same_layout(k, dk, dv)
+    _lib.check("fa_bwd_dkdv_dq_noalloc", _lib.lib().fa_bwd_dkdv_dq_noalloc(
+        ctypes.byref(p), _vp(q), _vp(k), _vp(v), _vp(do), _vp(lse), _vp(delta), _vp(dq_out), _vp(dk), _vp(dv),
+        _stream()))
+    return dq_out, dk, dv
+
+
 def backward(q, k, v, o, do, lse, *, scale, causal=False, causal_offset=0, window=0, dropout_p=0.0,
              seed=0, mask=None, share_ds=False):
     """Delta preprocess, then the dK/dV and dQ passes; returns (dq, dk, dv, delta).

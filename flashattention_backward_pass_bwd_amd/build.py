@@ -32,6 +32,7 @@ SOURCES = [
     "fa_decode.hip",
     "fa_decode_kv.hip",
     "fa_debug.hip",
+    "fa_noalloc.hip",
     "fa_api.cpp",
 ]
 

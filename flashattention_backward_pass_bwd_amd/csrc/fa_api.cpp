@@ -197,6 +197,28 @@ fa_status fa_bwd_dq_ds(const fa_bwd_params* p, const void* K, const void* ds_ws,
   return hip_status(fa::launch_dqs_bf16(a, p->head_dim, K, ds_ws, dQ, as_stream(stream)));
 }
 
+fa_status fa_bwd_dkdv_dq_noalloc(const fa_bwd_params* p, const void* Q, const void* K, const void* V,
+                                 const void* dO, const float* L, const float* delta, void* dQ, void* dK, void* dV,
+                                 fa_stream_t stream) {
+  PrefillArgs a;
+  uint64_t need = 0;
+  if (p == nullptr || Q == nullptr || K == nullptr || V == nullptr || dO == nullptr || L == nullptr ||
+      delta == nullptr || dQ == nullptr || dK == nullptr || dV == nullptr)
+    return FA_ERR_NULL;
+  fa_status s = check_ws(p, &a, &need);
+  if (s != FA_OK) return s;
+  if (need > (uint64_t)FA_BWD_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(dQ) || !aligned16(dK) ||
+      !aligned16(dV) || (reinterpret_cast<uintptr_t>(L) & 3u) || (reinterpret_cast<uintptr_t>(delta) & 3u))
+    return FA_ERR_ALIGN;
+  void* ws = nullptr;
+  if (fa::noalloc_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+  const hipStream_t st = as_stream(stream);
+  s = hip_status(fa::launch_dkdv_bf16_ws(a, p->head_dim, Q, K, V, dO, L, delta, dK, dV, ws, st));
+  if (s != FA_OK) return s;
+  return hip_status(fa::launch_dqs_bf16(a, p->head_dim, K, ws, dQ, st));
+}
+
 fa_status fa_fwd(const fa_bwd_params* p, const void* Q, const void* K, const void* V, void* O, float* L,
                  fa_stream_t stream) {
   PrefillArgs a;
@@ -274,6 +296,7 @@ const char* fa_bwd_status_string(fa_status s) {
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a base pointer or row stride is not 16-byte aligned";
     case FA_ERR_ARG: return "FA_ERR_ARG: invalid scalar argument (dropout_p, causal, offset, window or stride)";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
+    case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: the problem needs more dS workspace than the library-owned buffer holds";
   }
   return "unknown fa_status";
 }

@@ -62,5 +62,7 @@ int decode_kv_rows_per_block();
 hipError_t launch_debug_visibility(const PrefillArgs& a, uint8_t* out, hipStream_t st);
 hipError_t launch_debug_dropout(const PrefillArgs& a, uint8_t* out, hipStream_t st);
 hipError_t launch_calib_mfma(const void* ops, float* sink, int blocks, int iters, hipStream_t st);
+// Device address of the library-owned dS workspace on the current device (fetched once per device).
+hipError_t noalloc_scratch(void** ptr);
 
 }  // namespace fa

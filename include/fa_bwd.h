@@ -46,7 +46,8 @@ typedef enum fa_status {
                               or seq_q, seq_k, causal_offset or window above 2^29 */
   FA_ERR_ALIGN = -4,       /* base or row stride not a multiple of 16 bytes, or D not unit-stride */
   FA_ERR_ARG = -5,         /* dropout_p not in [0,1), causal_offset < 0, window < 0, bad stride */
-  FA_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+  FA_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
+  FA_ERR_SCRATCH = -7      /* the problem needs more dS workspace than the library-owned buffer holds */
 } fa_status;
 
 typedef enum fa_dtype {
@@ -190,6 +191,27 @@ fa_status fa_bwd_dkdv_ds(const fa_bwd_params* p, const void* Q, const void* K, c
                          void* ds_ws, uint64_t ws_bytes, fa_stream_t stream);
 fa_status fa_bwd_dq_ds(const fa_bwd_params* p, const void* K, const void* ds_ws, uint64_t ws_bytes,
                        void* dQ, fa_stream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): both
+ * passes of the shared-dS pair, fa_bwd_dkdv_ds then fa_bwd_dq_ds, in one
+ * call, with the dS workspace in a buffer the library owns instead of a
+ * caller-given one.  Writes dK, dV and dQ exactly as that pair does (the
+ * same kernels, bitwise the same results).  The buffer is a static device
+ * array of FA_BWD_NOALLOC_SCRATCH_BYTES on every GPU the library runs on,
+ * held from the first launch on that GPU until the process ends; the call
+ * itself allocates nothing.  Its contents are opaque and stay from one call
+ * to the next; calls that overlap on one GPU (unordered streams) race on it,
+ * so order them.  The stream must belong to the current device.
+ * Errors as fa_bwd_dkdv_ds, plus FA_ERR_SCRATCH when
+ * fa_bwd_ds_workspace_size(p) exceeds FA_BWD_NOALLOC_SCRATCH_BYTES (checked
+ * before any launch).
+ */
+#define FA_BWD_NOALLOC_SCRATCH_BYTES (128u << 20)
+fa_status fa_bwd_dkdv_dq_noalloc(const fa_bwd_params* p, const void* Q, const void* K, const void* V,
+                                 const void* dO, const float* L, const float* delta, void* dQ, void* dK,
+                                 void* dV, fa_stream_t stream);
 
 /*
  * Decode-step backward, pass 1 ([wgsl-dec]): one query per head, unscaled

@@ -274,8 +274,35 @@ def test_invalid_calibration_arguments():
     assert f(ctypes.c_void_p(4096 + 4), FAKE, 4, 1, None) == _lib.FA_ERR_ALIGN
 
 
+def test_invalid_noalloc_arguments():
+    L = _lib.lib()
+    p = _valid()
+    P = ctypes.byref(p)
+    f = lambda *ptrs: L.fa_bwd_dkdv_dq_noalloc(P, *ptrs, None)
+    ten = [FAKE] * 9
+    odd = ctypes.c_void_p(4096 + 8)
+    assert L.fa_bwd_dkdv_dq_noalloc(None, *ten, None) == _lib.FA_ERR_NULL
+    for i in range(9):
+        assert f(*ten[:i], None, *ten[i + 1:]) == _lib.FA_ERR_NULL, i
+    assert f(odd, *ten[1:]) == _lib.FA_ERR_ALIGN
+    assert f(*ten[:6], odd, *ten[7:]) == _lib.FA_ERR_ALIGN
+    # a problem whose dS workspace exceeds the library-owned buffer: rejected before any HIP call
+    p.seq_q = p.seq_k = 8192
+    p.q_stride_b, p.kv_stride_b = 8192 * 8 * 128, 8192 * 2 * 128
+    assert _ws_bytes(L, p) > _lib.NOALLOC_SCRATCH_BYTES
+    assert f(*ten) == _lib.FA_ERR_SCRATCH
+    p.dtype = _lib.FA_DTYPE_F32
+    assert f(*ten) == _lib.FA_ERR_UNSUPPORTED
+
+
+def test_noalloc_buffer_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_BWD_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == _lib.NOALLOC_SCRATCH_BYTES
+
+
 def test_status_strings():
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         s = _lib.status_string(code)
         assert s.startswith("FA_")
     assert "unknown" in _lib.status_string(-99)
