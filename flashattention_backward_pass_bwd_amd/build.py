@@ -38,11 +38,15 @@ SOURCES = [
 
 ARCH = "gfx950"
 
-# Per-file extra flags (none at present: the bf16 tile kernels fix their own
-# instruction order with scheduling fences and issue their MFMAs as inline
-# assembly, so the compiler's scheduling strategy and MFMA register form do
-# not shape them).
-EXTRA_FLAGS: dict = {}
+# Per-file extra flags.  The bf16 tile kernels fix their own instruction order
+# with scheduling fences and issue their MFMAs as inline assembly, so the
+# compiler's scheduling strategy and MFMA register form do not shape them; but
+# every slot loop must unroll completely (register arrays indexed by a runtime
+# slot number become select chains and spills).  The 64-row dQ kernel's slot
+# loop is larger than the default size limit of a requested full unroll.
+EXTRA_FLAGS: dict = {
+    "fa_dq2_bf16.hip": ["-mllvm", "-pragma-unroll-threshold=100000"],
+}
 
 COMMON_FLAGS = [
     "-O3",

@@ -33,6 +33,10 @@ fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
   if (p->causal != 0 && p->causal != 1) return FA_ERR_ARG;
   if (p->causal_offset < 0 || p->window < 0) return FA_ERR_ARG;
   if (!(p->dropout_p >= 0.0f && p->dropout_p < 1.0f)) return FA_ERR_ARG;  // also rejects NaN
+  // The tile kernels seed the score chains with -L / scale: scale finite, nonzero, with a finite reciprocal.
+  if (!isfinite(p->scale) || p->scale == 0.0f || !isfinite(1.0 / (double)p->scale) ||
+      !isfinite((float)(1.0 / (double)p->scale)))
+    return FA_ERR_ARG;
   const int64_t qs[3] = {p->q_stride_b, p->q_stride_s, p->q_stride_h};
   const int64_t ks[3] = {p->kv_stride_b, p->kv_stride_s, p->kv_stride_h};
   const int64_t per16 = 16 / elem_bytes(p->dtype);
@@ -76,6 +80,7 @@ fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
   a->ksh = p->kv_stride_h;
   a->scale = p->scale;
   a->scale_log2 = (float)((double)p->scale * 1.4426950408889634);
+  a->inv_scale = (float)(1.0 / (double)p->scale);
   a->causal = p->causal;
   a->offset = p->causal_offset;
   a->window = p->window;
@@ -294,7 +299,7 @@ const char* fa_bwd_status_string(fa_status s) {
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: a size is <= 0 or num_heads is not a multiple of num_kv_heads";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head_dim, dtype, grouping or length outside the built kernels";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a base pointer or row stride is not 16-byte aligned";
-    case FA_ERR_ARG: return "FA_ERR_ARG: invalid scalar argument (dropout_p, causal, offset, window or stride)";
+    case FA_ERR_ARG: return "FA_ERR_ARG: invalid scalar argument (dropout_p, causal, offset, window, stride or scale)";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported an error";
     case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: the problem needs more dS workspace than the library-owned buffer holds";
   }

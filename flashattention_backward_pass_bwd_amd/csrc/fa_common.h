@@ -24,7 +24,8 @@ struct PrefillArgs {
   int64_t qsb, qss, qsh;          // element strides of Q, O, dO, dQ
   int64_t ksb, kss, ksh;          // element strides of K, V, dK, dV
   float scale;                    // softmax scale (applied to dQ and dK at the end)
-  float scale_log2;               // scale * log2(e): P = exp2(qk * scale_log2 + mask * log2e - L * log2e)
+  float scale_log2;               // scale * log2(e): P = exp2(scale_log2 * (qk - L / scale) + mask * log2e)
+  float inv_scale;                // 1 / scale (scale is finite and nonzero)
   int causal, offset, window;
   int drop;                       // dropout enabled (p > 0)
   uint32_t drop_thr;              // keep iff draw >= drop_thr

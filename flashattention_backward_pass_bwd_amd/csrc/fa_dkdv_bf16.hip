@@ -26,11 +26,11 @@
 // see fa_tiles.h) filled by direct global->LDS copies three tiles ahead; one
 // barrier per tile separates the last reads of a stage from its refill.  L and
 // Delta (64 floats per tile) travel through an 8-stage ring four tiles ahead;
-// two tiles before use, wave 0 turns L into -L*log2(e) and wave 1 turns Delta
-// into -Delta in place.  K is held multiplied by scale*log2(e) and the S chain
-// starts from the rows' -L*log2(e), so the MFMAs yield the exponent and P is a
-// single exp2; without dropout the dP chain starts from -Delta and yields
-// dP - Delta directly.  For causal attention without a window, block i
+// two tiles before use, wave 0 turns L into -L/scale and wave 1 turns Delta
+// into -Delta in place.  The S chain starts from the rows' -L/scale, so its
+// fp32 result times scale*log2(e) is the exponent and P is one multiply and an
+// exp2 (K enters the MFMAs as it is stored: no rounding of a scaled copy); without
+// dropout the dP chain starts from -Delta and yields dP - Delta directly.  For causal attention without a window, block i
 // also takes key block nkb-1-i, so every block carries the same work.
 //
 // Workspace mode (WS): the pass also stores every tile's dS, as the bf16 values
@@ -128,22 +128,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     const int jl = kw0 + l32;
 
     // K and V rows of this wave's keys in accumulation registers (keys past the
-    // end repeat the last key; no element of theirs is counted).  K is stored
-    // multiplied by scale*log2(e) (rounded to bf16), so the S chain yields the
-    // exponent's first term directly.
+    // end repeat the last key; no element of theirs is counted).
     bf16x8 kr[KS], vr[KS];
     const int64_t koff = (int64_t)b * a.ksb + (int64_t)jl * a.kss + (int64_t)kvh * a.ksh;
     const int64_t kclamp = (int64_t)b * a.ksb + (int64_t)min(jl, a.Sk - 1) * a.kss + (int64_t)kvh * a.ksh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      kr[s] = *reinterpret_cast<const bf16x8*>(K + kclamp + 16 * s + 8 * h2);
+      kr[s] = ld16_agpr(K + kclamp + 16 * s + 8 * h2);
       vr[s] = ld16_agpr(V + kclamp + 16 * s + 8 * h2);
-    }
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) kr[s][e] = (__bf16)((float)kr[s][e] * a.scale_log2);
-      to_agpr(kr[s]);
     }
     f32x16 acck[DB], accv[DB];
 #pragma unroll
@@ -303,12 +295,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         }
       };
       // Once a stage's L/Delta landed and a barrier passed, each wave rewrites 16
-      // rows of it in place: L -> -L*log2(e) (lanes 0-15) and, when the dP chain
+      // rows of it in place: L -> -L/scale (lanes 0-15) and, when the dP chain
       // is seeded with it, Delta -> -Delta (lanes 16-31).  The read and the write
       // go into different sections, so the LDS latency hides behind MFMAs.
       const bool fix_lane = lane < (FOLD ? 32 : 16);
       float* const fix_p = lane < 16 ? &sL[0][16 * wave + lane] : &sDel[0][16 * wave + (lane & 15)];
-      const float fix_f = lane < 16 ? -kLog2e : -1.f;
+      const float fix_f = lane < 16 ? -a.inv_scale : -1.f;
       float fix_v = 0.f;
       auto fix_at = [&](int lst) { return fix_lane ? fix_p + lst * BQ : &sDum[0][lane]; };
       auto fix_rd = [&](int lst) { fix_v = *fix_at(lst); };
@@ -353,7 +345,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       };
 
       // What an S/dP + exp/dS section needs first, read by the section before it:
-      // the A operands of its first PF MFMAs, the -L*log2(e) rows its S chain
+      // the A operands of its first PF MFMAs, the -L/scale rows its S chain
       // starts from, and the -Delta rows its dP chain starts from (FOLD) or the
       // Delta rows of the exp/dS half (dropout).
 #ifndef FA_DKDV_PF
@@ -435,13 +427,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         float pr[16], pv[16], dv[16];
         float mk[16];  // mask values of the half (MASK), read ahead from sM
         // exp of element r (C-layout register r of half me); se holds
-        // S*scale*log2(e) - L*log2(e).
+        // Q.K - L/scale, so scale*log2(e)*se is the exponent (S - L)*log2(e).
         // A mask value at or below the -1e30 sentinel excludes the element: added
         // in the exponent it makes exp2 exactly 0 (|S - L| is far below 1e29), so
         // it needs no compare of its own, and interior tiles with a mask take
         // the same path without the visibility test.
         auto ew_exp = [&](int r) {
-          float x = se[r];
+          float x = se[r] * a.scale_log2;
           if constexpr (MASK) x = __builtin_fmaf(mk[r], kLog2e, x);
           if constexpr (!FULL) x = elem_visible(r, lb, span) ? x : -__builtin_inff();
           pr[r] = __builtin_amdgcn_exp2f(x);

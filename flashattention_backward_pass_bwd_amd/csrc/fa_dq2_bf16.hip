@@ -11,7 +11,7 @@
 // issues half the LDS reads, copies and loop bookkeeping per MFMA of a
 // 32-row wave.  Per 32-key half of a 64-key tile:
 //   X: S^T = K Q^T and dP^T = V dO^T for both row blocks (32 MFMAs, chains
-//      started from -L_i*log2(e) and -Delta_i as in the 32-row kernel); the
+//      started from -L_i/scale and -Delta_i as in the 32-row kernel); the
 //      exps of S^T run under the dP^T MFMAs;
 //   Y: dQ^T += K^T dS^T of the previous half (16 MFMAs) with dS of this half.
 // So one set of S/dP accumulators is live at a time and dQ trails S/dP by a
@@ -102,9 +102,8 @@ __global__ __launch_bounds__(256, 1) void dq2_bf16_kernel(PrefillArgs a, const _
     const int q0 = qbi * kDq2RowsPerBlock;
     const int qw0 = q0 + wave * kDq2RowsPerWave;
 
-    // Q (times scale*log2(e), rounded to bf16) and dO rows of both row blocks
-    // into accumulation registers; rows past the end repeat the last row and
-    // are not written.
+    // Q and dO rows of both row blocks into accumulation registers; rows past
+    // the end repeat the last row and are not written.
     int il[RB];
     int64_t qoff[RB];
     bf16x8 qr[RB][KS], gr[RB][KS];
@@ -116,11 +115,11 @@ __global__ __launch_bounds__(256, 1) void dq2_bf16_kernel(PrefillArgs a, const _
       const int64_t qclamp = (int64_t)b * a.qsb + (int64_t)min(il[rb], a.Sq - 1) * a.qss + (int64_t)h * a.qsh;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        qr[rb][s] = *reinterpret_cast<const bf16x8*>(Q + qclamp + 16 * s + 8 * h2);
+        qr[rb][s] = ld16_agpr(Q + qclamp + 16 * s + 8 * h2);
         gr[rb][s] = ld16_agpr(dO + qclamp + 16 * s + 8 * h2);
       }
       const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq + min(il[rb], a.Sq - 1);
-      nl[rb] = il[rb] < a.Sq ? -L[lrow] * kLog2e : -__builtin_inff();
+      nl[rb] = il[rb] < a.Sq ? -L[lrow] * a.inv_scale : 0.f;  // rows past the end: never counted
       del[rb] = il[rb] < a.Sq ? Dl[lrow] : 0.f;
     }
     f32x16 accq[RB][DB];
@@ -129,14 +128,6 @@ __global__ __launch_bounds__(256, 1) void dq2_bf16_kernel(PrefillArgs a, const _
 #pragma unroll
       for (int d = 0; d < DB; ++d) accq[rb][d] = f32x16{};
     wait_all_vmem();
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qr[rb][s][e] = (__bf16)((float)qr[rb][s][e] * a.scale_log2);
-        to_agpr(qr[rb][s]);
-      }
 
     int kb, ke;
     key_range(a, q0, min(q0 + kDq2RowsPerBlock, a.Sq) - 1, kb, ke);
@@ -228,7 +219,7 @@ __global__ __launch_bounds__(256, 1) void dq2_bf16_kernel(PrefillArgs a, const _
           }
         }
         auto ew_exp = [&](int rb, int r) {
-          float x = s[rb][r];
+          float x = s[rb][r] * a.scale_log2;  // s holds Q.K - L/scale
           if constexpr (!FULL) {
             const bool ok = elem_visible(r, lb[rb], span[rb]);
             x = ok ? x : -__builtin_inff();

@@ -9,9 +9,9 @@
 // Per 64-key tile and wave: S^T = K Q^T and dP^T = V dO^T (row-major A
 // operands from LDS), P and dS^T in registers, then dQ^T += K^T dS^T (K
 // transposed through ds_read_b64_tr_b16).  S^T has one query per lane column,
-// so L_i and Delta_i are per-lane scalars: Q is held multiplied by
-// scale*log2(e) and the S^T chain starts from -L_i*log2(e), so P is a single
-// exp2 of the MFMA result, and without dropout the dP^T chain starts from
+// so L_i and Delta_i are per-lane scalars: the S^T chain starts from
+// -L_i/scale, so P is the exp2 of the fp32 MFMA result times scale*log2(e) (Q
+// enters the MFMAs as stored), and without dropout the dP^T chain starts from
 // -Delta_i, so dP - Delta comes out of the MFMAs.  dS^T is already the B
 // operand of the last contraction.
 //
@@ -137,18 +137,16 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
 
     // Q and dO rows of this wave's queries, straight into accumulation registers
     // (rows past the end repeat the last row; their results are not written).
-    // Q is stored multiplied by scale*log2(e) (rounded to bf16), so the S^T chain
-    // yields the exponent's first term directly.
     bf16x8 qr[KS], gr[KS];
     const int64_t qoff = (int64_t)b * a.qsb + (int64_t)il * a.qss + (int64_t)h * a.qsh;
     const int64_t qclamp = (int64_t)b * a.qsb + (int64_t)min(il, a.Sq - 1) * a.qss + (int64_t)h * a.qsh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      qr[s] = *reinterpret_cast<const bf16x8*>(Q + qclamp + 16 * s + 8 * h2);
+      qr[s] = ld16_agpr(Q + qclamp + 16 * s + 8 * h2);
       gr[s] = ld16_agpr(dO + qclamp + 16 * s + 8 * h2);
     }
     const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq + min(il, a.Sq - 1);
-    const float nl = il < a.Sq ? -L[lrow] * kLog2e : -__builtin_inff();
+    const float nl = il < a.Sq ? -L[lrow] * a.inv_scale : 0.f;  // rows past the end: never counted
     const float del = il < a.Sq ? Dl[lrow] : 0.f;
     uint32_t rk = 0;
     if constexpr (DROP) rk = drop_row_key(a, b, h, il);
@@ -160,19 +158,13 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
 #pragma unroll
     for (int d = 0; d < DB; ++d) accq[d] = f32x16{};
     wait_all_vmem();  // Q, dO rows, L and Delta are in registers before the copy ring starts
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qr[s][e] = (__bf16)((float)qr[s][e] * a.scale_log2);
-      to_agpr(qr[s]);
-    }
 
     int kb, ke;
     key_range(a, q0, min(q0 + kDqRowsPerBlock, a.Sq) - 1, kb, ke);
     const int ntiles = (ke - kb + BK - 1) / BK;
 
     if (ntiles > 0) {
-      // The S^T chain starts from -L_i*log2(e) and (without dropout) the dP^T
+      // The S^T chain starts from -L_i/scale and (without dropout) the dP^T
       // chain from -Delta_i: every C register of a lane is query row i.
       f32x16 nls, dpi;
 #pragma unroll
@@ -271,9 +263,9 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
         float pv[16], dv[16];
         float mk[16];  // mask values of the half (MASK), read ahead from sM
         // exp of element r (C-layout register r of half me); se holds
-        // S*scale*log2(e) - L*log2(e).
+        // Q.K - L/scale, so scale*log2(e)*se is the exponent (S - L)*log2(e).
         auto ew_exp = [&](int r) {
-          float x = se[r];
+          float x = se[r] * a.scale_log2;
           if constexpr (!FULL) {
             bool ok = elem_visible(r, lb, span);
             if constexpr (MASK) {

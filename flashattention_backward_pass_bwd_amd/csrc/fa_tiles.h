@@ -103,14 +103,15 @@ __device__ __forceinline__ void dma16_nt(const void* sbase, uint32_t voff, uint3
 // later kernel).  Inline assembly like the copies: the compiler places no
 // waits for it.  Stores count in vmcnt like loads (completing in issue
 // order), so callers' manual waits include the stores issued after the
-// accesses they wait for.  Its data registers are next written many
-// instructions later (more than the one wait state a store of more than 8
-// bytes needs).
+// accesses they wait for.  A store of more than 8 bytes reads its data
+// registers after issue: a VALU write of them needs a wait state after the
+// store, which the compiler does not insert for an asm statement, so the
+// statement ends with two.
 #ifndef FA_WS_STORE_POLICY
 #define FA_WS_STORE_POLICY " nt"
 #endif
 __device__ __forceinline__ void st16_nt(void* sbase, uint32_t voff, const bf16x8& v) {
-  asm volatile("s_nop 4\n\tglobal_store_dwordx4 %0, %1, %2" FA_WS_STORE_POLICY
+  asm volatile("s_nop 4\n\tglobal_store_dwordx4 %0, %1, %2" FA_WS_STORE_POLICY "\n\ts_nop 1"
                : : "v"(voff), "v"(v), "s"(sgpr_ptr(sbase)));
 }
 

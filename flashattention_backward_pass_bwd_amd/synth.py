@@ -41,6 +41,7 @@ class PrefillWorkload:
     dropout_p: float = 0.0
     dropout_seed: int = 0
     seed: int = 0
+    qk_std: float = 1.0  # standard deviation of the Q and K draws (scores then have std ~ qk_std^2 at scale 1/sqrt(D))
 
     def resized(self, **kw) -> "PrefillWorkload":
         return dataclasses.replace(self, **kw)
@@ -106,11 +107,15 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def prefill_inputs(w: PrefillWorkload):
-    """Q, K, V, dO ([B,H,S,D] float32, bf16-representable for bf16) and the mask."""
+    """Q, K, V, dO ([B,H,S,D] float32, bf16-representable for bf16) and the mask.
+
+    Q and K are N(0, qk_std^2) draws (the fp32 standard normal times qk_std, then
+    rounded to the storage dtype); V and dO are N(0, 1)."""
     rng = np.random.Generator(np.random.PCG64(w.seed))
     B, Hq, Hkv, Sq, Sk, D = w.batch, w.num_heads, w.num_kv_heads, w.seq_q, w.seq_k, w.head_dim
-    q = _store(rng.standard_normal((B, Hq, Sq, D), dtype=np.float32), w.dtype)
-    k = _store(rng.standard_normal((B, Hkv, Sk, D), dtype=np.float32), w.dtype)
+    sd = np.float32(w.qk_std)
+    q = _store(rng.standard_normal((B, Hq, Sq, D), dtype=np.float32) * sd, w.dtype)
+    k = _store(rng.standard_normal((B, Hkv, Sk, D), dtype=np.float32) * sd, w.dtype)
     v = _store(rng.standard_normal((B, Hkv, Sk, D), dtype=np.float32), w.dtype)
     do = _store(rng.standard_normal((B, Hq, Sq, D), dtype=np.float32), w.dtype)
     mask = None

@@ -45,7 +45,8 @@ typedef enum fa_status {
   FA_ERR_UNSUPPORTED = -3, /* head_dim / dtype / history length / row stride outside the built kernels,
                               or seq_q, seq_k, causal_offset or window above 2^29 */
   FA_ERR_ALIGN = -4,       /* base or row stride not a multiple of 16 bytes, or D not unit-stride */
-  FA_ERR_ARG = -5,         /* dropout_p not in [0,1), causal_offset < 0, window < 0, bad stride */
+  FA_ERR_ARG = -5,         /* dropout_p not in [0,1), causal_offset < 0, window < 0, bad stride,
+                              scale zero or not finite */
   FA_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
   FA_ERR_SCRATCH = -7      /* the problem needs more dS workspace than the library-owned buffer holds */
 } fa_status;
@@ -103,7 +104,7 @@ typedef struct fa_bwd_params {
   int32_t head_dim;     /* 64 or 128 */
   int64_t q_stride_b, q_stride_s, q_stride_h;    /* elements; Q, O, dO, dQ */
   int64_t kv_stride_b, kv_stride_s, kv_stride_h; /* elements; K, V, dK, dV */
-  float scale;
+  float scale;           /* softmax scale; finite, nonzero, with a finite fp32 reciprocal (else FA_ERR_ARG) */
   int32_t causal;        /* 0 or 1 */
   int32_t causal_offset; /* >= 0: query i sits at key position i + causal_offset */
   int32_t window;        /* 0 = no window */

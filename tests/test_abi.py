@@ -94,6 +94,11 @@ BAD = [
     ("q_stride_s", 8 * 128 + 4, _lib.FA_ERR_ALIGN),
     ("kv_stride_h", 130, _lib.FA_ERR_ALIGN),
     ("q_stride_b", -1, _lib.FA_ERR_ARG),
+    # the score chains start from -L / scale: a zero, infinite, NaN or subnormal scale is rejected
+    ("scale", 0.0, _lib.FA_ERR_ARG),
+    ("scale", float("inf"), _lib.FA_ERR_ARG),
+    ("scale", float("nan"), _lib.FA_ERR_ARG),
+    ("scale", 1e-39, _lib.FA_ERR_ARG),
 ]
 
 
@@ -112,6 +117,7 @@ def test_invalid_prefill_arguments(field, value, code):
     assert L.fa_bwd_debug_dropout_keep(P, FAKE, None) == code
     assert L.fa_bwd_dkdv_ds(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == code
     assert L.fa_bwd_dq_ds(P, FAKE, FAKE, 1 << 40, FAKE, None) == code
+    assert L.fa_bwd_dkdv_dq_noalloc(P, *([FAKE] * 9), None) == code
 
 
 def test_null_and_misaligned_pointers():

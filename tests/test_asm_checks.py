@@ -14,6 +14,12 @@
   than the next MFMA of its own chain within the twelve wait states an XDL
   result needs (the count the compiler itself inserts for
   v_mfma_f32_32x32x16_bf16 on gfx950).
+* A VMEM store of more than 8 bytes reads its data registers after issue;
+  a write to them by the next instruction (one wait state is needed) would
+  change the stored data.  Checked for the inline-assembly stores.
+* The tile kernels use no scratch memory (no VGPR spills; SGPRs spill only
+  into VGPR lanes): a spill in their software pipelines means a slot loop did
+  not unroll or the register plan broke.
 """
 import concurrent.futures
 import os
@@ -305,3 +311,56 @@ def test_result_read_detector_flags_plain_cases():
     ])
     bad = _result_reads(text)
     assert len(bad) == 1 and "v_exp_f32_e32 v30, v3" in bad[0]
+
+
+def test_tile_kernels_use_no_scratch():
+    for src, text in _compiled().items():
+        spills = [int(m) for m in re.findall(r"\.vgpr_spill_count:\s+(\d+)", text)]
+        scratch = [int(m) for m in re.findall(r"; ScratchSize:\s+(\d+)", text)]
+        assert spills and max(spills) == 0, (src, "vgpr spills", spills)
+        assert scratch and max(scratch) == 0, (src, "scratch bytes", scratch)
+
+
+_WIDE_STORE = re.compile(r"^(global|flat|buffer|scratch)_store_dwordx[34]\b")
+
+
+def _store_data_hazards(text):
+    """Instructions that write a wide inline-asm store's data registers in the
+    wait state right after it."""
+    bad = []
+    seq = _instructions(text)
+    for i, (ins, inside) in enumerate(seq):
+        op = ins.split()[0]
+        if not (inside and _WIDE_STORE.match(op)):
+            continue
+        ops = [o.strip() for o in ins[len(op):].split(",")]
+        data = _regs(ops[0] if op.startswith("buffer_") else ops[1])
+        for nins, _ in seq[i + 1:i + 2]:
+            if nins == "<kernel>" or nins.split()[0] == "s_nop":
+                break
+            w = _regs(nins[len(nins.split()[0]):].split(",")[0]) if not nins.startswith(("s_", "ds_write", "global_store", "buffer_store")) else set()
+            if w & data:
+                bad.append(f"{ins} -> {nins}")
+    return bad
+
+
+def test_wide_asm_stores_keep_their_data_for_a_wait_state():
+    found = 0
+    for src, text in _compiled().items():
+        found += len([1 for ins, inside in _instructions(text) if inside and _WIDE_STORE.match(ins.split()[0])])
+        assert _store_data_hazards(text) == [], src
+    assert found > 0
+
+
+def test_store_data_detector_flags_plain_cases():
+    text = "\n".join([
+        "_ZN2fa1kEv:",
+        ";;#ASMSTART", "\tglobal_store_dwordx4 v160, v[4:7], s[58:59] nt", ";;#ASMEND",
+        "\tv_cvt_pk_bf16_f32 v5, v1, v2",                          # flagged: writes store data at once
+        ";;#ASMSTART", "\tglobal_store_dwordx4 v160, v[8:11], s[58:59] nt", "\ts_nop 1", ";;#ASMEND",
+        "\tv_cvt_pk_bf16_f32 v9, v1, v2",                          # fine: wait states in between
+        ";;#ASMSTART", "\tglobal_store_dwordx4 v160, v[12:15], s[58:59] nt", ";;#ASMEND",
+        "\tv_cvt_pk_bf16_f32 v20, v1, v2",                         # fine: other registers
+    ])
+    bad = _store_data_hazards(text)
+    assert len(bad) == 1 and "v5" in bad[0], bad

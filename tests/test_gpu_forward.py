@@ -39,8 +39,13 @@ def _check(w, inp, mask_dev=None):
     say(f"  L: max err {err.max() if err.size else 0.0:.2e} (tol 1e-4)")
     assert err.size == 0 or err.max() <= 1e-4
     assert_close(logical(o), ref_o, "bf16", "o")
-    lonly = api.lse(p, q, k).cpu().numpy().astype(np.float64)  # the L-only sweep: the same values
-    assert np.array_equal(np.isinf(lonly), inf) and np.abs(lonly[~inf] - got_l[~inf]).max(initial=0.0) <= 1e-5 * max(1.0, np.abs(got_l[~inf]).max(initial=1.0))
+    # the L-only sweep against the oracle's L, at the same bar, and against the forward's L
+    lonly = api.lse(p, q, k).cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isinf(lonly), inf) and np.all(lonly[inf] > 0), "L-only sweep: rows with nothing counted"
+    lerr = np.abs(lonly[~inf] - ref_l[~inf]) / np.maximum(1.0, np.abs(ref_l[~inf]))
+    say(f"  L-only sweep: max err {lerr.max() if lerr.size else 0.0:.2e} (tol 1e-4)")
+    assert lerr.size == 0 or lerr.max() <= 1e-4
+    assert np.abs(lonly[~inf] - got_l[~inf]).max(initial=0.0) <= 1e-5 * max(1.0, np.abs(got_l[~inf]).max(initial=1.0))
     return logical(o), got_l
 
 

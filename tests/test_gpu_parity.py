@@ -53,6 +53,16 @@ CASES = {
     "mask_noncausal_bf16": synth.EXTRAS_BF16.resized(batch=1, num_heads=4, num_kv_heads=4, seq_q=190, seq_k=260,
                                                      causal=False, window=0, mask_density=0.3, dropout_p=0.0,
                                                      seed=20),
+    # large logits: Q, K ~ N(0, 3^2) and N(0, 4^2), so the scaled scores have std ~9 and ~16
+    # (peaked softmax rows); plain causal D = 128, and with window, mask and dropout
+    "logits_std9_bf16_d128": synth.LONG_BF16.resized(num_heads=4, num_kv_heads=2, seq_q=520, seq_k=520,
+                                                     qk_std=3.0, seed=25),
+    "logits_std16_bf16_d128": synth.LONG_BF16.resized(num_heads=4, num_kv_heads=2, seq_q=520, seq_k=520,
+                                                      qk_std=4.0, seed=26),
+    "logits_std16_extras_bf16": synth.EXTRAS_BF16.resized(batch=1, num_heads=4, num_kv_heads=2, seq_q=400,
+                                                          seq_k=400, window=160, qk_std=4.0, seed=27),
+    "logits_std16_bf16_d64": synth.LONG_BF16.resized(head_dim=64, num_heads=4, num_kv_heads=2, seq_q=300,
+                                                     seq_k=300, scale=0.125, qk_std=4.0, seed=28),
 }
 
 
@@ -111,22 +121,31 @@ def _spec(w):
     return spec_of(w)
 
 
-def test_fully_masked_row_is_zero_and_finite():
-    w = synth.EXTRAS_BF16.resized(dtype="f32", batch=2, num_heads=4, num_kv_heads=2, seq_q=96, seq_k=96,
-                                  window=8, mask_density=0.05, seed=21)
+@pytest.mark.parametrize("variant", ["f32", "bf16_recompute", "bf16_shared_ds"])
+def test_fully_masked_row_is_zero_and_finite(variant):
+    """Rows where nothing counts (L = +inf): dQ rows exactly 0, no NaN anywhere, the
+    rest at the dtype's bar; fp32 and both bf16 paths (window, mask, dropout, GQA)."""
+    dtype = "f32" if variant == "f32" else "bf16"
+    w = synth.EXTRAS_BF16.resized(dtype=dtype, batch=2, num_heads=4, num_kv_heads=2, seq_q=96 if dtype == "f32" else 230,
+                                  seq_k=96 if dtype == "f32" else 230, window=8 if dtype == "f32" else 70,
+                                  mask_density=0.05, seed=21)
     inp = synth.prefill_inputs(w)
     inp["mask"][1, 0, 0, 0] = np.float32(-1e30)  # row 0 of batch 1 sees only key 0, now excluded
     inp["mask"][0, 0, 5, :] = np.float32(-1e30)  # row 5 of batch 0: every key excluded
+    inp["mask"][1, 0, 200 if dtype == "bf16" else 90, :] = np.float32(-1e30)  # a row in a later tile
     o, lse = forward_inputs(w, inp)
-    assert np.isinf(lse[1, :, 0]).all() and np.isinf(lse[0, :, 5]).all()
-    got = gpu_backward(w, inp, o, lse)
+    dead = [(1, 0), (0, 5), (1, 200 if dtype == "bf16" else 90)]
+    for b, i in dead:
+        assert np.isinf(lse[b, :, i]).all()
+    got = gpu_backward(w, inp, o, lse, share_ds=(variant == "bf16_shared_ds"))
     for k in ("dq", "dk", "dv"):
         assert np.isfinite(got[k]).all()
-    assert np.all(got["dq"][1, :, 0] == 0.0) and np.all(got["dq"][0, :, 5] == 0.0)
+    for b, i in dead:
+        assert np.all(got["dq"][b, :, i] == 0.0), (b, i)
     delta, dq, dk, dv = oracle.backward(inp["q"], inp["k"], inp["v"], o, inp["do"], lse, _spec(w), inp["mask"])
-    assert_close(got["dq"], dq, "f32", "dq")
-    assert_close(got["dk"], dk, "f32", "dk")
-    assert_close(got["dv"], dv, "f32", "dv")
+    assert_close(got["dq"], dq, dtype, "dq")
+    assert_close(got["dk"], dk, dtype, "dk")
+    assert_close(got["dv"], dv, dtype, "dv")
 
 
 def test_unseen_keys_and_rows_get_exact_zeros():
