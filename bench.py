@@ -6,12 +6,19 @@ step = the whole backward path: Delta preprocess + dK/dV pass + dQ pass, all
 inputs resident in HBM.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|extras|causal_f32|decode|copy]
-                  [--no-cpu-baseline]
+                  [--path shared_ds|recompute] [--no-cpu-baseline] [--no-mfma-ceiling] [--no-side-workloads]
 
-O and L (inputs of the backward) are produced once, before timing, by a plain
-torch fp32 reference forward on the GPU (chunked QK^T / softmax / PV); they are
-inputs only, never part of the timed path.  The cpu_baseline leg times the
-CPU fp64 oracle on one head of the same workload.
+O and L (inputs of the backward) are produced once, before timing: for the
+bf16 workloads by the library's own forward (fa_fwd, parity-tested against the
+oracle forward), for the fp32 ones by a plain torch fp32 reference forward on
+the GPU (chunked QK^T / softmax / PV); they are inputs only, never part of the
+timed path (the forward is timed separately).  The cpu_baseline leg times the
+CPU fp64 oracle on one GQA group of the same workload.
+
+The default (long) run also times, in the same process and with the same
+steps, the long workload on the other bf16 path (recompute vs shared dS) and
+the two other prefill workloads (the bf16 GQA window + mask + dropout one and
+the fp32 causal MHA one), each reported as a summary under its own key.
 """
 
 from __future__ import annotations
@@ -47,6 +54,8 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mfma-ceiling", action="store_true",
                     help="skip the calibration of the bf16 MFMA rate on N(0,1) operands (about 0.5 s)")
+    ap.add_argument("--no-side-workloads", action="store_true",
+                    help="long workload: skip the other bf16 path and the extras / fp32 causal summaries")
     return ap.parse_args()
 
 
@@ -193,8 +202,8 @@ def _cpu_baseline(w, q, k, v, o, do, lse):
                       f"{dt:.1f} s for {flops / 1e9:.1f} nominal GFLOP", "seconds": dt}
 
 
-def bench_prefill(args, w):
-    import numpy as np
+def _prepare(w):
+    """Seeded inputs of workload w on the device, in its layout, and the O, L of its forward."""
     import torch
 
     from flashattention_backward_pass_bwd_amd import api, synth
@@ -215,7 +224,7 @@ def bench_prefill(args, w):
     p = api.make_params(q, k, scale=w.scale, causal=w.causal, causal_offset=w.causal_offset, window=w.window,
                         dropout_p=w.dropout_p, seed=w.dropout_seed, mask=mask)
     if w.dtype == "bf16":
-        # O, L from the library's forward (parity-tested against the oracle), timed below
+        # O, L from the library's forward (parity-tested against the oracle)
         _log(f"inputs of {w.name} on device; forward for O, L")
         o, lse = api.forward(p, q, k, v)
     else:
@@ -224,15 +233,23 @@ def bench_prefill(args, w):
         o, lse = _torch_reference_forward(q, k, v, w, mask, keep)
         del keep
     torch.cuda.synchronize()
-    _log("O, L ready; timing")
+    return {"q": q, "k": k, "v": v, "do": do, "mask": mask, "o": o, "lse": lse, "p": p, "dev": dev}
 
+
+def _time_path(args, w, t, shared):
+    """Event-timed steps (preprocess + dK/dV + dQ) of one path: (ms per step, per-kernel ms, workspace bytes)."""
+    import torch
+
+    from flashattention_backward_pass_bwd_amd import api
+
+    dev, p = t["dev"], t["p"]
+    q, k, v, do, o, lse = t["q"], t["k"], t["v"], t["do"], t["o"], t["lse"]
     delta = torch.empty((w.batch, w.num_heads, w.seq_q), dtype=torch.float32, device=dev)
     dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=dev)
     dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=dev)
     dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=dev)
-    # bf16: the dK/dV pass stores dS and the dQ pass reads it (the workspace is
-    # allocated here, outside the timed steps); fp32: both passes recompute.
-    shared = w.dtype == "bf16" and args.path == "shared_ds"
+    # shared dS: the dK/dV pass stores dS and the dQ pass reads it (the workspace
+    # is allocated here, outside the timed steps); recompute: both passes recompute.
     ws = api.ds_workspace(p, dev) if shared else None
     ws_bytes = api.ds_workspace_bytes(p) if shared else 0
 
@@ -263,24 +280,85 @@ def bench_prefill(args, w):
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record()
-    for s in range(args.steps):
-        step(evs[s])
+    for s_ in range(args.steps):
+        step(evs[s_])
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(stop)
-    ms = total_ms / args.steps
-    t_pre = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    t_dkdv = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    t_dq = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    ms = start.elapsed_time(stop) / args.steps
+    kms = {"preprocess": sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps,
+           "dkdv": sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps,
+           "dq": sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps}
+    del ws
+    return ms, kms, ws_bytes, wall
 
+
+def _work(w):
+    """Nominal FLOP (the metric's count), visible pairs, peak and its dtype's name."""
     nominal = 10.0 * w.batch * w.num_heads * w.seq_q * w.seq_k * w.head_dim * (0.5 if w.causal else 1.0)
     pairs = _visible_pairs(w) * w.batch * w.num_heads
-    value = nominal / (ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    # dominant kernel: the dK/dV pass executes 4 of the contractions (QK^T, dO V^T, dV, dK): 8*D FLOP per visible pair
-    dkdv_flops = 8.0 * w.head_dim * pairs
-    achieved = dkdv_flops / (t_dkdv * 1e-3) / 1e12
+    return nominal, pairs, peak
+
+
+def _dkdv_roofline(w, t_dkdv, pairs, peak):
+    # the dK/dV pass executes 4 of the contractions (QK^T, dO V^T, dV, dK): 8*D FLOP per visible pair
+    achieved = 8.0 * w.head_dim * pairs / (t_dkdv * 1e-3) / 1e12
+    return {"kernel": "dkdv_kernel", "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+            "per_unit": "8*D FLOP per visible (b,h,i,j) pair", "units": pairs}
+
+
+def _dq_ds_roofline(w, t_dq, ws_bytes):
+    # the dQ pass over stored dS streams the workspace once: HBM-bound
+    dq_bytes = ws_bytes + (w.batch * w.num_kv_heads * w.seq_k * w.head_dim +
+                           w.batch * w.num_heads * w.seq_q * w.head_dim) * 2
+    gbs = dq_bytes / (t_dq * 1e-3) / 1e9
+    return {"kernel": "dqs_kernel", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "per_unit": "the stored dS (16 KB per visible 64x128 tile) + K read, dQ written",
+            "algorithmic_bytes": dq_bytes}
+
+
+def _summary(args, w):
+    """Compact record of another prefill workload, timed the same way as the main line."""
+    import torch
+
+    t = _prepare(w)
+    shared = w.dtype == "bf16"
+    ms, kms, ws_bytes, _ = _time_path(args, w, t, shared)
+    nominal, pairs, peak = _work(w)
+    value = nominal / (ms * 1e-3) / 1e12
+    out = {"workload": w.name, "dtype": w.dtype, "path": "shared_ds" if shared else "recompute",
+           "ms_per_step": round(ms, 4), "value": round(value, 2), "unit": "TFLOP/s",
+           "peak": peak, "pct_of_peak": round(100.0 * value / peak, 2),
+           "nominal_gflop": round(nominal / 1e9, 3), "window_aware_gflop": round(10.0 * w.head_dim * pairs / 1e9, 3),
+           "window_aware_pct_of_peak": round(100.0 * 10.0 * w.head_dim * pairs / (ms * 1e-3) / 1e12 / peak, 2),
+           "kernels_ms": {k_: round(v_, 4) for k_, v_ in kms.items()},
+           "roofline": _dkdv_roofline(w, kms["dkdv"], pairs, peak)}
+    if shared:
+        out["roofline_dq"] = _dq_ds_roofline(w, kms["dq"], ws_bytes)
+    _log(f"{w.name}: {ms:.4f} ms/step ({out['pct_of_peak']}% of the {w.dtype} peak)")
+    del t
+    torch.cuda.synchronize()
+    return out
+
+
+def bench_prefill(args, w):
+    import torch
+
+    from flashattention_backward_pass_bwd_amd import api, synth
+
+    t = _prepare(w)
+    p, q, k, v, o, lse = t["p"], t["q"], t["k"], t["v"], t["o"], t["lse"]
+    _log("O, L ready; timing")
+    shared = w.dtype == "bf16" and args.path == "shared_ds"
+    ms, kms, ws_bytes, wall = _time_path(args, w, t, shared)
+    nominal, pairs, peak = _work(w)
+    value = nominal / (ms * 1e-3) / 1e12
+    roof = _dkdv_roofline(w, kms["dkdv"], pairs, peak)
+    roof["traffic"] = _dkdv_traffic_bytes() if (w.name == synth.LONG_BF16.name and shared) else None
+    roof["traffic_unit"] = "bytes per launch (HBM, FETCH_SIZE+WRITE_SIZE scaled by the copy calibration)"
     out = {
         "metric": "attention-backward TFLOP/s and % of MI355X bf16 MFMA peak, 1 GPU",
         "value": round(value, 2),
@@ -303,23 +381,22 @@ def bench_prefill(args, w):
                    "dropout_p": w.dropout_p, "nominal_gflop": round(nominal / 1e9, 3),
                    "path": "shared_ds" if shared else "recompute", "ds_workspace_bytes": ws_bytes,
                    "window_aware_gflop": round(10.0 * w.head_dim * pairs / 1e9, 3)},
-        "kernels_ms": {"preprocess": round(t_pre, 4), "dkdv": round(t_dkdv, 4), "dq": round(t_dq, 4)},
-        "roofline": {"kernel": "dkdv_kernel", "bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": _dkdv_traffic_bytes() if w.name == synth.LONG_BF16.name else None,
-                     "traffic_unit": "bytes per launch (HBM, FETCH_SIZE+WRITE_SIZE scaled by the copy calibration)",
-                     "per_unit": "8*D FLOP per visible (b,h,i,j) pair", "units": pairs},
+        "kernels_ms": {k_: round(v_, 4) for k_, v_ in kms.items()},
+        "roofline": roof,
     }
     if shared:
-        # the dQ pass over stored dS streams the workspace once: HBM-bound
-        esz = 2
-        dq_bytes = ws_bytes + (w.batch * w.num_kv_heads * w.seq_k * w.head_dim +
-                               w.batch * w.num_heads * w.seq_q * w.head_dim) * esz
-        gbs = dq_bytes / (t_dq * 1e-3) / 1e9
-        out["roofline_dq"] = {"kernel": "dqs_kernel", "bound": "hbm", "achieved": round(gbs, 1),
-                              "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                              "per_unit": "the stored dS (16 KB per visible 64x128 tile) + K read, dQ written",
-                              "algorithmic_bytes": dq_bytes}
+        out["roofline_dq"] = _dq_ds_roofline(w, kms["dq"], ws_bytes)
+    _log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+    side = w.name == synth.LONG_BF16.name and not args.no_side_workloads
+    if side and w.dtype == "bf16":
+        # the same workload on the other bf16 path (no dS workspace on the recompute path)
+        oms, okms, ows, _ = _time_path(args, w, t, not shared)
+        out["other_path"] = {"path": "recompute" if shared else "shared_ds", "ms_per_step": round(oms, 4),
+                             "value": round(nominal / (oms * 1e-3) / 1e12, 2),
+                             "pct_of_peak": round(100.0 * nominal / (oms * 1e-3) / 1e12 / peak, 2),
+                             "kernels_ms": {k_: round(v_, 4) for k_, v_ in okms.items()},
+                             "ds_workspace_bytes": ows}
+        _log(f"other path ({out['other_path']['path']}): {oms:.3f} ms/step")
     if w.dtype == "bf16":
         # the forward on the same inputs, timed on its own after the backward steps
         for _ in range(2):
@@ -336,18 +413,23 @@ def bench_prefill(args, w):
                           "achieved": round(ftf, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(ftf / peak, 4),
                           "per_unit": "4*D FLOP per visible (b,h,i,j) pair (QK^T and PV)", "units": pairs}
         _log(f"forward: {fms:.3f} ms")
-    _log(f"timed {args.steps} steps: {ms:.3f} ms/step")
     if w.dtype == "bf16" and not args.no_mfma_ceiling:
         ceiling = _mfma_ceiling()
         out["roofline"]["mfma_ceiling"] = {
-            "value": round(ceiling, 1), "unit": "TFLOP/s", "frac": round(achieved / ceiling, 4),
+            "value": round(ceiling, 1), "unit": "TFLOP/s", "frac": round(roof["achieved"] / ceiling, 4),
             "how": "back-to-back v_mfma_f32_32x32x16_bf16 on every SIMD, N(0,1) bf16 operands rotating "
                    "over registers (fa_bwd_calib_mfma_bf16), after the timed steps"}
         _log(f"MFMA ceiling on N(0,1) operands: {ceiling:.1f} TFLOP/s")
     if not args.no_cpu_baseline:
-        _log("cpu baseline: oracle on one head")
-        out["cpu_baseline"] = _cpu_baseline(w, q, k, v, o, do, lse)
+        _log("cpu baseline: oracle on one GQA group")
+        out["cpu_baseline"] = _cpu_baseline(w, q, k, v, o, t["do"], lse)
         _log(f"cpu baseline took {out['cpu_baseline']['seconds']:.1f} s")
+    if side:
+        del t, p, q, k, v, o, lse
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        out["side_workloads"] = {"extras": _summary(args, synth.EXTRAS_BF16),
+                                 "causal_f32": _summary(args, synth.CAUSAL_F32)}
     return out
 
 

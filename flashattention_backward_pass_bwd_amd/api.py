@@ -182,16 +182,35 @@ def dkdv_dq_noalloc(p: _lib.FaBwdParams, q, k, v, do, lse, delta, dq_out=None, d
     return dq_out, dk, dv
 
 
+# The shared-dS path's workspace grows as B * Hq * Sq * Sk * 2 bytes (8.7 GB for
+# one 16k x 16k sequence of 32 heads): it is used only while it fits in this
+# share of the device memory that is free at the call.
+DS_WORKSPACE_FRACTION = 0.5
+
+
+def use_shared_ds(dtype_code: int, ws_bytes: int, free_bytes: int, fraction: float = DS_WORKSPACE_FRACTION) -> bool:
+    """Path choice of backward(): share dS through a workspace (bf16 only) when
+    the workspace takes at most `fraction` of the free device memory, else
+    recompute dS in the dQ pass (no workspace)."""
+    return dtype_code == _lib.FA_DTYPE_BF16 and 0 < ws_bytes <= fraction * free_bytes
+
+
 def backward(q, k, v, o, do, lse, *, scale, causal=False, causal_offset=0, window=0, dropout_p=0.0,
-             seed=0, mask=None, share_ds=False):
+             seed=0, mask=None, share_ds=None):
     """Delta preprocess, then the dK/dV and dQ passes; returns (dq, dk, dv, delta).
 
-    share_ds (bf16): the dK/dV pass stores dS in a workspace and the dQ pass
-    reads it (fa_bwd_dkdv_ds, fa_bwd_dq_ds) instead of recomputing it."""
+    share_ds: None or True -- bf16 shares dS: the dK/dV pass stores it in a
+    workspace and the dQ pass reads it (fa_bwd_dkdv_ds, fa_bwd_dq_ds) instead of
+    recomputing it, as long as the workspace fits in DS_WORKSPACE_FRACTION of
+    the free device memory (use_shared_ds); otherwise, for fp32, or with
+    share_ds=False, both passes recompute (fa_bwd_dkdv, fa_bwd_dq)."""
     p = make_params(q, k, scale=scale, causal=causal, causal_offset=causal_offset, window=window,
                     dropout_p=dropout_p, seed=seed, mask=mask)
     _same_layout(q, o, do)
     delta = preprocess(p, o, do)
+    if share_ds is None or share_ds:
+        share_ds = p.dtype == _lib.FA_DTYPE_BF16 and use_shared_ds(
+            p.dtype, ds_workspace_bytes(p), torch.cuda.mem_get_info(q.device)[0])
     if share_ds:
         ws = ds_workspace(p, q.device)
         dk_, dv_ = dkdv_ds(p, q, k, v, do, lse, delta, ws)

@@ -6,6 +6,7 @@
 #include <math.h>
 
 #include "fa_bwd.h"
+#include "fa_bwd_calib.h"
 #include "fa_internal.h"
 
 namespace {

@@ -274,21 +274,6 @@ const char* fa_bwd_status_string(fa_status s);
 fa_status fa_bwd_debug_visibility(const fa_bwd_params* p, uint8_t* out, fa_stream_t stream);
 fa_status fa_bwd_debug_dropout_keep(const fa_bwd_params* p, uint8_t* out, fa_stream_t stream);
 
-/*
- * Calibration kernel for the MFMA roofline (not a step of the backward): the
- * bf16 MFMA rate the chip sustains on given operand data.  `blocks` workgroups
- * of 256 threads (one wave per SIMD) each issue iters x 32 back-to-back
- * v_mfma_f32_32x32x16_bf16 per wave, four independent accumulator chains,
- * operands rotating over four register blocks, nothing else in the loop.
- *   operands: device, 16-byte aligned, 2048 x 8 bf16 (32 KiB), read only
- *             (thread t: A blocks at [t + 256 i], B blocks at [1024 + t + 256 i]).
- *   sink:     device float [blocks * 256], written (keeps the work alive).
- * Work: blocks * 4 * iters * 32 * 32768 FLOP.  Errors: FA_ERR_NULL,
- * FA_ERR_ARG (blocks or iters <= 0), FA_ERR_ALIGN (operands).
- */
-fa_status fa_bwd_calib_mfma_bf16(const void* operands, float* sink, int32_t blocks, int32_t iters,
-                                 fa_stream_t stream);
-
 #ifdef __cplusplus
 }
 #endif

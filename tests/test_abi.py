@@ -16,13 +16,19 @@ from flashattention_backward_pass_bwd_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa_bwd.h")
+CALIB_HEADER = os.path.join(ROOT, "include", "fa_bwd_calib.h")  # the measurement hook, apart from the method
 
 pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libfa_bwd.so not built")
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(headers=(HEADER, CALIB_HEADER)):
+    text = "".join(open(h).read() for h in headers)
     return sorted(set(re.findall(r"^\s*(?:fa_status|int32_t|const char\*)\s+(fa_\w+)\s*\(", text, re.M)))
+
+
+def test_method_header_holds_only_the_method():
+    assert "fa_bwd_calib_mfma_bf16" not in _declared_functions((HEADER,))
+    assert _declared_functions((CALIB_HEADER,)) == ["fa_bwd_calib_mfma_bf16"]
 
 
 def test_header_declares_the_binding_surface():
