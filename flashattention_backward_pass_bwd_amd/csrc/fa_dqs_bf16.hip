@@ -19,28 +19,33 @@
 
 namespace fa {
 
-template <int D>
-__global__ __launch_bounds__(256, 1) void dqs_bf16_kernel(PrefillArgs a, const __bf16* __restrict__ K,
+// BK keys per step (64: half a workspace tile, one block per CU; 32: a
+// quarter, and a ring small enough for two blocks per CU, each hiding the
+// other's barrier waits).
+template <int D, int BK>
+__global__ __launch_bounds__(256, BK == 32 ? 2 : 1) void dqs_bf16_kernel(PrefillArgs a, const __bf16* __restrict__ K,
                                                           const unsigned char* __restrict__ ws,
                                                           __bf16* __restrict__ dQ, int nqt, int nchunk, int nkb) {
-  constexpr int BK = 64;               // keys per step: half a workspace tile
   constexpr int NCH = D / 8;           // 16-byte chunks per K row
   constexpr int DB = D / 32;           // 32-row blocks of dQ^T
   constexpr int NST = 3;               // ring stages
   constexpr int RPI = 1024 / (2 * D);  // K rows per 1 KB copy
   constexpr int NKC = BK / RPI / 4;    // K copies per wave per step
-  constexpr int NDC = 8;               // dS copies per wave per step (2 row halves x 4 KB)
+  constexpr int NG = BK / 32;          // 32-key groups per step
+  constexpr int NDC = 4 * NG;          // dS copies per wave per step (2 row halves x NG x 2 KB)
   constexpr int NC = NKC + NDC;
   constexpr int KT = BK * D;           // K elements of a stage
   constexpr int SH = BK * 32;          // dS elements of a row half of a wave's step
-  // A row half of a step is four 1 KB blocks (32-key group w', 16-row group t),
+  constexpr int JS = kWsKeys / BK;     // steps per workspace tile
+  static_assert(NKC >= 1 && (BK == 32 || BK == 64), "step width");
+  // A row half of a step is 2*NG 1 KB blocks (32-key group w', 16-row group t),
   // each copied as it is; in LDS the blocks sit 1152 bytes apart, so the two
   // row groups' blocks fall into different halves of the 64 banks.
   constexpr int SBLK = 576;            // elements from one block to the next in LDS
-  constexpr int SHP = 4 * SBLK;        // LDS elements of a row half of a wave's stage
-  static_assert(kWsRows == 64 && kWsKeys == 2 * BK && kWsTileBytes == 2 * 2 * SH * 2,
-                "a workspace tile is two steps of two row halves");
-  constexpr int NSLOT = 8 * DB;        // MFMAs per step and wave
+  constexpr int SHP = 2 * NG * SBLK;   // LDS elements of a row half of a wave's stage
+  static_assert(kWsRows == 64 && kWsKeys == JS * BK && kWsTileBytes == JS * 2 * SH * 2,
+                "a workspace tile is JS steps of two row halves");
+  constexpr int NSLOT = (BK / 16) * DB * 2;  // MFMAs per step and wave
   constexpr int CSP = 2 * NC <= NSLOT ? 2 : 1;  // MFMA slots per copy
   static_assert(NC * CSP <= NSLOT, "a step's copies fit its MFMA slots");
 
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(256, 1) void dqs_bf16_kernel(PrefillArgs a, const _
       tp += n;
     }
   }
-  const int nsteps = kb0 >= 0 ? 2 * (kb1 - kb0 + 1) : 0;
+  const int nsteps = kb0 >= 0 ? JS * (kb1 - kb0 + 1) : 0;
 
   // Copy cursor: the step whose copies go out next (held at the last step, so
   // the copies past the end repeat it into stages that are never read).
@@ -98,8 +103,8 @@ __global__ __launch_bounds__(256, 1) void dqs_bf16_kernel(PrefillArgs a, const _
   auto advance = [&](Cur& c) {
     if (c.s + 1 >= nsteps) return;
     ++c.s;
-    if (c.j == 0) {
-      c.j = 1;
+    if (c.j + 1 < JS) {
+      ++c.j;
     } else {
       c.tp += c.n;
       ++c.kb;
@@ -136,13 +141,13 @@ __global__ __launch_bounds__(256, 1) void dqs_bf16_kernel(PrefillArgs a, const _
                ws + tile * kWsTileBytes + c.j * (BK * 64), stage};
   };
   // Copy i of a job (0 .. NC-1): first the K rows, then the dS (row half
-  // i'/4, 1 KB part i'%4).
+  // i'/(2*NG), 1 KB part i'%(2*NG)).
   auto issue = [&](const Job& jb, int i) {
     if (i < NKC) {
       const uint32_t off = min(cp_off[i], jb.lim2 + cp_chk[i]);
       dma16(jb.kp, off, lds_addr(&sK[jb.stage][(wave * NKC + i) * RPI * D]));
     } else {
-      const int c = i - NKC, m = c >> 2, part = c & 3;
+      const int c = i - NKC, m = c / (2 * NG), part = c % (2 * NG);
       dma16_nt(jb.sp + m * 8192 + part * 1024, 16u * (uint32_t)lane,
                lds_addr(&sS[jb.stage][wave][m][part * SBLK]));
     }
@@ -244,13 +249,16 @@ __global__ __launch_bounds__(256, 1) void dqs_bf16_kernel(PrefillArgs a, const _
   }
 }
 
+#ifndef FA_DQS_BK
+#define FA_DQS_BK 32
+#endif
 template <int D>
 static hipError_t launch_t(const PrefillArgs& a, const void* K, const void* ws, void* dQ, hipStream_t st) {
   const int nqt = (a.Sq + kWsRows - 1) / kWsRows;
   const int nchunk = (a.group + 3) / 4;
   const int nkb = (a.Sk + kWsKeys - 1) / kWsKeys;
   const unsigned grid = (unsigned)(nqt * nchunk * a.B * a.Hkv);
-  hipLaunchKernelGGL((dqs_bf16_kernel<D>), dim3(grid), dim3(256), 0, st, a, static_cast<const __bf16*>(K),
+  hipLaunchKernelGGL((dqs_bf16_kernel<D, FA_DQS_BK>), dim3(grid), dim3(256), 0, st, a, static_cast<const __bf16*>(K),
                      static_cast<const unsigned char*>(ws), static_cast<__bf16*>(dQ), nqt, nchunk, nkb);
   return hipGetLastError();
 }
