@@ -8,11 +8,10 @@ inputs resident in HBM.  Prints ONE JSON line.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long|extras|causal_f32|decode|copy]
                   [--path shared_ds|recompute] [--no-cpu-baseline] [--no-mfma-ceiling] [--no-side-workloads]
 
-O and L (inputs of the backward) are produced once, before timing: for the
-bf16 workloads by the library's own forward (fa_fwd, parity-tested against the
-oracle forward), for the fp32 ones by a plain torch fp32 reference forward on
-the GPU (chunked QK^T / softmax / PV); they are inputs only, never part of the
-timed path (the forward is timed separately).  The cpu_baseline leg times the
+O and L (inputs of the backward) are produced once, before timing, by the
+library's own forward (fa_fwd, parity-tested against the oracle forward); they
+are inputs only, never part of the timed path (the forward is timed
+separately).  The cpu_baseline leg times the
 CPU fp64 oracle on one GQA group of the same workload.
 
 The default (long) run also times, in the same process and with the same
@@ -107,49 +106,6 @@ def _visible_pairs(w) -> int:
     return int(np.maximum(hi - lo, 0).sum())
 
 
-def _torch_reference_forward(q, k, v, w, mask=None, keep=None):
-    """O, L of the workload from plain torch fp32 ops on the GPU (input preparation only)."""
-    import torch
-
-    B, Sq, Hq, D = q.shape
-    Sk = k.shape[1]
-    g = w.num_heads // w.num_kv_heads
-    o = torch.empty_like(q)
-    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
-    inv = 1.0 / (1.0 - w.dropout_p) if w.dropout_p > 0 else 1.0
-    chunk = 2048
-    jj = torch.arange(Sk, device=q.device)
-    for b in range(B):
-        for h in range(Hq):
-            kf = k[b, :, h // g, :].float().contiguous()
-            vf = v[b, :, h // g, :].float().contiguous()
-            kt = kf.t().contiguous()
-            for r0 in range(0, Sq, chunk):
-                r1 = min(Sq, r0 + chunk)
-                qf = q[b, r0:r1, h, :].float().contiguous()
-                s = (qf @ kt) * w.scale
-                ii = torch.arange(r0, r1, device=q.device)[:, None] + w.causal_offset
-                vis = torch.ones_like(s, dtype=torch.bool)
-                if w.causal:
-                    vis &= jj[None, :] <= ii
-                if w.window > 0:
-                    vis &= (jj[None, :] - ii).abs() < w.window
-                if mask is not None:
-                    mv = mask[b, 0, r0:r1, :]
-                    vis &= mv > -1e30
-                    s = s + mv
-                s = torch.where(vis, s, torch.full_like(s, -float("inf")))
-                L = torch.logsumexp(s, dim=-1)
-                L = torch.where(torch.isfinite(L), L, torch.full_like(L, float("inf")))
-                p = torch.exp(s - L[:, None])
-                p = torch.where(vis, p, torch.zeros_like(p))
-                if keep is not None:
-                    p = p * keep[b, h, r0:r1, :].float() * inv
-                o[b, r0:r1, h, :] = (p @ vf).to(o.dtype)
-                lse[b, h, r0:r1] = L
-    return o, lse
-
-
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dkdv_bf16_long_traffic.txt")
 TRAFFIC_SOURCES = ["fa_dkdv_bf16.hip", "fa_tiles.h", "fa_common.h", "fa_internal.h"]
 
@@ -223,15 +179,9 @@ def _prepare(w):
     del inp
     p = api.make_params(q, k, scale=w.scale, causal=w.causal, causal_offset=w.causal_offset, window=w.window,
                         dropout_p=w.dropout_p, seed=w.dropout_seed, mask=mask)
-    if w.dtype == "bf16":
-        # O, L from the library's forward (parity-tested against the oracle)
-        _log(f"inputs of {w.name} on device; forward for O, L")
-        o, lse = api.forward(p, q, k, v)
-    else:
-        keep = api.debug_dropout_keep(p, dev) if w.dropout_p > 0 else None
-        _log(f"inputs of {w.name} on device; reference forward for O, L")
-        o, lse = _torch_reference_forward(q, k, v, w, mask, keep)
-        del keep
+    # O, L from the library's forward (parity-tested against the oracle forward)
+    _log(f"inputs of {w.name} on device; forward for O, L")
+    o, lse = api.forward(p, q, k, v)
     torch.cuda.synchronize()
     return {"q": q, "k": k, "v": v, "do": do, "mask": mask, "o": o, "lse": lse, "p": p, "dev": dev}
 
@@ -373,8 +323,7 @@ def bench_prefill(args, w):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": ("synthetic (seeded N(0,1) inputs; O, L from the library's forward)" if w.dtype == "bf16" else
-                 "synthetic (seeded N(0,1) inputs; O, L from a torch fp32 reference forward)"),
+        "data": "synthetic (seeded N(0,1) inputs; O, L from the library's forward)",
         "config": {"workload": w.name, "batch": w.batch, "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
                    "seq_q": w.seq_q, "seq_k": w.seq_k, "head_dim": w.head_dim, "layout": w.layout,
                    "causal": w.causal, "window": w.window, "mask_density": w.mask_density,
@@ -397,22 +346,21 @@ def bench_prefill(args, w):
                              "kernels_ms": {k_: round(v_, 4) for k_, v_ in okms.items()},
                              "ds_workspace_bytes": ows}
         _log(f"other path ({out['other_path']['path']}): {oms:.3f} ms/step")
-    if w.dtype == "bf16":
-        # the forward on the same inputs, timed on its own after the backward steps
-        for _ in range(2):
-            api.forward(p, q, k, v, o, lse)
-        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        f0.record()
-        for _ in range(args.steps):
-            api.forward(p, q, k, v, o, lse)
-        f1.record()
-        torch.cuda.synchronize()
-        fms = f0.elapsed_time(f1) / args.steps
-        ftf = 4.0 * w.head_dim * pairs / (fms * 1e-3) / 1e12
-        out["forward"] = {"kernel": "fwd_kernel", "what": "O, L (fa_fwd)", "ms": round(fms, 4), "bound": "mfma",
-                          "achieved": round(ftf, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(ftf / peak, 4),
-                          "per_unit": "4*D FLOP per visible (b,h,i,j) pair (QK^T and PV)", "units": pairs}
-        _log(f"forward: {fms:.3f} ms")
+    # the forward on the same inputs, timed on its own after the backward steps
+    for _ in range(2):
+        api.forward(p, q, k, v, o, lse)
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(args.steps):
+        api.forward(p, q, k, v, o, lse)
+    f1.record()
+    torch.cuda.synchronize()
+    fms = f0.elapsed_time(f1) / args.steps
+    ftf = 4.0 * w.head_dim * pairs / (fms * 1e-3) / 1e12
+    out["forward"] = {"kernel": "fwd_kernel", "what": "O, L (fa_fwd)", "ms": round(fms, 4), "bound": "mfma",
+                      "achieved": round(ftf, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(ftf / peak, 4),
+                      "per_unit": "4*D FLOP per visible (b,h,i,j) pair (QK^T and PV)", "units": pairs}
+    _log(f"forward: {fms:.3f} ms")
     if w.dtype == "bf16" and not args.no_mfma_ceiling:
         ceiling = _mfma_ceiling()
         out["roofline"]["mfma_ceiling"] = {

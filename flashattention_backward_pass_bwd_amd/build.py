@@ -29,6 +29,7 @@ SOURCES = [
     "fa_dq2_bf16.hip",
     "fa_dqs_bf16.hip",
     "fa_fwd_bf16.hip",
+    "fa_fwd.hip",
     "fa_decode.hip",
     "fa_decode_kv.hip",
     "fa_debug.hip",

@@ -231,10 +231,9 @@ fa_status fa_fwd(const fa_bwd_params* p, const void* Q, const void* K, const voi
   if (p == nullptr || Q == nullptr || K == nullptr || V == nullptr || O == nullptr || L == nullptr) return FA_ERR_NULL;
   fa_status s = check_prefill(p, &a);
   if (s != FA_OK) return s;
-  if (p->dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || (reinterpret_cast<uintptr_t>(L) & 3u))
     return FA_ERR_ALIGN;
-  return hip_status(fa::launch_fwd_bf16(a, p->head_dim, Q, K, V, O, L, as_stream(stream)));
+  return hip_status(fa::launch_fwd(a, p->dtype, p->head_dim, Q, K, V, O, L, as_stream(stream)));
 }
 
 fa_status fa_bwd_lse(const fa_bwd_params* p, const void* Q, const void* K, float* L, fa_stream_t stream) {
@@ -242,9 +241,8 @@ fa_status fa_bwd_lse(const fa_bwd_params* p, const void* Q, const void* K, float
   if (p == nullptr || Q == nullptr || K == nullptr || L == nullptr) return FA_ERR_NULL;
   fa_status s = check_prefill(p, &a);
   if (s != FA_OK) return s;
-  if (p->dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
   if (!aligned16(Q) || !aligned16(K) || (reinterpret_cast<uintptr_t>(L) & 3u)) return FA_ERR_ALIGN;
-  return hip_status(fa::launch_fwd_bf16(a, p->head_dim, Q, K, nullptr, nullptr, L, as_stream(stream)));
+  return hip_status(fa::launch_fwd(a, p->dtype, p->head_dim, Q, K, nullptr, nullptr, L, as_stream(stream)));
 }
 
 int32_t fa_bwd_decode_max_history(const fa_decode_params* p) {

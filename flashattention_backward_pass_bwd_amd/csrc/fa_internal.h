@@ -45,6 +45,9 @@ hipError_t launch_dkdv_bf16_ws(const PrefillArgs& a, int D, const void* Q, const
 hipError_t launch_dqs_bf16(const PrefillArgs& a, int D, const void* K, const void* ws, void* dQ, hipStream_t st);
 hipError_t launch_fwd_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V, void* O,
                            float* L, hipStream_t st);
+// The forward of either dtype (O == nullptr: L alone, V not read).
+hipError_t launch_fwd(const PrefillArgs& a, int dtype, int D, const void* Q, const void* K, const void* V, void* O,
+                      float* L, hipStream_t st);
 hipError_t launch_dq_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V,
                           const void* dO, const float* L, const float* delta, void* dQ, hipStream_t st);
 hipError_t launch_dq2_bf16(const PrefillArgs& a, const void* Q, const void* K, const void* V, const void* dO,

@@ -115,16 +115,15 @@ typedef struct fa_bwd_params {
 } fa_bwd_params;
 
 /*
- * Forward pass with the same conventions, bf16 only: the O and L the backward
- * takes ([wgsl-fa2] header: the forward whose outputs the two passes read,
- * its online log-sum-exp sweep; [metal-dq] L as an input).  With S_ij =
+ * Forward pass with the same conventions (bf16 or fp32): the O and L the
+ * backward takes ([wgsl-fa2] header: the forward whose outputs the two passes
+ * read, its online log-sum-exp sweep; [metal-dq] L as an input).  With S_ij =
  * scale * Q_i.K_j + mask_ij on counted (visible, unmasked) elements:
  *   L_i = ln sum_j exp(S_ij)  (+inf when no element of row i counts),
  *   O_i = sum_j exp(S_ij - L_i) M_ij V_j  (M the dropout multiplier; 0 rows
  *   when nothing counts).
  * Q, K, V, O as in fa_bwd_params (O shares Q's strides); L fp32, contiguous
- * [batch, num_heads, seq_q].  Errors as fa_bwd_dq, plus FA_ERR_UNSUPPORTED
- * for fp32.
+ * [batch, num_heads, seq_q].  Errors as fa_bwd_dq.
  */
 fa_status fa_fwd(const fa_bwd_params* p, const void* Q, const void* K, const void* V, void* O, float* L,
                  fa_stream_t stream);
@@ -132,8 +131,8 @@ fa_status fa_fwd(const fa_bwd_params* p, const void* Q, const void* K, const voi
 /*
  * L alone, for a caller whose forward did not keep it ([wgsl-fa2] the dQ
  * pass's first sweep: the online log-sum-exp of the scores): the L of fa_fwd
- * (dropout does not enter it), without reading V or writing O.  bf16 only;
- * errors as fa_fwd.
+ * (dropout does not enter it), without reading V or writing O.  bf16 or
+ * fp32; errors as fa_fwd.
  */
 fa_status fa_bwd_lse(const fa_bwd_params* p, const void* Q, const void* K, float* L, fa_stream_t stream);
 

@@ -252,8 +252,10 @@ def test_invalid_forward_arguments():
     assert L.fa_bwd_lse(P, FAKE, None, FAKE, None) == _lib.FA_ERR_NULL
     assert L.fa_bwd_lse(P, FAKE, odd, FAKE, None) == _lib.FA_ERR_ALIGN
     p.dtype = _lib.FA_DTYPE_F32
+    assert L.fa_fwd(P, None, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_NULL
+    assert L.fa_bwd_lse(P, FAKE, odd, FAKE, None) == _lib.FA_ERR_ALIGN
+    p.head_dim = 96
     assert L.fa_fwd(P, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_UNSUPPORTED
-    assert L.fa_bwd_lse(P, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_UNSUPPORTED
 
 
 def test_invalid_decode_pass2_arguments():
