@@ -28,7 +28,8 @@ fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
       p->head_dim <= 0)
     return FA_ERR_SHAPE;
   if (p->num_heads % p->num_kv_heads != 0) return FA_ERR_SHAPE;
-  if (p->head_dim != 64 && p->head_dim != 128) return FA_ERR_UNSUPPORTED;
+  // any multiple of 8 up to 128: tiles are 64 or 128 wide, the tail zero-padded
+  if (p->head_dim > 128 || p->head_dim % 8 != 0) return FA_ERR_UNSUPPORTED;
   if (p->seq_q > kMaxSeq || p->seq_k > kMaxSeq || p->causal_offset > kMaxSeq || p->window > kMaxSeq)
     return FA_ERR_UNSUPPORTED;
   if (p->causal != 0 && p->causal != 1) return FA_ERR_ARG;
@@ -72,6 +73,7 @@ fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
   a->Hkv = p->num_kv_heads;
   a->Sq = p->seq_q;
   a->Sk = p->seq_k;
+  a->D = p->head_dim;
   a->group = p->num_heads / p->num_kv_heads;
   a->qsb = p->q_stride_b;
   a->qss = p->q_stride_s;

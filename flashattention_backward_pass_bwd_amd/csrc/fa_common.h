@@ -21,6 +21,7 @@ constexpr float kMaskedSentinel = -1.0e30f;  // an additive mask entry <= this e
 // Everything a prefill kernel needs, resolved on the host (passed by value).
 struct PrefillArgs {
   int B, Hq, Hkv, Sq, Sk, group;  // group = Hq / Hkv
+  int D;                          // head_dim: a multiple of 8 up to the kernel's tile width (64 or 128)
   int64_t qsb, qss, qsh;          // element strides of Q, O, dO, dQ
   int64_t ksb, kss, ksh;          // element strides of K, V, dK, dV
   float scale;                    // softmax scale (applied to dQ and dK at the end)
@@ -122,6 +123,13 @@ __device__ __forceinline__ float strided_sum(float x) {
   if constexpr (M <= 32) x = halves_sum(x);
   return x;
 }
+
+// A head dimension below the tile width (64 or 128) is padded: a 16-byte
+// chunk c of a row with only n real chunks is read from chunk c mod n instead
+// (an address inside the row), and the operand it meets in the contraction
+// over d is zero there (register-held rows are zeroed past D), so the padding
+// adds exact zeros; outputs past D are not stored.
+__host__ __device__ __forceinline__ int pad_chunk(int c, int n) { return c < n ? c : c % n; }
 
 // Geometric visibility (ferrotensor-backend flash_attention_v2_backward.wgsl, fab2_visible).
 __device__ __forceinline__ bool visible(const PrefillArgs& a, int i, int j) {

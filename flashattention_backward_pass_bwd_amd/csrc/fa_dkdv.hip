@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __
   const int64_t koff = (int64_t)b * a.ksb + (int64_t)jl * a.kss + (int64_t)kvh * a.ksh;
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    if (jl < a.Sk) {
+    if (jl < a.Sk && 2 * CH * s + CH * h2 < a.D) {  // zero past the head dimension
       kr[s] = ld16<T>(K + koff + 2 * CH * s + CH * h2);
       vr[s] = ld16<T>(V + koff + 2 * CH * s + CH * h2);
     } else {
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __
         const int cc = c % (D / CH);
         const int i = qt + r;
         chunk qv{}, gv{};
-        if (i < a.Sq) {
+        if (i < a.Sq && cc * CH < a.D) {
           const int64_t off = (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh + cc * CH;
           qv = ld16<T>(Q + off);
           gv = ld16<T>(dO + off);
@@ -202,6 +202,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int dd = 32 * d + 8 * r4 + 4 * h2;
+        if (dd >= a.D) continue;  // past the head dimension
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           dK[koff + dd + e] = from_f32<T>(acck[d][4 * r4 + e] * a.scale);
@@ -241,7 +242,7 @@ hipError_t launch_dkdv(const PrefillArgs& a, int dtype, int D, const void* Q, co
                        const void* V, const void* dO, const float* L, const float* delta, void* dK,
                        void* dV, hipStream_t st) {
   if (dtype == kBF16) return launch_dkdv_bf16(a, D, Q, K, V, dO, L, delta, dK, dV, st);
-  return D == 64 ? launch_d<float, 64>(a, Q, K, V, dO, L, delta, dK, dV, st)
+  return D <= 64 ? launch_d<float, 64>(a, Q, K, V, dO, L, delta, dK, dV, st)
                  : launch_d<float, 128>(a, Q, K, V, dO, L, delta, dK, dV, st);
 }
 

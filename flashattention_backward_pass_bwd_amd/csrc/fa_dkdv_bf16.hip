@@ -134,8 +134,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     const int64_t kclamp = (int64_t)b * a.ksb + (int64_t)min(jl, a.Sk - 1) * a.kss + (int64_t)kvh * a.ksh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      kr[s] = ld16_agpr(K + kclamp + 16 * s + 8 * h2);
-      vr[s] = ld16_agpr(V + kclamp + 16 * s + 8 * h2);
+      kr[s] = ld16_agpr(row_chunk(K + kclamp, 2 * s + h2, a.D / 8));  // zero past the head dimension
+      vr[s] = ld16_agpr(row_chunk(V + kclamp, 2 * s + h2, a.D / 8));
     }
     f32x16 acck[DB], accv[DB];
 #pragma unroll
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
 #pragma unroll
       for (int i = 0; i < NIW; ++i) {
         const int r = (wave * NIW + i) * RPI + cp_row;
-        cp_chk[i] = 16u * (uint32_t)(cp_pc ^ swz<D>(r));
+        cp_chk[i] = 16u * (uint32_t)pad_chunk(cp_pc ^ swz<D>(r), a.D / 8);
         cp_off[i] = 2u * (uint32_t)r * (uint32_t)a.qss + cp_chk[i];
       }
       constexpr int NC = 2 * NIW;  // copies per tile per wave
@@ -742,6 +742,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int dd = 32 * d + 8 * r4 + 4 * h2;
+          if (dd >= a.D) continue;  // past the head dimension
           bf16x4 ok4, ov4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -786,14 +787,14 @@ static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, c
 hipError_t launch_dkdv_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V,
                             const void* dO, const float* L, const float* delta, void* dK, void* dV,
                             hipStream_t st) {
-  return D == 64 ? launch_d<64, false>(a, Q, K, V, dO, L, delta, dK, dV, nullptr, st)
+  return D <= 64 ? launch_d<64, false>(a, Q, K, V, dO, L, delta, dK, dV, nullptr, st)
                  : launch_d<128, false>(a, Q, K, V, dO, L, delta, dK, dV, nullptr, st);
 }
 
 hipError_t launch_dkdv_bf16_ws(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V,
                                const void* dO, const float* L, const float* delta, void* dK, void* dV, void* ws,
                                hipStream_t st) {
-  return D == 64 ? launch_d<64, true>(a, Q, K, V, dO, L, delta, dK, dV, ws, st)
+  return D <= 64 ? launch_d<64, true>(a, Q, K, V, dO, L, delta, dK, dV, ws, st)
                  : launch_d<128, true>(a, Q, K, V, dO, L, delta, dK, dV, ws, st);
 }
 

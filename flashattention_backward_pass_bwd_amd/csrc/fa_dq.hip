@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(PrefillArgs a, const T* __re
   const int64_t qoff = (int64_t)b * a.qsb + (int64_t)il * a.qss + (int64_t)h * a.qsh;
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    if (il < a.Sq) {
+    if (il < a.Sq && 2 * CH * s + CH * h2 < a.D) {  // zero past the head dimension
       qr[s] = ld16<T>(Q + qoff + 2 * CH * s + CH * h2);
       gr[s] = ld16<T>(dO + qoff + 2 * CH * s + CH * h2);
     } else {
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(PrefillArgs a, const T* __re
       const int cc = c % (D / CH);
       const int j = kt + r;
       chunk kv{}, vv{};
-      if (j < a.Sk) {
+      if (j < a.Sk && cc * CH < a.D) {
         const int64_t off = (int64_t)b * a.ksb + (int64_t)j * a.kss + (int64_t)kvh * a.ksh + cc * CH;
         kv = ld16<T>(K + off);
         vv = ld16<T>(V + off);
@@ -176,6 +176,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(PrefillArgs a, const T* __re
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int dd = 32 * d + 8 * r4 + 4 * h2;
+        if (dd >= a.D) continue;  // past the head dimension
 #pragma unroll
         for (int e = 0; e < 4; ++e) dQ[qoff + dd + e] = from_f32<T>(accq[d][4 * r4 + e] * a.scale);
       }
@@ -212,7 +213,7 @@ hipError_t launch_dq(const PrefillArgs& a, int dtype, int D, const void* Q, cons
                      const void* V, const void* dO, const float* L, const float* delta, void* dQ,
                      hipStream_t st) {
   if (dtype == kBF16) return launch_dq_bf16(a, D, Q, K, V, dO, L, delta, dQ, st);
-  return D == 64 ? launch_d<float, 64>(a, Q, K, V, dO, L, delta, dQ, st)
+  return D <= 64 ? launch_d<float, 64>(a, Q, K, V, dO, L, delta, dQ, st)
                  : launch_d<float, 128>(a, Q, K, V, dO, L, delta, dQ, st);
 }
 

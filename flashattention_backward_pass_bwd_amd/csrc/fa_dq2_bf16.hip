@@ -115,8 +115,8 @@ __global__ __launch_bounds__(256, 1) void dq2_bf16_kernel(PrefillArgs a, const _
       const int64_t qclamp = (int64_t)b * a.qsb + (int64_t)min(il[rb], a.Sq - 1) * a.qss + (int64_t)h * a.qsh;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        qr[rb][s] = ld16_agpr(Q + qclamp + 16 * s + 8 * h2);
-        gr[rb][s] = ld16_agpr(dO + qclamp + 16 * s + 8 * h2);
+        qr[rb][s] = ld16_agpr(row_chunk(Q + qclamp, 2 * s + h2, a.D / 8));  // zero past the head dimension
+        gr[rb][s] = ld16_agpr(row_chunk(dO + qclamp, 2 * s + h2, a.D / 8));
       }
       const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq + min(il[rb], a.Sq - 1);
       nl[rb] = il[rb] < a.Sq ? -L[lrow] * a.inv_scale : 0.f;  // rows past the end: never counted
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256, 1) void dq2_bf16_kernel(PrefillArgs a, const _
 #pragma unroll
       for (int i = 0; i < NIW; ++i) {
         const int r = (wave * NIW + i) * RPI + cp_row;
-        cp_chk[i] = 16u * (uint32_t)(cp_pc ^ swz<D>(r));
+        cp_chk[i] = 16u * (uint32_t)pad_chunk(cp_pc ^ swz<D>(r), a.D / 8);
         cp_off[i] = 2u * (uint32_t)r * (uint32_t)a.kss + cp_chk[i];
       }
       auto job_at = [&](int kt, int64_t base, int stage) {
@@ -423,6 +423,7 @@ __global__ __launch_bounds__(256, 1) void dq2_bf16_kernel(PrefillArgs a, const _
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const int dd = 32 * d + 8 * r4 + 4 * h2;
+            if (dd >= a.D) continue;  // past the head dimension
             bf16x4 o4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(accq[rb][d][4 * r4 + e] * a.scale);

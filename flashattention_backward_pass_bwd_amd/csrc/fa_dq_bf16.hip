@@ -142,8 +142,8 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
     const int64_t qclamp = (int64_t)b * a.qsb + (int64_t)min(il, a.Sq - 1) * a.qss + (int64_t)h * a.qsh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      qr[s] = ld16_agpr(Q + qclamp + 16 * s + 8 * h2);
-      gr[s] = ld16_agpr(dO + qclamp + 16 * s + 8 * h2);
+      qr[s] = ld16_agpr(row_chunk(Q + qclamp, 2 * s + h2, a.D / 8));  // zero past the head dimension
+      gr[s] = ld16_agpr(row_chunk(dO + qclamp, 2 * s + h2, a.D / 8));
     }
     const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq + min(il, a.Sq - 1);
     const float nl = il < a.Sq ? -L[lrow] * a.inv_scale : 0.f;  // rows past the end: never counted
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
 #pragma unroll
       for (int i = 0; i < NIW; ++i) {
         const int r = (wave * NIW + i) * RPI + cp_row;
-        cp_chk[i] = 16u * (uint32_t)(cp_pc ^ swz<D>(r));
+        cp_chk[i] = 16u * (uint32_t)pad_chunk(cp_pc ^ swz<D>(r), a.D / 8);
         cp_off[i] = 2u * (uint32_t)r * (uint32_t)a.kss + cp_chk[i];
       }
       // A job from a tile's first key and its element offset in K/V.
@@ -530,6 +530,7 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int dd = 32 * d + 8 * r4 + 4 * h2;
+          if (dd >= a.D) continue;  // past the head dimension
           bf16x4 o4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(accq[d][4 * r4 + e] * a.scale);
@@ -568,11 +569,12 @@ static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, c
 
 hipError_t launch_dq_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V,
                           const void* dO, const float* L, const float* delta, void* dQ, hipStream_t st) {
-  // Head dimension 128 without window, mask or dropout: two row blocks per wave
-  // (a window leaves its 256-row blocks more invisible key tiles than it saves).
-  if (D == 128 && a.window == 0 && a.mask == nullptr && a.drop == 0)
+  // Head dimension above 64 (tiles 128 wide) without window, mask or dropout:
+  // two row blocks per wave (a window leaves its 256-row blocks more invisible
+  // key tiles than it saves).
+  if (D > 64 && a.window == 0 && a.mask == nullptr && a.drop == 0)
     return launch_dq2_bf16(a, Q, K, V, dO, L, delta, dQ, st);
-  return D == 64 ? launch_d<64>(a, Q, K, V, dO, L, delta, dQ, st) : launch_d<128>(a, Q, K, V, dO, L, delta, dQ, st);
+  return D <= 64 ? launch_d<64>(a, Q, K, V, dO, L, delta, dQ, st) : launch_d<128>(a, Q, K, V, dO, L, delta, dQ, st);
 }
 
 }  // namespace fa

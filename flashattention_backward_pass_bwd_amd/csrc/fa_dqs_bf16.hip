@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256, BK == 32 ? 2 : 1) void dqs_bf16_kernel(Prefill
 #pragma unroll
   for (int u = 0; u < NKC; ++u) {
     const int r = (wave * NKC + u) * RPI + cp_row;
-    cp_chk[u] = 16u * (uint32_t)(cp_pc ^ swz<D>(r));
+    cp_chk[u] = 16u * (uint32_t)pad_chunk(cp_pc ^ swz<D>(r), a.D / 8);
     cp_off[u] = 2u * (uint32_t)r * (uint32_t)a.kss + cp_chk[u];
   }
   struct Job {
@@ -238,6 +238,7 @@ __global__ __launch_bounds__(256, BK == 32 ? 2 : 1) void dqs_bf16_kernel(Prefill
         for (int d = 0; d < DB; ++d) {
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
+            if (32 * d + 8 * r4 + 4 * h2 >= a.D) continue;  // past the head dimension
             bf16x4 o4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[2 * d + m][4 * r4 + e] * a.scale);
@@ -264,7 +265,7 @@ static hipError_t launch_t(const PrefillArgs& a, const void* K, const void* ws, 
 }
 
 hipError_t launch_dqs_bf16(const PrefillArgs& a, int D, const void* K, const void* ws, void* dQ, hipStream_t st) {
-  return D == 64 ? launch_t<64>(a, K, ws, dQ, st) : launch_t<128>(a, K, ws, dQ, st);
+  return D <= 64 ? launch_t<64>(a, K, ws, dQ, st) : launch_t<128>(a, K, ws, dQ, st);
 }
 
 }  // namespace fa

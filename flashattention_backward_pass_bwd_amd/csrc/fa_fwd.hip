@@ -61,7 +61,8 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(PrefillArgs a, const fl
   chunk qr[KS];
   const int64_t qoff = (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh;
 #pragma unroll
-  for (int s = 0; s < KS; ++s) qr[s] = i < a.Sq ? ld16<float>(Q + qoff + 2 * CH * s + CH * h2) : chunk{};
+  for (int s = 0; s < KS; ++s)  // zero past the head dimension
+    qr[s] = i < a.Sq && 2 * CH * s + CH * h2 < a.D ? ld16<float>(Q + qoff + 2 * CH * s + CH * h2) : chunk{};
   const uint32_t rkey = (DROP && WO) ? drop_row_key(a, b, h, i) : 0u;
 
   f32x16 acc[WO ? DB : 1];
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(PrefillArgs a, const fl
       const int cc = c % (D / CH);
       const int j = kt + r;
       chunk kv{}, vv{};
-      if (j < a.Sk) {
+      if (j < a.Sk && cc * CH < a.D) {
         const int64_t off = (int64_t)b * a.ksb + (int64_t)j * a.kss + (int64_t)kvh * a.ksh + cc * CH;
         kv = ld16<float>(K + off);
         if constexpr (WO) vv = ld16<float>(V + off);
@@ -179,6 +180,7 @@ __global__ __launch_bounds__(256, 1) void fwd_f32_kernel(PrefillArgs a, const fl
       for (int d = 0; d < DB; ++d) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
+          if (32 * d + 8 * r4 + 4 * h2 >= a.D) continue;  // past the head dimension
           f32x4 o4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) o4[e] = acc[d][4 * r4 + e] * inv;
@@ -218,7 +220,7 @@ static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, c
 hipError_t launch_fwd(const PrefillArgs& a, int dtype, int D, const void* Q, const void* K, const void* V, void* O,
                       float* L, hipStream_t st) {
   if (dtype == kBF16) return launch_fwd_bf16(a, D, Q, K, V, O, L, st);
-  return D == 64 ? launch_d<64>(a, Q, K, V, O, L, st) : launch_d<128>(a, Q, K, V, O, L, st);
+  return D <= 64 ? launch_d<64>(a, Q, K, V, O, L, st) : launch_d<128>(a, Q, K, V, O, L, st);
 }
 
 }  // namespace fa

@@ -65,7 +65,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
   bf16x8 qr[KS];
   const __bf16* qrow = Q + (int64_t)b * a.qsb + (int64_t)ic * a.qss + (int64_t)h * a.qsh;
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qr[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * h2);
+  for (int ks = 0; ks < KS; ++ks)  // zero past the head dimension
+    qr[ks] = 2 * ks + h2 < a.D / 8 ? *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * h2) : bf16x8{};
 
   int kb, ke;
   key_range(a, q0, min(q0 + kFwdRowsPerBlock, a.Sq) - 1, kb, ke);
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
 #pragma unroll
   for (int u = 0; u < NIW; ++u) {
     const int r = (wave * NIW + u) * RPI + lane / NCH;
-    cp_chk[u] = 16u * (uint32_t)((lane % NCH) ^ swz<D>(r));
+    cp_chk[u] = 16u * (uint32_t)pad_chunk((lane % NCH) ^ swz<D>(r), a.D / 8);
     cp_off[u] = 2u * (uint32_t)r * (uint32_t)a.kss + cp_chk[u];
   }
   auto issue = [&](int kt, int st) {  // the copies of the tile at key kt into stage st
@@ -227,6 +228,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
     for (int d = 0; d < (WO ? DB : 0); ++d) {
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
+        if (32 * d + 8 * r4 + 4 * h2 >= a.D) continue;  // past the head dimension
         bf16x4 o4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[d][4 * r4 + e] * inv);
@@ -267,7 +269,7 @@ static hipError_t launch_d(const PrefillArgs& a, const void* Q, const void* K, c
 // O == nullptr: L alone (V is not read).
 hipError_t launch_fwd_bf16(const PrefillArgs& a, int D, const void* Q, const void* K, const void* V, void* O,
                            float* L, hipStream_t st) {
-  return D == 64 ? launch_d<64>(a, Q, K, V, O, L, st) : launch_d<128>(a, Q, K, V, O, L, st);
+  return D <= 64 ? launch_d<64>(a, Q, K, V, O, L, st) : launch_d<128>(a, Q, K, V, O, L, st);
 }
 
 }  // namespace fa

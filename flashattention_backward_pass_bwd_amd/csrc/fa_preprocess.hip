@@ -19,7 +19,7 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PrefillArgs a, const T*
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
   float acc = 0.f;
-  if (row < rows) {
+  if (row < rows && lane_in_row * CH < a.D) {  // lanes past the head dimension add nothing
     const int i = (int)(row % a.Sq);
     const int64_t bh = row / a.Sq;
     const int h = (int)(bh % a.Hq);
@@ -47,8 +47,8 @@ static hipError_t launch(const PrefillArgs& a, const void* O, const void* dO, fl
 
 hipError_t launch_preprocess(const PrefillArgs& a, int dtype, int D, const void* O, const void* dO,
                              float* delta, hipStream_t st) {
-  if (dtype == kBF16) return D == 64 ? launch<__bf16, 64>(a, O, dO, delta, st) : launch<__bf16, 128>(a, O, dO, delta, st);
-  return D == 64 ? launch<float, 64>(a, O, dO, delta, st) : launch<float, 128>(a, O, dO, delta, st);
+  if (dtype == kBF16) return D <= 64 ? launch<__bf16, 64>(a, O, dO, delta, st) : launch<__bf16, 128>(a, O, dO, delta, st);
+  return D <= 64 ? launch<float, 64>(a, O, dO, delta, st) : launch<float, 128>(a, O, dO, delta, st);
 }
 
 }  // namespace fa

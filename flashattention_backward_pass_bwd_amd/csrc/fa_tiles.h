@@ -241,6 +241,16 @@ __device__ __forceinline__ void to_agpr(bf16x8& v) { asm volatile("" : "+a"(v));
 // stationary B operands), as inline assembly: the compiler neither copies the
 // value between register files nor waits for it; the caller waits with
 // wait_vmcnt before the first MFMA that reads it.
+// Sixteen zero bytes in device memory: a lane whose chunk of a register-held
+// row lies past a padded head dimension loads its operand from here.
+static __device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
+
+// Address of chunk c (8 bf16) of a row, or of the zero chunk when c is past the
+// row's n real chunks.
+__device__ __forceinline__ const void* row_chunk(const __bf16* row, int c, int n) {
+  return c < n ? static_cast<const void*>(row + 8 * c) : static_cast<const void*>(kZeroChunk);
+}
+
 __device__ __forceinline__ bf16x8 ld16_agpr(const void* p) {
   bf16x8 v;
   asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(v) : "v"(p) : "memory");

@@ -42,7 +42,8 @@ typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = -1,        /* a required pointer is NULL */
   FA_ERR_SHAPE = -2,       /* a size <= 0, or num_heads % num_kv_heads != 0 */
-  FA_ERR_UNSUPPORTED = -3, /* head_dim / dtype / history length / row stride outside the built kernels,
+  FA_ERR_UNSUPPORTED = -3, /* head_dim (prefill: not a multiple of 8 up to 128), dtype, history length or
+                              row stride outside the built kernels,
                               or seq_q, seq_k, causal_offset or window above 2^29 */
   FA_ERR_ALIGN = -4,       /* base or row stride not a multiple of 16 bytes, or D not unit-stride */
   FA_ERR_ARG = -5,         /* dropout_p not in [0,1), causal_offset < 0, window < 0, bad stride,
@@ -101,7 +102,7 @@ typedef struct fa_bwd_params {
   int32_t num_kv_heads; /* Hkv, divides Hq */
   int32_t seq_q;
   int32_t seq_k;
-  int32_t head_dim;     /* 64 or 128 */
+  int32_t head_dim;     /* any multiple of 8 up to 128 (tiles are 64 or 128 wide, the tail zero-padded) */
   int64_t q_stride_b, q_stride_s, q_stride_h;    /* elements; Q, O, dO, dQ */
   int64_t kv_stride_b, kv_stride_s, kv_stride_h; /* elements; K, V, dK, dV */
   float scale;           /* softmax scale; finite, nonzero, with a finite fp32 reciprocal (else FA_ERR_ARG) */

@@ -84,7 +84,6 @@ def _valid():
 FAKE = ctypes.c_void_p(4096)  # never dereferenced: every case below fails validation first
 
 BAD = [
-    ("head_dim", 96, _lib.FA_ERR_UNSUPPORTED),
     ("head_dim", 0, _lib.FA_ERR_SHAPE),
     ("dtype", 7, _lib.FA_ERR_UNSUPPORTED),
     ("batch", 0, _lib.FA_ERR_SHAPE),
@@ -100,6 +99,11 @@ BAD = [
     ("q_stride_s", 8 * 128 + 4, _lib.FA_ERR_ALIGN),
     ("kv_stride_h", 130, _lib.FA_ERR_ALIGN),
     ("q_stride_b", -1, _lib.FA_ERR_ARG),
+    # head_dim: any multiple of 8 up to 128
+    ("head_dim", 0, _lib.FA_ERR_SHAPE),
+    ("head_dim", 100, _lib.FA_ERR_UNSUPPORTED),
+    ("head_dim", 136, _lib.FA_ERR_UNSUPPORTED),
+    ("head_dim", 4, _lib.FA_ERR_UNSUPPORTED),
     # the score chains start from -L / scale: a zero, infinite, NaN or subnormal scale is rejected
     ("scale", 0.0, _lib.FA_ERR_ARG),
     ("scale", float("inf"), _lib.FA_ERR_ARG),
@@ -254,7 +258,7 @@ def test_invalid_forward_arguments():
     p.dtype = _lib.FA_DTYPE_F32
     assert L.fa_fwd(P, None, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_NULL
     assert L.fa_bwd_lse(P, FAKE, odd, FAKE, None) == _lib.FA_ERR_ALIGN
-    p.head_dim = 96
+    p.head_dim = 100  # not a multiple of 8
     assert L.fa_fwd(P, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_UNSUPPORTED
 
 
@@ -320,3 +324,21 @@ def test_status_strings():
         s = _lib.status_string(code)
         assert s.startswith("FA_")
     assert "unknown" in _lib.status_string(-99)
+
+
+@pytest.mark.parametrize("head_dim", [8, 16, 40, 72, 96, 120, 128])
+def test_general_head_dims_pass_validation(head_dim):
+    """Every multiple of 8 up to 128 passes the checks: a call with NULL data
+    pointers then stops at FA_ERR_NULL, never at FA_ERR_UNSUPPORTED."""
+    L = _lib.lib()
+    for dtype in (_lib.FA_DTYPE_BF16, _lib.FA_DTYPE_F32):
+        p = _valid()
+        p.dtype, p.head_dim = dtype, head_dim
+        p.q_stride_b, p.q_stride_s, p.q_stride_h = 100 * 8 * head_dim, 8 * head_dim, head_dim
+        p.kv_stride_b, p.kv_stride_s, p.kv_stride_h = 120 * 2 * head_dim, 2 * head_dim, head_dim
+        P = ctypes.byref(p)
+        assert L.fa_bwd_dkdv(P, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == _lib.FA_ERR_NULL
+        assert L.fa_bwd_dq(P, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == _lib.FA_ERR_NULL
+        assert L.fa_fwd(P, FAKE, FAKE, FAKE, None, FAKE, None) == _lib.FA_ERR_NULL
+        if dtype == _lib.FA_DTYPE_BF16:
+            assert _ws_bytes(L, p) > 0
