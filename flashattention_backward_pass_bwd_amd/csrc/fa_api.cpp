@@ -62,9 +62,10 @@ fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
       if (mask_rec > (int64_t)UINT32_MAX && p->dtype == FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     }
   }
-  // Grid sizes (the kernels index blocks with 32-bit integers).
-  const int64_t nq = (p->seq_q + fa::kDqRowsPerBlock - 1) / fa::kDqRowsPerBlock;
-  const int64_t nk = (p->seq_k + fa::kDkdvKeysPerBlock - 1) / fa::kDkdvKeysPerBlock;
+  // Grid sizes (the kernels index blocks with 32-bit integers; the smallest
+  // blocks, of the fp32 passes, hold 32 rows or 32 keys).
+  const int64_t nq = (p->seq_q + 31) / 32;
+  const int64_t nk = (p->seq_k + 31) / 32;
   if (nq * p->batch * p->num_heads >= (int64_t(1) << 31) || nk * p->batch * p->num_kv_heads >= (int64_t(1) << 31))
     return FA_ERR_UNSUPPORTED;
 

@@ -6,19 +6,34 @@
 //   P_ij = exp(S_ij - L_i) on counted elements (0 elsewhere),
 //   dS_ij = P_ij (M_ij dO_i.V_j - Delta_i).
 //
-// gfx950 design: a 256-thread block owns 128 keys of one (b, kvh); each of its
-// four waves keeps its 32 keys' K and V rows in registers as MFMA B operands
-// and accumulates dK^T, dV^T (D x 32, fp32) in registers.  The block streams
-// BQ-row tiles of Q and dO through LDS, stored row-major (A operand of
-// S = Q K^T and dP = dO V^T) and transposed (A operand of dV^T += dO^T (P.M)
-// and dK^T += Q^T dS).  S and dP come out of the MFMA in the C layout whose
-// per-lane column is a key, which is exactly the B-operand layout the second
-// pair of contractions needs, so P and dS never leave registers.
+// gfx950 design: a 256-thread block owns KG groups of 32 keys of one (b, kvh)
+// and streams RT-row tiles of Q and dO through LDS, stored row-major (A operand
+// of S = Q K^T and dP = dO V^T) and transposed (A operand of dV^T += dO^T (P.M)
+// and dK^T += Q^T dS).  Its four waves split the block as KG key groups x RS
+// row slices (KG * RS = 4, RT = 32 * RS): each wave keeps its 32 keys' K and V
+// rows in registers as MFMA B operands (v_mfma_f32_32x32x2_f32) and
+// accumulates dK^T, dV^T (D x 32, fp32) over its 32-row slice of every tile;
+// the RS partial sums of a key group are added through LDS at the end.
+// Splitting the rows of a key block over waves (instead of giving each wave
+// keys of its own) shortens the longest chain of tiles a wave walks -- under
+// causal attention the first keys see every row -- by RS and gives RS x as
+// many blocks, so small problems fill the chip.  S and dP come out of the MFMA
+// in the C layout whose per-lane column is a key, which is exactly the
+// B-operand layout the second pair of contractions needs, so P and dS never
+// leave registers.
 #include "fa_internal.h"
 
 namespace fa {
 
-template <typename T, int D, int BQ, bool MASK, bool DROP>
+template <int D>
+struct DkdvF32Shape {
+  static constexpr int KG = D <= 64 ? 1 : 2;  // 32-key groups per block
+  static constexpr int RS = 4 / KG;           // row slices per tile
+  static constexpr int RT = 32 * RS;          // rows per tile
+  static constexpr int KEYS = 32 * KG;        // keys per block
+};
+
+template <typename T, int D, bool MASK, bool DROP>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __restrict__ Q,
                                                       const T* __restrict__ K,
                                                       const T* __restrict__ V,
@@ -28,21 +43,28 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __
                                                       T* __restrict__ dK, T* __restrict__ dV) {
   using M = Mma<T>;
   using chunk = typename M::chunk;
+  using Sh = DkdvF32Shape<D>;
+  constexpr int RS = Sh::RS, RT = Sh::RT;
   constexpr int CH = M::CH;
-  constexpr int KS = D / (2 * CH);            // k-blocks of the head_dim contraction
+  constexpr int KS = D / (2 * CH);             // k-blocks of the head_dim contraction
   constexpr int PR = D + 16 / (int)sizeof(T);  // row-major LDS pitch (elements): +16 B per row
-  constexpr int PT = BQ + 4;                   // transposed LDS pitch (elements)
-  constexpr int MB = BQ / 32;                  // 32-row blocks in a Q tile
+  constexpr int PT = RT + 4;                   // transposed LDS pitch (elements)
   constexpr int TC = 16 / CH;                  // B-operand chunks per 32-row C block
   constexpr int DB = D / 32;                   // 32-row blocks of dK^T / dV^T
+  constexpr int NPART = 2 * DB * 16;           // partial-sum registers per lane (dK^T and dV^T)
+  static_assert(Sh::KG * RS == 4 && (2 * RT * PR + 2 * D * PT) * (int)sizeof(T) >= 4 * NPART * 64 * 4,
+                "the tile area holds every wave's partial sums");
 
-  __shared__ __attribute__((aligned(16))) T sQ[BQ * PR];
-  __shared__ __attribute__((aligned(16))) T sdO[BQ * PR];
-  __shared__ __attribute__((aligned(16))) T sQT[D * PT];
-  __shared__ __attribute__((aligned(16))) T sdOT[D * PT];
-  __shared__ float sL[BQ];
-  __shared__ float sDel[BQ];
-  __shared__ uint32_t sRK[DROP ? BQ : 1];
+  // Q, dO (row-major) and Q^T, dO^T of a tile; after the last tile, the waves'
+  // partial dK^T, dV^T.
+  __shared__ __attribute__((aligned(16))) T sTile[2 * RT * PR + 2 * D * PT];
+  T* const sQ = sTile;
+  T* const sdO = sTile + RT * PR;
+  T* const sQT = sTile + 2 * RT * PR;
+  T* const sdOT = sQT + D * PT;
+  __shared__ float sL[RT];
+  __shared__ float sDel[RT];
+  __shared__ uint32_t sRK[DROP ? RT : 1];
 
   const int nbh = a.B * a.Hkv;
   const int kb = blockIdx.x / nbh;  // ascending key block: longest causal work first
@@ -54,8 +76,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __
   const int lane = tid % 64;
   const int h2 = lane / 32;
   const int l32 = lane % 32;
-  const int k0 = kb * kDkdvKeysPerBlock;
-  const int kw0 = k0 + wave * kDkdvKeysPerWave;
+  const int kg = wave / RS;  // this wave's key group
+  const int rs = wave % RS;  // and its row slice of every tile
+  const int k0 = kb * Sh::KEYS;
+  const int kw0 = k0 + 32 * kg;
   const int jl = kw0 + l32;  // this lane's key (its C-layout column)
 
   chunk kr[KS], vr[KS];
@@ -79,14 +103,14 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __
   }
 
   int qb, qe;
-  query_range(a, k0, min(k0 + kDkdvKeysPerBlock, a.Sk) - 1, qb, qe);
+  query_range(a, k0, min(k0 + Sh::KEYS, a.Sk) - 1, qb, qe);
 
   for (int g = 0; g < a.group; ++g) {
     const int h = kvh * a.group + g;
     const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq;
-    for (int qt = qb; qt < qe; qt += BQ) {
+    for (int qt = qb; qt < qe; qt += RT) {
       __syncthreads();  // the previous tile has been consumed
-      for (int c = tid; c < BQ * (D / CH); c += 256) {
+      for (int c = tid; c < RT * (D / CH); c += 256) {
         const int r = c / (D / CH);
         const int cc = c % (D / CH);
         const int i = qt + r;
@@ -104,7 +128,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __
           sdOT[(cc * CH + e) * PT + r] = gv[e];
         }
       }
-      for (int r = tid; r < BQ; r += 256) {
+      for (int r = tid; r < RT; r += 256) {
         const int i = qt + r;
         const bool in = i < a.Sq;
         sL[r] = in ? L[lrow + i] * kLog2e : __builtin_inff();
@@ -113,87 +137,101 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __
       }
       __syncthreads();
 
-      if (rect_none_visible(a, qt, qt + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1)) continue;
-      const bool full = !MASK && !DROP && rect_all_visible(a, qt, qt + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1);
+      const int qw = qt + 32 * rs;  // this wave's 32 rows of the tile
+      if (rect_none_visible(a, qw, qw + 31, kw0, kw0 + 31)) continue;
+      const bool full = !MASK && !DROP && rect_all_visible(a, qw, qw + 31, kw0, kw0 + 31);
 
-      // S = Q K^T and dP = dO V^T for this wave's 32 keys (C column = key).
-      f32x16 s[MB], dp[MB];
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        s[m] = f32x16{};
-        dp[m] = f32x16{};
-      }
+      // S = Q K^T and dP = dO V^T for this wave's rows and keys (C column = key).
+      f32x16 s{}, dp{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          const int base = (32 * m + l32) * PR + 2 * CH * ks + CH * h2;
-          M::run(s[m], *reinterpret_cast<const chunk*>(&sQ[base]), kr[ks]);
-          M::run(dp[m], *reinterpret_cast<const chunk*>(&sdO[base]), vr[ks]);
-        }
+        const int base = (32 * rs + l32) * PR + 2 * CH * ks + CH * h2;
+        M::run(s, *reinterpret_cast<const chunk*>(&sQ[base]), kr[ks]);
+        M::run(dp, *reinterpret_cast<const chunk*>(&sdO[base]), vr[ks]);
       }
 
       // Elementwise: P, dropout, dS.  s <- P*M, dp <- dS.
 #pragma unroll
-      for (int m = 0; m < MB; ++m) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = 32 * m + 8 * (r / 4) + 4 * h2 + (r % 4);
-          const int i = qt + row;
-          const float l2 = sL[row];
-          float p;
-          if (full) {
-            p = __builtin_amdgcn_exp2f(s[m][r] * a.scale_log2 - l2);
-          } else {
-            bool ok = visible(a, i, jl);
-            float madd = 0.f;
-            if constexpr (MASK) {
-              if (ok) {
-                const float mv = mask_at(a, b, h, i, jl);
-                ok = !(mv <= kMaskedSentinel);
-                madd = mv * kLog2e;
-              }
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * rs + 8 * (r / 4) + 4 * h2 + (r % 4);
+        const int i = qt + row;
+        const float l2 = sL[row];
+        float p;
+        if (full) {
+          p = __builtin_amdgcn_exp2f(s[r] * a.scale_log2 - l2);
+        } else {
+          bool ok = visible(a, i, jl);
+          float madd = 0.f;
+          if constexpr (MASK) {
+            if (ok) {
+              const float mv = mask_at(a, b, h, i, jl);
+              ok = !(mv <= kMaskedSentinel);
+              madd = mv * kLog2e;
             }
-            p = ok ? __builtin_amdgcn_exp2f(s[m][r] * a.scale_log2 + madd - l2) : 0.f;
           }
-          float dpv = dp[m][r];
-          float pm = p;
-          if constexpr (DROP) {
-            const float mm = drop_keep(sRK[row], jl, a.drop_thr) ? a.drop_inv : 0.f;
-            dpv *= mm;
-            pm = p * mm;
-          }
-          dp[m][r] = p * (dpv - sDel[row]);
-          s[m][r] = pm;
+          p = ok ? __builtin_amdgcn_exp2f(s[r] * a.scale_log2 + madd - l2) : 0.f;
         }
+        float dpv = dp[r];
+        float pm = p;
+        if constexpr (DROP) {
+          const float mm = drop_keep(sRK[row], jl, a.drop_thr) ? a.drop_inv : 0.f;
+          dpv *= mm;
+          pm = p * mm;
+        }
+        dp[r] = p * (dpv - sDel[row]);
+        s[r] = pm;
       }
 
-      // dV^T += dO^T (P.M),  dK^T += Q^T dS  (contraction over the tile's queries).
+      // dV^T += dO^T (P.M),  dK^T += Q^T dS  (contraction over the wave's rows).
 #pragma unroll
-      for (int m = 0; m < MB; ++m) {
+      for (int t = 0; t < TC; ++t) {
+        const chunk pmc = M::from_acc(s, t * CH);
+        const chunk dsc = M::from_acc(dp, t * CH);
 #pragma unroll
-        for (int t = 0; t < TC; ++t) {
-          const chunk pmc = M::from_acc(s[m], t * CH);
-          const chunk dsc = M::from_acc(dp[m], t * CH);
+        for (int d = 0; d < DB; ++d) {
+          const int trow = (32 * d + l32) * PT;
+          chunk ao, aq;
 #pragma unroll
-          for (int d = 0; d < DB; ++d) {
-            const int trow = (32 * d + l32) * PT;
-            chunk ao, aq;
+          for (int sg = 0; sg < CH / 4; ++sg) {
+            const int q = 32 * rs + 8 * ((CH / 4) * t + sg) + 4 * h2;
 #pragma unroll
-            for (int sg = 0; sg < CH / 4; ++sg) {
-              const int q = 32 * m + 8 * ((CH / 4) * t + sg) + 4 * h2;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                ao[4 * sg + e] = sdOT[trow + q + e];
-                aq[4 * sg + e] = sQT[trow + q + e];
-              }
+            for (int e = 0; e < 4; ++e) {
+              ao[4 * sg + e] = sdOT[trow + q + e];
+              aq[4 * sg + e] = sQT[trow + q + e];
             }
-            M::run(accv[d], ao, pmc);
-            M::run(acck[d], aq, dsc);
           }
+          M::run(accv[d], ao, pmc);
+          M::run(acck[d], aq, dsc);
         }
       }
     }
+  }
+
+  // Sum the row slices' partial dK^T, dV^T of each key group through LDS:
+  // register n of lane l of wave w at sPart[(w * NPART + n) * 64 + l].
+  __syncthreads();  // every wave is done with the tiles
+  float* const sPart = reinterpret_cast<float*>(sTile);
+  if (rs != 0) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sPart[(wave * NPART + 32 * d + r) * 64 + lane] = acck[d][r];
+        sPart[(wave * NPART + 32 * d + 16 + r) * 64 + lane] = accv[d][r];
+      }
+  }
+  __syncthreads();
+  if (rs != 0) return;
+#pragma unroll
+  for (int o = 1; o < RS; ++o) {
+    const int w = wave + o;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acck[d][r] += sPart[(w * NPART + 32 * d + r) * 64 + lane];
+        accv[d][r] += sPart[(w * NPART + 32 * d + 16 + r) * 64 + lane];
+      }
   }
 
   if (jl < a.Sk) {
@@ -217,10 +255,9 @@ template <typename T, int D, bool MASK, bool DROP>
 static hipError_t launch_t(const PrefillArgs& a, const void* Q, const void* K, const void* V,
                            const void* dO, const float* L, const float* delta, void* dK, void* dV,
                            hipStream_t st) {
-  constexpr int BQ = 64;
-  const int nkb = (a.Sk + kDkdvKeysPerBlock - 1) / kDkdvKeysPerBlock;
-  const unsigned grid = (unsigned)(nkb * a.B * a.Hkv);
-  hipLaunchKernelGGL((dkdv_kernel<T, D, BQ, MASK, DROP>), dim3(grid), dim3(256), 0, st, a,
+  const int nkb = (a.Sk + DkdvF32Shape<D>::KEYS - 1) / DkdvF32Shape<D>::KEYS;
+  const unsigned grid = (unsigned)((int64_t)nkb * a.B * a.Hkv);
+  hipLaunchKernelGGL((dkdv_kernel<T, D, MASK, DROP>), dim3(grid), dim3(256), 0, st, a,
                      static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
                      static_cast<const T*>(dO), L, delta, static_cast<T*>(dK), static_cast<T*>(dV));
   return hipGetLastError();

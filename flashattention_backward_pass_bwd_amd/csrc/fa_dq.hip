@@ -4,18 +4,32 @@
 //   dQ_i = scale * sum_j dS_ij K_j,  dS_ij = P_ij (M_ij dO_i.V_j - Delta_i),
 //   P_ij = exp(S_ij - L_i) on counted elements, 0 elsewhere.
 //
-// gfx950 design: a 256-thread block owns 128 query rows of one (b, h); each
-// wave keeps its 32 rows of Q and dO in registers as MFMA B operands and
-// accumulates dQ^T (D x 32, fp32).  The block streams BK-key tiles of K and V
-// through LDS (row-major: A operand of S^T = K Q^T and dP^T = V dO^T; K also
-// transposed: A operand of dQ^T += K^T dS^T).  S^T comes out of the MFMA with
-// one query per lane column, so dS^T is already the B operand of the last
+// gfx950 design: a 256-thread block owns RG groups of 32 query rows of one
+// (b, h) and streams BK-key tiles of K and V through LDS (row-major: A operand
+// of S^T = K Q^T and dP^T = V dO^T; K also transposed: A operand of
+// dQ^T += K^T dS^T).  Its four waves split the block as RG row groups x KSL key
+// slices (RG * KSL = 4, BK = 32 * KSL): each wave keeps its 32 rows of Q and dO
+// in registers as MFMA B operands (v_mfma_f32_32x32x2_f32) and accumulates
+// dQ^T (D x 32, fp32) over its 32-key slice of every tile; the KSL partial
+// sums of a row group are added through LDS at the end.  Splitting the keys of
+// a row block over waves shortens the longest chain of tiles a wave walks --
+// under causal attention the last rows see every key -- by KSL and gives KSL x
+// as many blocks, so small problems fill the chip.  S^T comes out of the MFMA
+// with one query per lane column, so dS^T is already the B operand of the last
 // contraction and L_i, Delta_i are per-lane scalars.
 #include "fa_internal.h"
 
 namespace fa {
 
-template <typename T, int D, int BK, bool MASK, bool DROP>
+template <int D>
+struct DqF32Shape {
+  static constexpr int RG = D <= 64 ? 1 : 2;  // 32-row groups per block
+  static constexpr int KSL = 4 / RG;          // key slices per tile
+  static constexpr int BK = 32 * KSL;         // keys per tile
+  static constexpr int ROWS = 32 * RG;        // query rows per block
+};
+
+template <typename T, int D, bool MASK, bool DROP>
 __global__ __launch_bounds__(256, 1) void dq_kernel(PrefillArgs a, const T* __restrict__ Q,
                                                     const T* __restrict__ K,
                                                     const T* __restrict__ V,
@@ -25,20 +39,26 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(PrefillArgs a, const T* __re
                                                     T* __restrict__ dQ) {
   using M = Mma<T>;
   using chunk = typename M::chunk;
+  using Sh = DqF32Shape<D>;
+  constexpr int KSL = Sh::KSL, BK = Sh::BK;
   constexpr int CH = M::CH;
   constexpr int KS = D / (2 * CH);
   constexpr int PR = D + 16 / (int)sizeof(T);
   constexpr int PT = BK + 4;
-  constexpr int MB = BK / 32;
   constexpr int TC = 16 / CH;
   constexpr int DB = D / 32;
+  constexpr int NPART = DB * 16;  // partial-sum registers per lane (dQ^T)
+  static_assert(Sh::RG * KSL == 4 && (2 * BK * PR + D * PT) * (int)sizeof(T) >= 4 * NPART * 64 * 4,
+                "the tile area holds every wave's partial sums");
 
-  __shared__ __attribute__((aligned(16))) T sK[BK * PR];
-  __shared__ __attribute__((aligned(16))) T sV[BK * PR];
-  __shared__ __attribute__((aligned(16))) T sKT[D * PT];
+  // K, V (row-major) and K^T of a tile; after the last tile, the waves' partial dQ^T.
+  __shared__ __attribute__((aligned(16))) T sTile[2 * BK * PR + D * PT];
+  T* const sK = sTile;
+  T* const sV = sTile + BK * PR;
+  T* const sKT = sTile + 2 * BK * PR;
 
   const int nbh = a.B * a.Hq;
-  const int nqb = (a.Sq + kDqRowsPerBlock - 1) / kDqRowsPerBlock;
+  const int nqb = (a.Sq + Sh::ROWS - 1) / Sh::ROWS;
   const int qbi = nqb - 1 - (int)(blockIdx.x / nbh);  // last query block first: longest causal work
   // Consecutive blocks cycle over KV heads first, so the query heads of one
   // KV head land on the same XCD (blocks are dealt round-robin over XCDs).
@@ -54,8 +74,10 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(PrefillArgs a, const T* __re
   const int lane = tid % 64;
   const int h2 = lane / 32;
   const int l32 = lane % 32;
-  const int q0 = qbi * kDqRowsPerBlock;
-  const int qw0 = q0 + wave * kDqRowsPerWave;
+  const int rg = wave / KSL;  // this wave's row group
+  const int ksl = wave % KSL; // and its key slice of every tile
+  const int q0 = qbi * Sh::ROWS;
+  const int qw0 = q0 + 32 * rg;
   const int il = qw0 + l32;  // this lane's query row (its C-layout column)
 
   chunk qr[KS], gr[KS];
@@ -81,7 +103,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(PrefillArgs a, const T* __re
   for (int d = 0; d < DB; ++d) accq[d] = f32x16{};
 
   int kb, ke;
-  key_range(a, q0, min(q0 + kDqRowsPerBlock, a.Sq) - 1, kb, ke);
+  key_range(a, q0, min(q0 + Sh::ROWS, a.Sq) - 1, kb, ke);
 
   for (int kt = kb; kt < ke; kt += BK) {
     __syncthreads();
@@ -102,72 +124,79 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(PrefillArgs a, const T* __re
     }
     __syncthreads();
 
-    if (rect_none_visible(a, qw0, qw0 + kDqRowsPerWave - 1, kt, kt + BK - 1)) continue;
-    const bool full = !MASK && !DROP && rect_all_visible(a, qw0, qw0 + kDqRowsPerWave - 1, kt, kt + BK - 1);
+    const int kw = kt + 32 * ksl;  // this wave's 32 keys of the tile
+    if (rect_none_visible(a, qw0, qw0 + 31, kw, kw + 31)) continue;
+    const bool full = !MASK && !DROP && rect_all_visible(a, qw0, qw0 + 31, kw, kw + 31);
 
     // S^T = K Q^T, dP^T = V dO^T (C column = query).
-    f32x16 st[MB], dpt[MB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      st[m] = f32x16{};
-      dpt[m] = f32x16{};
-    }
+    f32x16 st{}, dpt{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        const int base = (32 * m + l32) * PR + 2 * CH * ks + CH * h2;
-        M::run(st[m], *reinterpret_cast<const chunk*>(&sK[base]), qr[ks]);
-        M::run(dpt[m], *reinterpret_cast<const chunk*>(&sV[base]), gr[ks]);
-      }
+      const int base = (32 * ksl + l32) * PR + 2 * CH * ks + CH * h2;
+      M::run(st, *reinterpret_cast<const chunk*>(&sK[base]), qr[ks]);
+      M::run(dpt, *reinterpret_cast<const chunk*>(&sV[base]), gr[ks]);
     }
 
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = kt + 32 * m + 8 * (r / 4) + 4 * h2 + (r % 4);
-        float p;
-        if (full) {
-          p = __builtin_amdgcn_exp2f(st[m][r] * a.scale_log2 - l2);
-        } else {
-          bool ok = visible(a, il, j);
-          float madd = 0.f;
-          if constexpr (MASK) {
-            if (ok) {
-              const float mv = mask_at(a, b, h, il, j);
-              ok = !(mv <= kMaskedSentinel);
-              madd = mv * kLog2e;
-            }
+    for (int r = 0; r < 16; ++r) {
+      const int j = kw + 8 * (r / 4) + 4 * h2 + (r % 4);
+      float p;
+      if (full) {
+        p = __builtin_amdgcn_exp2f(st[r] * a.scale_log2 - l2);
+      } else {
+        bool ok = visible(a, il, j);
+        float madd = 0.f;
+        if constexpr (MASK) {
+          if (ok) {
+            const float mv = mask_at(a, b, h, il, j);
+            ok = !(mv <= kMaskedSentinel);
+            madd = mv * kLog2e;
           }
-          p = ok ? __builtin_amdgcn_exp2f(st[m][r] * a.scale_log2 + madd - l2) : 0.f;
         }
-        float dpv = dpt[m][r];
-        if constexpr (DROP) dpv *= drop_keep(rk, j, a.drop_thr) ? a.drop_inv : 0.f;
-        dpt[m][r] = p * (dpv - del);
+        p = ok ? __builtin_amdgcn_exp2f(st[r] * a.scale_log2 + madd - l2) : 0.f;
       }
+      float dpv = dpt[r];
+      if constexpr (DROP) dpv *= drop_keep(rk, j, a.drop_thr) ? a.drop_inv : 0.f;
+      dpt[r] = p * (dpv - del);
     }
 
-    // dQ^T += K^T dS^T (contraction over the tile's keys).
+    // dQ^T += K^T dS^T (contraction over the wave's keys).
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
+    for (int t = 0; t < TC; ++t) {
+      const chunk dsc = M::from_acc(dpt, t * CH);
 #pragma unroll
-      for (int t = 0; t < TC; ++t) {
-        const chunk dsc = M::from_acc(dpt[m], t * CH);
+      for (int d = 0; d < DB; ++d) {
+        const int trow = (32 * d + l32) * PT;
+        chunk ak;
 #pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          const int trow = (32 * d + l32) * PT;
-          chunk ak;
+        for (int sg = 0; sg < CH / 4; ++sg) {
+          const int kk = 32 * ksl + 8 * ((CH / 4) * t + sg) + 4 * h2;
 #pragma unroll
-          for (int sg = 0; sg < CH / 4; ++sg) {
-            const int kk = 32 * m + 8 * ((CH / 4) * t + sg) + 4 * h2;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ak[4 * sg + e] = sKT[trow + kk + e];
-          }
-          M::run(accq[d], ak, dsc);
+          for (int e = 0; e < 4; ++e) ak[4 * sg + e] = sKT[trow + kk + e];
         }
+        M::run(accq[d], ak, dsc);
       }
     }
+  }
+
+  // Sum the key slices' partial dQ^T of each row group through LDS: register n
+  // of lane l of wave w at sPart[(w * NPART + n) * 64 + l].
+  __syncthreads();  // every wave is done with the tiles
+  float* const sPart = reinterpret_cast<float*>(sTile);
+  if (ksl != 0) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sPart[(wave * NPART + 16 * d + r) * 64 + lane] = accq[d][r];
+  }
+  __syncthreads();
+  if (ksl != 0) return;
+#pragma unroll
+  for (int o = 1; o < KSL; ++o) {
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) accq[d][r] += sPart[((wave + o) * NPART + 16 * d + r) * 64 + lane];
   }
 
   if (il < a.Sq) {
@@ -188,10 +217,9 @@ template <typename T, int D, bool MASK, bool DROP>
 static hipError_t launch_t(const PrefillArgs& a, const void* Q, const void* K, const void* V,
                            const void* dO, const float* L, const float* delta, void* dQ,
                            hipStream_t st) {
-  constexpr int BK = 64;
-  const int nqb = (a.Sq + kDqRowsPerBlock - 1) / kDqRowsPerBlock;
-  const unsigned grid = (unsigned)(nqb * a.B * a.Hq);
-  hipLaunchKernelGGL((dq_kernel<T, D, BK, MASK, DROP>), dim3(grid), dim3(256), 0, st, a,
+  const int nqb = (a.Sq + DqF32Shape<D>::ROWS - 1) / DqF32Shape<D>::ROWS;
+  const unsigned grid = (unsigned)((int64_t)nqb * a.B * a.Hq);
+  hipLaunchKernelGGL((dq_kernel<T, D, MASK, DROP>), dim3(grid), dim3(256), 0, st, a,
                      static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
                      static_cast<const T*>(dO), L, delta, static_cast<T*>(dQ));
   return hipGetLastError();
