@@ -3,10 +3,15 @@
 // ferrotensor-backend flash_attention_v2_backward.wgsl, pass-1 Delta).
 //
 // HBM-bound: each row is read once as 16-byte chunks by a group of lanes,
-// multiplied in fp32 and reduced across the group with DPP lane moves.
+// multiplied in fp32 and reduced across the group with DPP lane moves; a lane
+// group takes several rows, their loads in flight together.
 #include "fa_internal.h"
 
 namespace fa {
+
+// Each group of LPR lanes reduces RPG rows (RPG loads of O and of dO in flight
+// per lane before the first sum), so a block covers RPG * 256 / LPR rows.
+constexpr int kPreRowsPerGroup = 4;
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void preprocess_kernel(PrefillArgs a, const T* __restrict__ O,
@@ -14,30 +19,44 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PrefillArgs a, const T*
                                                          float* __restrict__ delta) {
   constexpr int CH = Mma<T>::CH;          // elements per 16-byte chunk
   constexpr int LPR = D / CH;             // lanes per row
-  constexpr int RPB = 256 / LPR;          // rows per block
+  constexpr int GPB = 256 / LPR;          // lane groups per block
+  constexpr int RPG = kPreRowsPerGroup;   // rows per lane group
   const int lane_in_row = threadIdx.x % LPR;
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / LPR;
-  float acc = 0.f;
-  if (row < rows && lane_in_row * CH < a.D) {  // lanes past the head dimension add nothing
-    const int i = (int)(row % a.Sq);
-    const int64_t bh = row / a.Sq;
-    const int h = (int)(bh % a.Hq);
-    const int b = (int)(bh / a.Hq);
-    const int64_t off = (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh + lane_in_row * CH;
-    const auto o = ld16<T>(O + off);
-    const auto g = ld16<T>(dO + off);
+  // group g of block k takes rows (k * RPG + u) * GPB + g, u = 0 .. RPG-1
+  const int64_t row0 = (int64_t)blockIdx.x * RPG * GPB + threadIdx.x / LPR;
+  const bool lane_in = lane_in_row * CH < a.D;  // lanes past the head dimension add nothing
+  typename Mma<T>::chunk o[RPG], g[RPG];
 #pragma unroll
-    for (int e = 0; e < CH; ++e) acc += to_f32(g[e]) * to_f32(o[e]);
+  for (int u = 0; u < RPG; ++u) {
+    const int64_t row = row0 + (int64_t)u * GPB;
+    o[u] = typename Mma<T>::chunk{};
+    g[u] = typename Mma<T>::chunk{};
+    if (row < rows && lane_in) {
+      const int i = (int)(row % a.Sq);
+      const int64_t bh = row / a.Sq;
+      const int h = (int)(bh % a.Hq);
+      const int b = (int)(bh / a.Hq);
+      const int64_t off = (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh + lane_in_row * CH;
+      o[u] = ld16<T>(O + off);
+      g[u] = ld16<T>(dO + off);
+    }
   }
-  acc = group_sum<LPR>(acc);
-  if (row < rows && lane_in_row == 0) delta[row] = acc;
+#pragma unroll
+  for (int u = 0; u < RPG; ++u) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < CH; ++e) acc += to_f32(g[u][e]) * to_f32(o[u][e]);
+    acc = group_sum<LPR>(acc);
+    const int64_t row = row0 + (int64_t)u * GPB;
+    if (row < rows && lane_in_row == 0) delta[row] = acc;
+  }
 }
 
 template <typename T, int D>
 static hipError_t launch(const PrefillArgs& a, const void* O, const void* dO, float* delta, hipStream_t st) {
   constexpr int LPR = D / Mma<T>::CH;
-  constexpr int RPB = 256 / LPR;
+  constexpr int RPB = kPreRowsPerGroup * 256 / LPR;  // rows per block
   const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
   const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
   hipLaunchKernelGGL((preprocess_kernel<T, D>), dim3(grid), dim3(256), 0, st, a,
