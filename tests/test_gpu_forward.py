@@ -97,7 +97,7 @@ def test_forward_full_size_sampled(which):
 
 
 @pytest.mark.parametrize("head_dim", [64, 128])
-@pytest.mark.parametrize("layout", ["per_head", "key_major", "key_padding"])
+@pytest.mark.parametrize("layout", ["per_head", "key_major", "key_padding", "padded_rows"])
 def test_forward_mask_layouts(layout, head_dim):
     """The mask layouts of the backward's tests (one mask per head with finite
     values, a key-major copy, a key-padding row broadcast over queries) with a
@@ -115,9 +115,18 @@ def test_forward_mask_layouts(layout, head_dim):
         m = np.where(rng.random((B, 1, Sq, Sk)) < 0.1, -1e30, 0.0).astype(np.float32)
         inp["mask"] = m
         mask_dev = torch.from_numpy(np.ascontiguousarray(m.transpose(0, 1, 3, 2))).cuda().transpose(2, 3)
-    else:
+    elif layout == "key_padding":
         m = np.where(rng.random((B, 1, 1, Sk)) < 0.15, -1e30, 0.0).astype(np.float32)
         inp["mask"] = m
         mask_dev = torch.from_numpy(m).cuda()
+    else:
+        # [B, 1, Sq, Sk] stored in rows padded to a multiple of 4 keys: 16-byte aligned rows (the
+        # vector mask paths) with a ragged last group of keys
+        m = np.where(rng.random((B, 1, Sq, Sk)) < 0.1, -1e30, 0.0).astype(np.float32)
+        inp["mask"] = m
+        full = torch.zeros((B, 1, Sq, (Sk + 3) // 4 * 4), dtype=torch.float32)
+        full[..., :Sk] = torch.from_numpy(m)
+        mask_dev = full.cuda()[..., :Sk]
+        assert mask_dev.stride(2) % 4 == 0 and Sk % 4 != 0
     say(f"[forward mask layout] {layout} D={head_dim}")
     _check(w, inp, mask_dev)

@@ -83,6 +83,8 @@ def test_long_workload_full_size_sampled():
     w = synth.LONG_BF16
     S = w.seq_q
     rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([[0, 1, 127, 128, 8191, S - 2, S - 1], rng.integers(0, S, 57)]))
-    keys = np.unique(np.concatenate([[0, 1, 127, 128, 8192, S - 2, S - 1], rng.integers(0, S, 57)]))
-    _run_checked(w, checked=[(0, 0), (0, 31)], rows=rows, keys=keys)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 8191, S - 2, S - 1], rng.integers(0, S, 249)]))
+    keys = np.unique(np.concatenate([[0, 1, 127, 128, 8192, S - 2, S - 1], rng.integers(0, S, 249)]))
+    # one checked head in every KV head, at every position within a group; every other head zero
+    _run_checked(w, checked=[(0, 0), (0, 5), (0, 10), (0, 15), (0, 16), (0, 21), (0, 26), (0, 31)], rows=rows,
+                 keys=keys)

@@ -181,7 +181,7 @@ def test_dropout_zero_is_no_dropout_bitwise():
 
 
 @pytest.mark.parametrize("head_dim", [64, 128])
-@pytest.mark.parametrize("layout", ["per_head", "key_major", "key_padding"])
+@pytest.mark.parametrize("layout", ["per_head", "key_major", "key_padding", "padded_rows"])
 def test_mask_layouts_bf16(layout, head_dim):
     """Masks with other strides than [B, 1, Sq, Sk] row-major: one mask per head,
     a key-major copy (key stride Sq), and a key-padding mask broadcast over rows
@@ -200,10 +200,19 @@ def test_mask_layouts_bf16(layout, head_dim):
         inp["mask"] = m
         mask_dev = torch.from_numpy(np.ascontiguousarray(m.transpose(0, 1, 3, 2))).cuda().transpose(2, 3)
         assert mask_dev.stride()[2:] == (1, Sq)
-    else:
+    elif layout == "key_padding":
         m = np.where(rng.random((B, 1, 1, Sk)) < 0.15, -1e30, 0.0).astype(np.float32)
         inp["mask"] = m
         mask_dev = torch.from_numpy(m).cuda()
+    else:
+        # [B, 1, Sq, Sk] stored in rows padded to a multiple of 4 keys: 16-byte aligned rows (the
+        # vector mask paths) with a ragged last group of keys
+        m = np.where(rng.random((B, 1, Sq, Sk)) < 0.1, -1e30, 0.0).astype(np.float32)
+        inp["mask"] = m
+        full = torch.zeros((B, 1, Sq, (Sk + 3) // 4 * 4), dtype=torch.float32)
+        full[..., :Sk] = torch.from_numpy(m)
+        mask_dev = full.cuda()[..., :Sk]
+        assert mask_dev.stride(2) % 4 == 0 and Sk % 4 != 0
     say(f"[mask layout] {layout} D={head_dim}: {w}")
     o, lse = forward_inputs(w, inp)
     got = gpu_backward(w, inp, o, lse, mask_dev=mask_dev)
