@@ -4,25 +4,32 @@
 //      d_scores_hj = probs_hj (dp_j - sum_pd)
 //   C: d_q_h = sum_j d_scores_hj K_j
 //
-// gfx950 design: HBM-bound (K and V dominate the bytes), so one 1024-thread
+// gfx950 design: HBM-bound (K and V dominate the bytes), so one 512-thread
 // block owns one (sequence, KV head) and serves all G query heads of the group
 // from a single pass over V (phase A) and a single pass over K (phase C); every
-// history row is read exactly once.  A row is read by D/8 lanes (8 floats
-// each, as two float4 loads that each cover a contiguous segment of the row),
-// so a wave reads 512/D rows at a time and loads are unrolled two deep.  dp,
-// then d_scores, stay in LDS as [len][G].  Row dot products reduce across the
+// history row is read exactly once, with the streaming (nt) cache policy.  A
+// row is read by D/8 lanes (8 floats each, as two float4 loads that each cover
+// a contiguous segment of the row), so a wave reads 512/D rows at a time and
+// loads are unrolled two deep.  dp, then d_scores, stay in LDS as [len][G]
+// (64 KB at G = 4 and 4096 rows), so two blocks share a CU and one streams
+// while the other sits in a barrier or the short phase B.  Row dot products reduce across the
 // row's lanes with butterfly shuffles; the final d_q reduces across the rows of
 // a wave through shuffles and then over the 16 waves through LDS.
 #include "fa_internal.h"
 
 namespace fa {
 
-constexpr int kDecThreads = 1024;
+constexpr int kDecThreads = 512;
 constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kDecLdsBytes = 160 * 1024;
 
+// 16-byte load with the streaming cache policy (each history row is read once).
+__device__ __forceinline__ f32x4 ldnt4(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+
 template <int D, int G>
-__global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a, const float* __restrict__ Kh,
+__global__ __launch_bounds__(kDecThreads, 2) void decode_kernel(DecodeArgs a, const float* __restrict__ Kh,
                                                                  const float* __restrict__ Vh,
                                                                  const float* __restrict__ probs,
                                                                  const float* __restrict__ dout,
@@ -67,7 +74,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a, co
       const int j = j0 + u * RPI;
 #pragma unroll
       for (int c = 0; c < NV4; ++c)
-        v[u][c] = j < len ? *reinterpret_cast<const f32x4*>(Vb + (int64_t)j * rowstride + 4 * LPR * c) : f32x4{};
+        v[u][c] = j < len ? ldnt4(Vb + (int64_t)j * rowstride + 4 * LPR * c) : f32x4{};
     }
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
@@ -140,7 +147,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void decode_kernel(DecodeArgs a, co
       const int j = j0 + u * RPI;
 #pragma unroll
       for (int c = 0; c < NV4; ++c)
-        kk[u][c] = j < len ? *reinterpret_cast<const f32x4*>(Kb + (int64_t)j * rowstride + 4 * LPR * c) : f32x4{};
+        kk[u][c] = j < len ? ldnt4(Kb + (int64_t)j * rowstride + 4 * LPR * c) : f32x4{};
     }
 #pragma unroll
     for (int u = 0; u < kDecUnroll; ++u) {
