@@ -2,9 +2,10 @@
 // flash_attention_backward_dq.metal, header: D = rowsum(dO * O);
 // ferrotensor-backend flash_attention_v2_backward.wgsl, pass-1 Delta).
 //
-// HBM-bound: each row is read once as 16-byte chunks by a group of lanes,
-// multiplied in fp32 and reduced across the group with DPP lane moves; a lane
-// group takes several rows, their loads in flight together.
+// HBM-bound: each row is read once as 16-byte chunks by a group of lanes (with
+// the streaming cache policy: nothing here is read again), multiplied in fp32
+// and reduced across the group with DPP lane moves; a lane group takes several
+// rows, their loads in flight together.
 #include "fa_internal.h"
 
 namespace fa {
@@ -12,6 +13,11 @@ namespace fa {
 // Each group of LPR lanes reduces RPG rows (RPG loads of O and of dO in flight
 // per lane before the first sum), so a block covers RPG * 256 / LPR rows.
 constexpr int kPreRowsPerGroup = 4;
+
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::chunk ld16_nt(const T* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const typename Mma<T>::chunk*>(p));
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void preprocess_kernel(PrefillArgs a, const T* __restrict__ O,
@@ -38,8 +44,8 @@ __global__ __launch_bounds__(256) void preprocess_kernel(PrefillArgs a, const T*
       const int h = (int)(bh % a.Hq);
       const int b = (int)(bh / a.Hq);
       const int64_t off = (int64_t)b * a.qsb + (int64_t)i * a.qss + (int64_t)h * a.qsh + lane_in_row * CH;
-      o[u] = ld16<T>(O + off);
-      g[u] = ld16<T>(dO + off);
+      o[u] = ld16_nt<T>(O + off);
+      g[u] = ld16_nt<T>(dO + off);
     }
   }
 #pragma unroll
