@@ -7,9 +7,15 @@
 //   dS_ij = P_ij (M_ij dO_i.V_j - Delta_i).
 //
 // gfx950 design: a 256-thread block owns KG groups of 32 keys of one (b, kvh)
-// and streams RT-row tiles of Q and dO through LDS, stored row-major (A operand
-// of S = Q K^T and dP = dO V^T) and transposed (A operand of dV^T += dO^T (P.M)
-// and dK^T += Q^T dS).  Its four waves split the block as KG key groups x RS
+// and streams RT-row tiles of Q and dO through LDS, stored row-major once: the
+// A operand of S = Q K^T and dP = dO V^T is read along the rows (16 bytes per
+// lane), that of dV^T += dO^T (P.M) and dK^T += Q^T dS down the columns (one
+// float per lane and k index, a half-wave reading 32 consecutive floats of a
+// row).  Rows are padded by 32 bytes, so the two half-waves of a column read,
+// four rows apart, fall into disjoint halves of the 64 banks.  At D = 64 the
+// tile area is 74 KB and two blocks share a CU, one computing while the other
+// loads its next tile (at D = 128, and with both a mask and dropout, the
+// registers allow one block per CU).  Its four waves split the block as KG key groups x RS
 // row slices (KG * RS = 4, RT = 32 * RS): each wave keeps its 32 keys' K and V
 // rows in registers as MFMA B operands (v_mfma_f32_32x32x2_f32) and
 // accumulates dK^T, dV^T (D x 32, fp32) over its 32-row slice of every tile;
@@ -34,7 +40,7 @@ struct DkdvF32Shape {
 };
 
 template <typename T, int D, bool MASK, bool DROP>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __restrict__ Q,
+__global__ __launch_bounds__(256, D <= 64 && !(MASK && DROP) ? 2 : 1) void dkdv_kernel(PrefillArgs a, const T* __restrict__ Q,
                                                       const T* __restrict__ K,
                                                       const T* __restrict__ V,
                                                       const T* __restrict__ dO,
@@ -47,27 +53,30 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __
   constexpr int RS = Sh::RS, RT = Sh::RT;
   constexpr int CH = M::CH;
   constexpr int KS = D / (2 * CH);             // k-blocks of the head_dim contraction
-  constexpr int PR = D + 16 / (int)sizeof(T);  // row-major LDS pitch (elements): +16 B per row
-  constexpr int PT = RT + 4;                   // transposed LDS pitch (elements)
+  constexpr int PR = D + 32 / (int)sizeof(T);  // LDS pitch (elements): +32 B per row
   constexpr int TC = 16 / CH;                  // B-operand chunks per 32-row C block
   constexpr int DB = D / 32;                   // 32-row blocks of dK^T / dV^T
   constexpr int NPART = 2 * DB * 16;           // partial-sum registers per lane (dK^T and dV^T)
-  static_assert(Sh::KG * RS == 4 && (2 * RT * PR + 2 * D * PT) * (int)sizeof(T) >= 4 * NPART * 64 * 4,
-                "the tile area holds every wave's partial sums");
+  constexpr int NTILE = 2 * RT * PR;                                // elements of a Q, dO tile
+  constexpr int NSUM = 4 * NPART * 64 * 4 / (int)sizeof(T);         // the four waves' partial sums
+  static_assert(Sh::KG * RS == 4 && NPART % (4 * RS) == 0, "block shape");
 
-  // Q, dO (row-major) and Q^T, dO^T of a tile; after the last tile, the waves'
-  // partial dK^T, dV^T.
-  __shared__ __attribute__((aligned(16))) T sTile[2 * RT * PR + 2 * D * PT];
+  // Q, dO of a tile (row-major); after the last tile, the waves' partial dK^T, dV^T.
+  __shared__ __attribute__((aligned(16))) T sTile[NTILE > NSUM ? NTILE : NSUM];
   T* const sQ = sTile;
   T* const sdO = sTile + RT * PR;
-  T* const sQT = sTile + 2 * RT * PR;
-  T* const sdOT = sQT + D * PT;
   __shared__ float sL[RT];
   __shared__ float sDel[RT];
   __shared__ uint32_t sRK[DROP ? RT : 1];
 
   const int nbh = a.B * a.Hkv;
-  const int kb = blockIdx.x / nbh;  // ascending key block: longest causal work first
+  // Key blocks: the first half ascending (longest causal work first), then the
+  // second half descending, so blocks i and i + grid/2 -- the two a CU holds
+  // when the whole grid is resident -- take key blocks kb and nkb-1-kb, whose
+  // causal work adds up to the same for every pair.
+  const int nkb = (a.Sk + Sh::KEYS - 1) / Sh::KEYS;
+  const int kl = blockIdx.x / nbh, nkh = (nkb + 1) / 2;
+  const int kb = kl < nkh ? kl : nkb - 1 - (kl - nkh);
   const int bh = blockIdx.x % nbh;  // consecutive blocks cycle over (b, kvh) -> one XCD per KV head
   const int b = bh / a.Hkv;
   const int kvh = bh % a.Hkv;
@@ -110,6 +119,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __
     const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq;
     for (int qt = qb; qt < qe; qt += RT) {
       __syncthreads();  // the previous tile has been consumed
+#pragma unroll 4
       for (int c = tid; c < RT * (D / CH); c += 256) {
         const int r = c / (D / CH);
         const int cc = c % (D / CH);
@@ -122,11 +132,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __
         }
         *reinterpret_cast<chunk*>(&sQ[r * PR + cc * CH]) = qv;
         *reinterpret_cast<chunk*>(&sdO[r * PR + cc * CH]) = gv;
-#pragma unroll
-        for (int e = 0; e < CH; ++e) {
-          sQT[(cc * CH + e) * PT + r] = qv[e];
-          sdOT[(cc * CH + e) * PT + r] = gv[e];
-        }
       }
       for (int r = tid; r < RT; r += 256) {
         const int i = qt + r;
@@ -148,6 +153,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __
         const int base = (32 * rs + l32) * PR + 2 * CH * ks + CH * h2;
         M::run(s, *reinterpret_cast<const chunk*>(&sQ[base]), kr[ks]);
         M::run(dp, *reinterpret_cast<const chunk*>(&sdO[base]), vr[ks]);
+        if (ks & 1) __builtin_amdgcn_sched_barrier(0);  // operand reads at most two k-blocks ahead
       }
 
       // Elementwise: P, dropout, dS.  s <- P*M, dp <- dS.
@@ -189,65 +195,59 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(PrefillArgs a, const T* __
         const chunk dsc = M::from_acc(dp, t * CH);
 #pragma unroll
         for (int d = 0; d < DB; ++d) {
-          const int trow = (32 * d + l32) * PT;
+          // A element (lane l, k slot e of half h2) = column 32d + l%32 of row
+          // 32*rs + 8t + 4*h2 + e: the rows C registers 4t .. 4t+3 of the lane hold.
           chunk ao, aq;
 #pragma unroll
           for (int sg = 0; sg < CH / 4; ++sg) {
             const int q = 32 * rs + 8 * ((CH / 4) * t + sg) + 4 * h2;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              ao[4 * sg + e] = sdOT[trow + q + e];
-              aq[4 * sg + e] = sQT[trow + q + e];
+              ao[4 * sg + e] = sdO[(q + e) * PR + 32 * d + l32];
+              aq[4 * sg + e] = sQ[(q + e) * PR + 32 * d + l32];
             }
           }
           M::run(accv[d], ao, pmc);
           M::run(acck[d], aq, dsc);
+          __builtin_amdgcn_sched_barrier(0);  // operand reads at most one column block ahead
         }
       }
     }
   }
 
-  // Sum the row slices' partial dK^T, dV^T of each key group through LDS:
-  // register n of lane l of wave w at sPart[(w * NPART + n) * 64 + l].
+  // Sum the row slices' partial dK^T, dV^T of each key group through LDS and
+  // store them: every wave puts its register n (n = 32d + r: dK^T block d, n =
+  // 32d + 16 + r: dV^T block d) of lane l at sPart[(wave * NPART + n) * 64 + l];
+  // then the wave with row slice rs sums registers rs * NPW .. (rs+1) * NPW - 1
+  // over the key group's RS waves and writes them, four registers (four
+  // consecutive columns of the lane's key) at a time.
   __syncthreads();  // every wave is done with the tiles
   float* const sPart = reinterpret_cast<float*>(sTile);
-  if (rs != 0) {
 #pragma unroll
-    for (int d = 0; d < DB; ++d)
+  for (int d = 0; d < DB; ++d)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sPart[(wave * NPART + 32 * d + r) * 64 + lane] = acck[d][r];
-        sPart[(wave * NPART + 32 * d + 16 + r) * 64 + lane] = accv[d][r];
-      }
-  }
-  __syncthreads();
-  if (rs != 0) return;
-#pragma unroll
-  for (int o = 1; o < RS; ++o) {
-    const int w = wave + o;
-#pragma unroll
-    for (int d = 0; d < DB; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acck[d][r] += sPart[(w * NPART + 32 * d + r) * 64 + lane];
-        accv[d][r] += sPart[(w * NPART + 32 * d + 16 + r) * 64 + lane];
-      }
-  }
-
-  if (jl < a.Sk) {
-#pragma unroll
-    for (int d = 0; d < DB; ++d) {
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int dd = 32 * d + 8 * r4 + 4 * h2;
-        if (dd >= a.D) continue;  // past the head dimension
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dK[koff + dd + e] = from_f32<T>(acck[d][4 * r4 + e] * a.scale);
-          dV[koff + dd + e] = from_f32<T>(accv[d][4 * r4 + e]);
-        }
-      }
+    for (int r = 0; r < 16; ++r) {
+      sPart[(wave * NPART + 32 * d + r) * 64 + lane] = acck[d][r];
+      sPart[(wave * NPART + 32 * d + 16 + r) * 64 + lane] = accv[d][r];
     }
+  __syncthreads();
+  if (jl >= a.Sk) return;
+  constexpr int NPW = NPART / RS;
+#pragma unroll
+  for (int q4 = 0; q4 < NPW / 4; ++q4) {
+    const int n0 = rs * NPW + 4 * q4;
+    const int dd = 32 * (n0 / 32) + 8 * ((n0 % 16) / 4) + 4 * h2;
+    if (dd >= a.D) continue;  // past the head dimension
+    const bool is_v = (n0 / 16) & 1;
+    float x[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int o = 0; o < RS; ++o)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] += sPart[((kg * RS + o) * NPART + n0 + e) * 64 + lane];
+    T* const out = is_v ? dV : dK;
+    const float f = is_v ? 1.f : a.scale;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[koff + dd + e] = from_f32<T>(x[e] * f);
   }
 }
 

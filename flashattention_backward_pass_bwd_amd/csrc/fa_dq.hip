@@ -5,9 +5,12 @@
 //   P_ij = exp(S_ij - L_i) on counted elements, 0 elsewhere.
 //
 // gfx950 design: a 256-thread block owns RG groups of 32 query rows of one
-// (b, h) and streams BK-key tiles of K and V through LDS (row-major: A operand
-// of S^T = K Q^T and dP^T = V dO^T; K also transposed: A operand of
-// dQ^T += K^T dS^T).  Its four waves split the block as RG row groups x KSL key
+// (b, h) and streams BK-key tiles of K and V through LDS, row-major: the A
+// operand of S^T = K Q^T and dP^T = V dO^T is read along the rows, that of
+// dQ^T += K^T dS^T down the columns of K (one float per lane and k index; rows
+// padded by 32 bytes, so the two half-waves, four rows apart, use disjoint
+// banks).  At D = 64 the tile area is 74 KB and two blocks share a CU.  Its
+// four waves split the block as RG row groups x KSL key
 // slices (RG * KSL = 4, BK = 32 * KSL): each wave keeps its 32 rows of Q and dO
 // in registers as MFMA B operands (v_mfma_f32_32x32x2_f32) and accumulates
 // dQ^T (D x 32, fp32) over its 32-key slice of every tile; the KSL partial
@@ -30,7 +33,7 @@ struct DqF32Shape {
 };
 
 template <typename T, int D, bool MASK, bool DROP>
-__global__ __launch_bounds__(256, 1) void dq_kernel(PrefillArgs a, const T* __restrict__ Q,
+__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void dq_kernel(PrefillArgs a, const T* __restrict__ Q,
                                                     const T* __restrict__ K,
                                                     const T* __restrict__ V,
                                                     const T* __restrict__ dO,
@@ -43,23 +46,25 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(PrefillArgs a, const T* __re
   constexpr int KSL = Sh::KSL, BK = Sh::BK;
   constexpr int CH = M::CH;
   constexpr int KS = D / (2 * CH);
-  constexpr int PR = D + 16 / (int)sizeof(T);
-  constexpr int PT = BK + 4;
+  constexpr int PR = D + 32 / (int)sizeof(T);  // LDS pitch (elements): +32 B per row
   constexpr int TC = 16 / CH;
   constexpr int DB = D / 32;
   constexpr int NPART = DB * 16;  // partial-sum registers per lane (dQ^T)
-  static_assert(Sh::RG * KSL == 4 && (2 * BK * PR + D * PT) * (int)sizeof(T) >= 4 * NPART * 64 * 4,
-                "the tile area holds every wave's partial sums");
+  static_assert(Sh::RG * KSL == 4 && 2 * BK * PR * (int)sizeof(T) >= Sh::RG * (KSL - 1) * NPART * 64 * 4,
+                "the tile area holds the partial sums of every wave but the first of each row group");
 
-  // K, V (row-major) and K^T of a tile; after the last tile, the waves' partial dQ^T.
-  __shared__ __attribute__((aligned(16))) T sTile[2 * BK * PR + D * PT];
+  // K, V of a tile (row-major); after the last tile, the waves' partial dQ^T.
+  __shared__ __attribute__((aligned(16))) T sTile[2 * BK * PR];
   T* const sK = sTile;
   T* const sV = sTile + BK * PR;
-  T* const sKT = sTile + 2 * BK * PR;
 
   const int nbh = a.B * a.Hq;
   const int nqb = (a.Sq + Sh::ROWS - 1) / Sh::ROWS;
-  const int qbi = nqb - 1 - (int)(blockIdx.x / nbh);  // last query block first: longest causal work
+  // Query blocks: the last half descending (longest causal work first), then
+  // the first half ascending, so blocks i and i + grid/2 -- the two a CU holds
+  // when the whole grid is resident -- take query blocks nqb-1-q and q.
+  const int ql = (int)(blockIdx.x / nbh), nqh = (nqb + 1) / 2;
+  const int qbi = ql < nqh ? nqb - 1 - ql : ql - nqh;
   // Consecutive blocks cycle over KV heads first, so the query heads of one
   // KV head land on the same XCD (blocks are dealt round-robin over XCDs).
   const int bhi = blockIdx.x % nbh;
@@ -119,8 +124,6 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(PrefillArgs a, const T* __re
       }
       *reinterpret_cast<chunk*>(&sK[r * PR + cc * CH]) = kv;
       *reinterpret_cast<chunk*>(&sV[r * PR + cc * CH]) = vv;
-#pragma unroll
-      for (int e = 0; e < CH; ++e) sKT[(cc * CH + e) * PT + r] = kv[e];
     }
     __syncthreads();
 
@@ -166,13 +169,14 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(PrefillArgs a, const T* __re
       const chunk dsc = M::from_acc(dpt, t * CH);
 #pragma unroll
       for (int d = 0; d < DB; ++d) {
-        const int trow = (32 * d + l32) * PT;
+        // A element (lane l, k slot e of half h2) = column 32d + l%32 of key row
+        // 32*ksl + 8t + 4*h2 + e: the keys C registers 4t .. 4t+3 of the lane hold.
         chunk ak;
 #pragma unroll
         for (int sg = 0; sg < CH / 4; ++sg) {
           const int kk = 32 * ksl + 8 * ((CH / 4) * t + sg) + 4 * h2;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ak[4 * sg + e] = sKT[trow + kk + e];
+          for (int e = 0; e < 4; ++e) ak[4 * sg + e] = sK[(kk + e) * PR + 32 * d + l32];
         }
         M::run(accq[d], ak, dsc);
       }
@@ -180,23 +184,26 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(PrefillArgs a, const T* __re
   }
 
   // Sum the key slices' partial dQ^T of each row group through LDS: register n
-  // of lane l of wave w at sPart[(w * NPART + n) * 64 + l].
+  // of lane l of the wave with key slice ksl > 0 at
+  // sPart[(slot * NPART + n) * 64 + l], slot = rg * (KSL - 1) + ksl - 1.
   __syncthreads();  // every wave is done with the tiles
   float* const sPart = reinterpret_cast<float*>(sTile);
   if (ksl != 0) {
+    const int slot = rg * (KSL - 1) + ksl - 1;
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sPart[(wave * NPART + 16 * d + r) * 64 + lane] = accq[d][r];
+      for (int r = 0; r < 16; ++r) sPart[(slot * NPART + 16 * d + r) * 64 + lane] = accq[d][r];
   }
   __syncthreads();
   if (ksl != 0) return;
 #pragma unroll
   for (int o = 1; o < KSL; ++o) {
+    const int slot = rg * (KSL - 1) + o - 1;
 #pragma unroll
     for (int d = 0; d < DB; ++d)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) accq[d][r] += sPart[((wave + o) * NPART + 16 * d + r) * 64 + lane];
+      for (int r = 0; r < 16; ++r) accq[d][r] += sPart[(slot * NPART + 16 * d + r) * 64 + lane];
   }
 
   if (il < a.Sq) {
