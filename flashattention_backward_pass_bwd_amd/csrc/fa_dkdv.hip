@@ -90,6 +90,12 @@ __global__ __launch_bounds__(256, D <= 64 && !(MASK && DROP) ? 2 : 1) void dkdv_
   const int k0 = kb * Sh::KEYS;
   const int kw0 = k0 + 32 * kg;
   const int jl = kw0 + l32;  // this lane's key (its C-layout column)
+  // Rows that see this lane's key: d = j - i in (dlo, dhi), row and key in
+  // range, i.e. rows [vlo, vlo + vspan); a boundary tile tests each element
+  // against that interval with one unsigned compare (no branch).
+  const DiagBounds vb = diag_bounds(a);
+  const int vlo = max(jl - vb.dhi + 1, 0);
+  const uint32_t vspan = (uint32_t)max((jl < a.Sk ? min(jl - vb.dlo, a.Sq) : 0) - vlo, 0);
 
   chunk kr[KS], vr[KS];
   const int64_t koff = (int64_t)b * a.ksb + (int64_t)jl * a.kss + (int64_t)kvh * a.ksh;
@@ -153,29 +159,27 @@ __global__ __launch_bounds__(256, D <= 64 && !(MASK && DROP) ? 2 : 1) void dkdv_
         const int base = (32 * rs + l32) * PR + 2 * CH * ks + CH * h2;
         M::run(s, *reinterpret_cast<const chunk*>(&sQ[base]), kr[ks]);
         M::run(dp, *reinterpret_cast<const chunk*>(&sdO[base]), vr[ks]);
-        if (ks & 1) __builtin_amdgcn_sched_barrier(0);  // operand reads at most two k-blocks ahead
       }
 
-      // Elementwise: P, dropout, dS.  s <- P*M, dp <- dS.
+      // Elementwise: P, dropout, dS.  s <- P*M, dp <- dS.  Element r sits at row
+      // qt + 32*rs + 4*h2 + c(r), c(r) = 8*(r/4) + r%4, visible iff c(r) - lb < vspan.
+      const int lb = vlo - (qt + 32 * rs + 4 * h2);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * rs + 8 * (r / 4) + 4 * h2 + (r % 4);
-        const int i = qt + row;
         const float l2 = sL[row];
         float p;
         if (full) {
           p = __builtin_amdgcn_exp2f(s[r] * a.scale_log2 - l2);
         } else {
-          bool ok = visible(a, i, jl);
+          bool ok = (uint32_t)(8 * (r / 4) + (r % 4) - lb) < vspan;
           float madd = 0.f;
           if constexpr (MASK) {
-            if (ok) {
-              const float mv = mask_at(a, b, h, i, jl);
-              ok = !(mv <= kMaskedSentinel);
-              madd = mv * kLog2e;
-            }
+            const float mv = ok ? mask_at(a, b, h, qt + row, jl) : 0.f;
+            ok = ok && !(mv <= kMaskedSentinel);
+            madd = mv * kLog2e;
           }
-          p = ok ? __builtin_amdgcn_exp2f(s[r] * a.scale_log2 + madd - l2) : 0.f;
+          p = __builtin_amdgcn_exp2f(ok ? s[r] * a.scale_log2 + madd - l2 : -__builtin_inff());
         }
         float dpv = dp[r];
         float pm = p;
@@ -209,7 +213,6 @@ __global__ __launch_bounds__(256, D <= 64 && !(MASK && DROP) ? 2 : 1) void dkdv_
           }
           M::run(accv[d], ao, pmc);
           M::run(acck[d], aq, dsc);
-          __builtin_amdgcn_sched_barrier(0);  // operand reads at most one column block ahead
         }
       }
     }

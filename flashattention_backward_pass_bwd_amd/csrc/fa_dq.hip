@@ -100,6 +100,12 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void dq_kernel(PrefillArgs a,
   const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq + il;
   const float l2 = il < a.Sq ? L[lrow] * kLog2e : __builtin_inff();
   const float del = il < a.Sq ? Dl[lrow] : 0.f;
+  // Keys this lane's row sees: d = j - i in (dlo, dhi), row and key in range,
+  // i.e. keys [vlo, vlo + vspan); a boundary tile tests each element against
+  // that interval with one unsigned compare (no branch).
+  const DiagBounds vb = diag_bounds(a);
+  const int vlo = max(il + vb.dlo + 1, 0);
+  const uint32_t vspan = (uint32_t)max((il < a.Sq ? min(il + vb.dhi, a.Sk) : 0) - vlo, 0);
   uint32_t rk = 0;
   if constexpr (DROP) rk = drop_row_key(a, b, h, il);
 
@@ -130,6 +136,8 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void dq_kernel(PrefillArgs a,
     const int kw = kt + 32 * ksl;  // this wave's 32 keys of the tile
     if (rect_none_visible(a, qw0, qw0 + 31, kw, kw + 31)) continue;
     const bool full = !MASK && !DROP && rect_all_visible(a, qw0, qw0 + 31, kw, kw + 31);
+    // Element r is key kw + 4*h2 + c(r), c(r) = 8*(r/4) + r%4: visible iff c(r) - lb < vspan.
+    const int lb = vlo - (kw + 4 * h2);
 
     // S^T = K Q^T, dP^T = V dO^T (C column = query).
     f32x16 st{}, dpt{};
@@ -147,16 +155,14 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void dq_kernel(PrefillArgs a,
       if (full) {
         p = __builtin_amdgcn_exp2f(st[r] * a.scale_log2 - l2);
       } else {
-        bool ok = visible(a, il, j);
+        bool ok = (uint32_t)(8 * (r / 4) + (r % 4) - lb) < vspan;
         float madd = 0.f;
         if constexpr (MASK) {
-          if (ok) {
-            const float mv = mask_at(a, b, h, il, j);
-            ok = !(mv <= kMaskedSentinel);
-            madd = mv * kLog2e;
-          }
+          const float mv = ok ? mask_at(a, b, h, il, j) : 0.f;
+          ok = ok && !(mv <= kMaskedSentinel);
+          madd = mv * kLog2e;
         }
-        p = ok ? __builtin_amdgcn_exp2f(st[r] * a.scale_log2 + madd - l2) : 0.f;
+        p = __builtin_amdgcn_exp2f(ok ? st[r] * a.scale_log2 + madd - l2 : -__builtin_inff());
       }
       float dpv = dpt[r];
       if constexpr (DROP) dpv *= drop_keep(rk, j, a.drop_thr) ? a.drop_inv : 0.f;
