@@ -46,9 +46,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
   __shared__ __attribute__((aligned(16))) __bf16 sK[2][BK * D];
   __shared__ __attribute__((aligned(16))) __bf16 sV[WO ? 2 : 1][BK * D];
 
+  // Last query blocks first (under causal attention the longest), and the
+  // query heads of one KV head next to each other (consecutive blocks go to
+  // different XCDs, so a KV head's K and V rows are shared through L2 by
+  // the blocks of its group that run together).
   const int nqb = (a.Sq + kFwdRowsPerBlock - 1) / kFwdRowsPerBlock;
-  const int qbi = blockIdx.x % nqb;
-  const int bh = blockIdx.x / nqb;
+  const int nbh = a.B * a.Hq;
+  const int qbi = nqb - 1 - (int)(blockIdx.x / nbh);
+  const int bh = blockIdx.x % nbh;
   const int h = bh % a.Hq;
   const int b = bh / a.Hq;
   const int kvh = h / a.group;
