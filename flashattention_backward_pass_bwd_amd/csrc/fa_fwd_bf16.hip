@@ -22,12 +22,15 @@
 // builtins, so the compiler keeps their wait states; two blocks share a CU.
 // With WO false the kernel computes L alone (no V, no O): the log-sum-exp
 // sweep for a caller whose forward did not keep L.
+#include <type_traits>
+
 #include "fa_internal.h"
 #include "fa_tiles.h"
 
 namespace fa {
 
 constexpr int kFwdRowsPerBlock = 128;
+constexpr float kLazyLog2 = 8.f;  // lag of a row's reference maximum before O is rescaled (log2 units)
 
 // MV: a mask whose keys are contiguous and 16-byte aligned in groups of 4
 // (mask_keys_contiguous): each lane reads its 4 consecutive keys at once.
@@ -134,95 +137,105 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
     const int jlo = max(i + vb.dlo + 1, 0);
     const int jhi = i < a.Sq ? min(i + vb.dhi, a.Sk) : 0;
     const uint32_t span = (uint32_t)max(jhi - jlo, 0);
-    // S^T of both 32-key halves first (row 32*half + l32 of the tile is the A
-    // operand's key): the second chain runs on the matrix cores while the
-    // first half's exponents are computed.
-    f32x16 sh[2];
+    // The tile's work, with the per-element visibility test compiled out of
+    // fully visible unmasked tiles.
+    auto tile = [&](auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
+      // S^T of both 32-key halves first (row 32*half + l32 of the tile is the A
+      // operand's key): the second chain runs on the matrix cores while the
+      // first half's exponents are computed.
+      f32x16 sh[2];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      sh[half] = f32x16{};
+      for (int half = 0; half < 2; ++half) {
+        sh[half] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kr = lds_read_b128(&sK[st][tile_off<D>(32 * half + l32, 2 * ks + h2)]);
-        sh[half] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qr[ks], sh[half], 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 kr = lds_read_b128(&sK[st][tile_off<D>(32 * half + l32, 2 * ks + h2)]);
+          sh[half] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qr[ks], sh[half], 0, 0, 0);
+        }
       }
-    }
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const f32x16& s = sh[half];
-      // Element r: key j = kt + 32*half + 8*(r/4) + 4*h2 + r%4 of row i.
-      float x[16];
-      float tmax = -__builtin_inff();
-      f32x4 mq[4];  // MV: the mask values of keys kt + 32*half + 8g + 4*h2 .. +3
-      if constexpr (MASK && MV) {
+      for (int half = 0; half < 2; ++half) {
+        const f32x16& s = sh[half];
+        // Element r: key j = kt + 32*half + 8*(r/4) + 4*h2 + r%4 of row i.
+        float x[16];
+        float tmax = -__builtin_inff();
+        f32x4 mq[4];  // MV: the mask values of keys kt + 32*half + 8g + 4*h2 .. +3
+        if constexpr (MASK && MV) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int j0 = kt + 32 * half + 8 * g + 4 * h2;
-          mq[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (i < a.Sq && j0 + 3 - i > vb.dlo && j0 - i < vb.dhi) {
-            if (j0 + 3 < a.Sk) {  // the whole group in range: one 16-byte load
-              mq[g] = *reinterpret_cast<const f32x4*>(mrow + j0);
-            } else {              // the last keys: one by one, none past Sk - 1
+          for (int g = 0; g < 4; ++g) {
+            const int j0 = kt + 32 * half + 8 * g + 4 * h2;
+            mq[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (i < a.Sq && j0 + 3 - i > vb.dlo && j0 - i < vb.dhi) {
+              if (j0 + 3 < a.Sk) {  // the whole group in range: one 16-byte load
+                mq[g] = *reinterpret_cast<const f32x4*>(mrow + j0);
+              } else {              // the last keys: one by one, none past Sk - 1
 #pragma unroll
-              for (int e = 0; e < 4; ++e) mq[g][e] = j0 + e < a.Sk ? mrow[j0 + e] : 0.f;
+                for (int e = 0; e < 4; ++e) mq[g][e] = j0 + e < a.Sk ? mrow[j0 + e] : 0.f;
+              }
             }
           }
         }
-      }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = kt + 32 * half + 8 * (r >> 2) + 4 * h2 + (r & 3);
-        bool ok = full || (uint32_t)(j - jlo) < span;
-        float v = s[r] * a.scale_log2;
-        if constexpr (MASK) {
-          float mv;
-          if constexpr (MV) mv = mq[r >> 2][r & 3];
-          else mv = ok ? mrow[(int64_t)j * a.msk] : 0.f;
-          ok = ok && !(mv <= kMaskedSentinel);
-          v = __builtin_fmaf(mv, kLog2e, v);
-        }
-        x[r] = ok ? v : -__builtin_inff();
-        tmax = fmaxf(tmax, x[r]);
-      }
-      const float mnew = fmaxf(m, halves_max(tmax));
-      const float mref = mnew == -__builtin_inff() ? 0.f : mnew;  // nothing counted yet: every term is 0
-      // Rescale only when some row's maximum grew (the other rows' factor is 1);
-      // after the first tiles of a row that is rare.
-      if (__builtin_amdgcn_ballot_w64(mnew > m) != 0) {
-        const float alpha = __builtin_amdgcn_exp2f(m - mref);
-        l *= alpha;
-        if constexpr (WO) {
-#pragma unroll
-          for (int d = 0; d < DB; ++d)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
-        }
-      }
-      m = mnew;
-      bf16x8 pm[2];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float p0 = __builtin_amdgcn_exp2f(x[r] - mref), p1 = __builtin_amdgcn_exp2f(x[r + 1] - mref);
-        l += p0 + p1;
-        if constexpr (DROP && WO) {
+        for (int r = 0; r < 16; ++r) {
           const int j = kt + 32 * half + 8 * (r >> 2) + 4 * h2 + (r & 3);
-          p0 = drop_keep(rkey, j, a.drop_thr) ? p0 * a.drop_inv : 0.f;
-          p1 = drop_keep(rkey, j + 1, a.drop_thr) ? p1 * a.drop_inv : 0.f;
+          bool ok = FULL || (uint32_t)(j - jlo) < span;
+          float v = s[r] * a.scale_log2;
+          if constexpr (MASK) {
+            float mv;
+            if constexpr (MV) mv = mq[r >> 2][r & 3];
+            else mv = ok ? mrow[(int64_t)j * a.msk] : 0.f;
+            ok = ok && !(mv <= kMaskedSentinel);
+            v = __builtin_fmaf(mv, kLog2e, v);
+          }
+          x[r] = ok ? v : -__builtin_inff();
+          tmax = fmaxf(tmax, x[r]);
         }
-        pm[r >> 3][r & 7] = (__bf16)p0;
-        pm[r >> 3][(r & 7) + 1] = (__bf16)p1;
-      }
-      // O^T += V^T (P.M)^T: k-step t covers keys 32*half + 16t .. +15.
+        // The row's reference m moves only when this half's maximum passes it by
+        // more than kLazyLog2 (then O and the sum are rescaled); otherwise the
+        // terms exp2(x - m) stay at most 2^kLazyLog2, well inside fp32 and bf16
+        // range, and O, the sum and L all use the same m, so the result is the same.
+        const float mt = halves_max(tmax);
+        const bool grow = mt > m + kLazyLog2;  // m = -inf: any counted element
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
+          m = grow ? mt : m;
+          l *= alpha;
+          if constexpr (WO) {
 #pragma unroll
-      for (int t = 0; t < (WO ? 2 : 0); ++t) {
+            for (int d = 0; d < DB; ++d)
 #pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          const __bf16* base = &sV[WO ? st : 0][(32 * half + 16 * t) * D];
-          const bf16x8 vt = concat(lds_read_tr(base + tr_lo[d]), lds_read_tr(base + tr_hi[d]));
-          acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pm[t], acc[d], 0, 0, 0);
+              for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
+          }
+        }
+        const float mref = m == -__builtin_inff() ? 0.f : m;  // nothing counted yet: every term is 0
+        bf16x8 pm[2];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float p0 = __builtin_amdgcn_exp2f(x[r] - mref), p1 = __builtin_amdgcn_exp2f(x[r + 1] - mref);
+          l += p0 + p1;
+          if constexpr (DROP && WO) {
+            const int j = kt + 32 * half + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            p0 = drop_keep(rkey, j, a.drop_thr) ? p0 * a.drop_inv : 0.f;
+            p1 = drop_keep(rkey, j + 1, a.drop_thr) ? p1 * a.drop_inv : 0.f;
+          }
+          pm[r >> 3][r & 7] = (__bf16)p0;
+          pm[r >> 3][(r & 7) + 1] = (__bf16)p1;
+        }
+        // O^T += V^T (P.M)^T: k-step t covers keys 32*half + 16t .. +15.
+#pragma unroll
+        for (int t = 0; t < (WO ? 2 : 0); ++t) {
+#pragma unroll
+          for (int d = 0; d < DB; ++d) {
+            const __bf16* base = &sV[WO ? st : 0][(32 * half + 16 * t) * D];
+            const bf16x8 vt = concat(lds_read_tr(base + tr_lo[d]), lds_read_tr(base + tr_hi[d]));
+            acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt, pm[t], acc[d], 0, 0, 0);
+          }
         }
       }
-    }
+    };
+    if (full) tile(std::true_type{});
+    else tile(std::false_type{});
   }
 
   const float lsum = halves_sum(l);
