@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
       constexpr bool FULL = decltype(full_c)::value;
       // S^T of both 32-key halves first (row 32*half + l32 of the tile is the A
       // operand's key): the second chain runs on the matrix cores while the
-      // first half's exponents are computed.
+      // first half's exponents are computed; one rescale test per tile.
       f32x16 sh[2];
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
@@ -154,12 +154,11 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
           sh[half] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr, qr[ks], sh[half], 0, 0, 0);
         }
       }
+      // The exponents of both halves (in place of S^T) and their maximum.
+      // Element r of half h: key j = kt + 32*h + 8*(r/4) + 4*h2 + r%4 of row i.
+      float tmax = -__builtin_inff();
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        const f32x16& s = sh[half];
-        // Element r: key j = kt + 32*half + 8*(r/4) + 4*h2 + r%4 of row i.
-        float x[16];
-        float tmax = -__builtin_inff();
         f32x4 mq[4];  // MV: the mask values of keys kt + 32*half + 8g + 4*h2 .. +3
         if constexpr (MASK && MV) {
 #pragma unroll
@@ -180,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
         for (int r = 0; r < 16; ++r) {
           const int j = kt + 32 * half + 8 * (r >> 2) + 4 * h2 + (r & 3);
           bool ok = FULL || (uint32_t)(j - jlo) < span;
-          float v = s[r] * a.scale_log2;
+          float v = sh[half][r] * a.scale_log2;
           if constexpr (MASK) {
             float mv;
             if constexpr (MV) mv = mq[r >> 2][r & 3];
@@ -188,31 +187,34 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
             ok = ok && !(mv <= kMaskedSentinel);
             v = __builtin_fmaf(mv, kLog2e, v);
           }
-          x[r] = ok ? v : -__builtin_inff();
-          tmax = fmaxf(tmax, x[r]);
+          sh[half][r] = ok ? v : -__builtin_inff();
+          tmax = fmaxf(tmax, sh[half][r]);
         }
-        // The row's reference m moves only when this half's maximum passes it by
-        // more than kLazyLog2 (then O and the sum are rescaled); otherwise the
-        // terms exp2(x - m) stay at most 2^kLazyLog2, well inside fp32 and bf16
-        // range, and O, the sum and L all use the same m, so the result is the same.
-        const float mt = halves_max(tmax);
-        const bool grow = mt > m + kLazyLog2;  // m = -inf: any counted element
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-          const float alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
-          m = grow ? mt : m;
-          l *= alpha;
-          if constexpr (WO) {
+      }
+      // The row's reference m moves only when the tile's maximum passes it by
+      // more than kLazyLog2 (then O and the sum are rescaled); otherwise the
+      // terms exp2(x - m) stay at most 2^kLazyLog2, well inside fp32 and bf16
+      // range, and O, the sum and L all use the same m, so the result is the same.
+      const float mt = halves_max(tmax);
+      const bool grow = mt > m + kLazyLog2;  // m = -inf: any counted element
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mt) : 1.f;
+        m = grow ? mt : m;
+        l *= alpha;
+        if constexpr (WO) {
 #pragma unroll
-            for (int d = 0; d < DB; ++d)
+          for (int d = 0; d < DB; ++d)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
-          }
+            for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
         }
-        const float mref = m == -__builtin_inff() ? 0.f : m;  // nothing counted yet: every term is 0
+      }
+      const float mref = m == -__builtin_inff() ? 0.f : m;  // nothing counted yet: every term is 0
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
         bf16x8 pm[2];
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          float p0 = __builtin_amdgcn_exp2f(x[r] - mref), p1 = __builtin_amdgcn_exp2f(x[r + 1] - mref);
+          float p0 = __builtin_amdgcn_exp2f(sh[half][r] - mref), p1 = __builtin_amdgcn_exp2f(sh[half][r + 1] - mref);
           l += p0 + p1;
           if constexpr (DROP && WO) {
             const int j = kt + 32 * half + 8 * (r >> 2) + 4 * h2 + (r & 3);
