@@ -49,17 +49,18 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(PrefillArgs a, const _
   __shared__ __attribute__((aligned(16))) __bf16 sK[2][BK * D];
   __shared__ __attribute__((aligned(16))) __bf16 sV[WO ? 2 : 1][BK * D];
 
-  // Last query blocks first (under causal attention the longest), and the
-  // query heads of one KV head next to each other (consecutive blocks go to
-  // different XCDs, so a KV head's K and V rows are shared through L2 by
-  // the blocks of its group that run together).
+  // Last query blocks first (under causal attention the longest); the KV head
+  // varies fastest, then the query head of its group: blocks are dealt to the
+  // XCDs round-robin, so the query heads of one KV head run on the same XCD
+  // and read its K and V rows through one L2.
   const int nqb = (a.Sq + kFwdRowsPerBlock - 1) / kFwdRowsPerBlock;
-  const int nbh = a.B * a.Hq;
-  const int qbi = nqb - 1 - (int)(blockIdx.x / nbh);
-  const int bh = blockIdx.x % nbh;
-  const int h = bh % a.Hq;
-  const int b = bh / a.Hq;
-  const int kvh = h / a.group;
+  const int nkv = a.B * a.Hkv;
+  const int kvi = blockIdx.x % nkv;
+  const int rest = blockIdx.x / nkv;
+  const int qbi = nqb - 1 - rest / a.group;
+  const int kvh = kvi % a.Hkv;
+  const int b = kvi / a.Hkv;
+  const int h = kvh * a.group + rest % a.group;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
