@@ -63,6 +63,12 @@ CASES = {
                                                           seq_k=400, window=160, qk_std=4.0, seed=27),
     "logits_std16_bf16_d64": synth.LONG_BF16.resized(head_dim=64, num_heads=4, num_kv_heads=2, seq_q=300,
                                                      seq_k=300, scale=0.125, qk_std=4.0, seed=28),
+    # the same on the fp32 path (the forward's per-wave key slices then reach very different
+    # maxima before they are merged)
+    "logits_std16_f32_d64": synth.CAUSAL_F32.resized(batch=1, num_heads=4, num_kv_heads=2, seq_q=300, seq_k=300,
+                                                     qk_std=4.0, seed=29),
+    "logits_std16_extras_f32": synth.EXTRAS_BF16.resized(dtype="f32", batch=1, num_heads=4, num_kv_heads=2,
+                                                         seq_q=200, seq_k=200, window=90, qk_std=4.0, seed=30),
 }
 
 
