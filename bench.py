@@ -363,10 +363,15 @@ def bench_prefill(args, w):
     _log(f"forward: {fms:.3f} ms")
     if w.dtype == "bf16" and not args.no_mfma_ceiling:
         ceiling = _mfma_ceiling()
+        # a SIMD retires one v_mfma_f32_32x32x16_bf16 (32768 FLOP) per 32 engine clocks: the peak's
+        # 1024 FLOP per clock per SIMD, so the MFMA-only rate gives the clock the chip holds under it
+        simds = 4 * torch.cuda.get_device_properties(0).multi_processor_count
         out["roofline"]["mfma_ceiling"] = {
             "value": round(ceiling, 1), "unit": "TFLOP/s", "frac": round(roof["achieved"] / ceiling, 4),
+            "engine_clock_ghz": round(ceiling * 1e12 / (simds * 1024.0) / 1e9, 3),
             "how": "back-to-back v_mfma_f32_32x32x16_bf16 on every SIMD, N(0,1) bf16 operands rotating "
-                   "over registers (fa_bwd_calib_mfma_bf16), after the timed steps"}
+                   "over registers (fa_bwd_calib_mfma_bf16), after the timed steps; engine_clock_ghz = "
+                   "that rate / (1024 FLOP per clock per SIMD x SIMDs)"}
         _log(f"MFMA ceiling on N(0,1) operands: {ceiling:.1f} TFLOP/s")
     if not args.no_cpu_baseline:
         _log("cpu baseline: oracle on one GQA group")
