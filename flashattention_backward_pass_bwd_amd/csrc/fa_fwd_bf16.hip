@@ -14,12 +14,14 @@
 // per-lane values (the two half-waves, which hold different keys of the same
 // rows, agree on the maximum through v_permlane32_swap and add their sums at
 // the end).  Per 64-key tile: K and V rows go into a 2-stage LDS ring
-// (swizzled, see fa_tiles.h) by direct global->LDS copies one tile ahead; per
-// 32-key half, S^T (A operand: K rows), the exponent in fp32
-// (scale applied to the fp32 product, so L keeps fp32 accuracy), the online
-// rescale of O^T, and O^T += V^T (P.M)^T with V^T through ds_read_b64_tr_b16
-// and (P.M)^T straight from the C registers of S^T.  The MFMAs are compiler
-// builtins, so the compiler keeps their wait states; two blocks share a CU.
+// (swizzled, see fa_tiles.h) by direct global->LDS copies one tile ahead;
+// S^T of both 32-key halves (A operand: K rows), the exponents in fp32 (scale
+// applied to the fp32 product, so L keeps fp32 accuracy), one lazy rescale
+// test for the tile (a row's reference maximum moves only when passed by more
+// than 2^8), and per half O^T += V^T (P.M)^T with V^T through
+// ds_read_b64_tr_b16 and (P.M)^T straight from the C registers of S^T.  The
+// MFMAs are compiler builtins, so the compiler keeps their wait states; two
+// blocks share a CU.
 // With WO false the kernel computes L alone (no V, no O): the log-sum-exp
 // sweep for a caller whose forward did not keep L.
 #include <type_traits>
