@@ -487,7 +487,7 @@ def bench_copy(args):
 def main():
     args = _args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has no multi-GPU path; "
               "the per-GPU kernel is what one GPU runs when the work is sharded by (batch, KV head).",
               file=sys.stderr)
         sys.exit(2)
