@@ -3,8 +3,11 @@
 fmix32 is pinned to published MurmurHash3_x86_32 vectors (tests/golden); the
 keep-mask composition built on it -- our own specification, since the pages
 call a dropout helper whose definition is not on them -- is pinned by its
-statistical properties: keep rate, no lag-1 correlation along i or j, a
-bijection in j within a row, and independence across seeds and heads.
+statistical properties (keep rate, no lag-1 correlation along i or j, a
+bijection in j within a row, independence across seeds and heads) and by its
+structure: a row's draws depend only on its flat index (b*H + h)*Sq + i, and
+the oracle backward drops exactly the pairs of each query row's own index
+(recovered from dV with one-hot dO rows, GQA with Sq != Sk).
 """
 import os
 
@@ -114,3 +117,52 @@ def test_p_zero_keeps_everything_and_multiplier():
     spec = oracle.Spec(scale=1.0, dropout_p=0.25, seed=9)
     m = oracle.dropout_multiplier(spec, 0, 0, 2, 16, np.arange(16), np.arange(16))
     assert set(np.unique(m)) <= {0.0, 1.0 / 0.75}
+
+
+def test_draw_depends_only_on_the_flat_row_index():
+    """The reading keys each row by its flat index (b*H + h)*Sq + i: row (b, h, i) of
+    a B x H x Sq problem draws what row (b*H + h)*Sq + i of a one-head problem with
+    B*H*Sq rows draws.  A slip in the flattening (Sk for Sq, b and h swapped, a
+    dropped term) moves rows and fails this."""
+    seed, B, H, Sq = 11, 3, 5, 37
+    cols = np.arange(70)
+    flat = oracle.dropout_draw(seed, 0, 0, 1, B * H * Sq, np.arange(B * H * Sq), cols)
+    for b in range(B):
+        for h in range(H):
+            rows = np.arange(Sq)
+            got = oracle.dropout_draw(seed, b, h, H, Sq, rows, cols)
+            np.testing.assert_array_equal(got, flat[(b * H + h) * Sq + rows])
+    # and the key enters on its own: column j of a row does not depend on the other columns asked for
+    one = oracle.dropout_draw(seed, 1, 2, H, Sq, [4], [9])
+    np.testing.assert_array_equal(one[0, 0], oracle.dropout_draw(seed, 1, 2, H, Sq, [4], cols)[0, 9])
+
+
+def test_backward_drops_the_pairs_of_its_own_rows():
+    """The oracle backward applies the keep bits of each query row's own flat index
+    (query head, not KV head; Sq, not Sk): with one-hot dO rows and no other
+    exclusion, dV[b, kvh, j, g*Sq + i] = P_ij M_ij of query head kvh*group + g, so
+    its nonzero pattern is the keep pattern.  GQA with Sq != Sk catches a hash fed
+    the KV head or the key length."""
+    B, Hq, Hkv, Sq, Sk = 2, 4, 2, 6, 9
+    group = Hq // Hkv
+    D = group * Sq
+    p, seed = 0.4, 23
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((B, Hq, Sq, D)) * 0.3
+    k = rng.standard_normal((B, Hkv, Sk, D)) * 0.3
+    v = rng.standard_normal((B, Hkv, Sk, D))
+    do = np.zeros((B, Hq, Sq, D))
+    for h in range(Hq):
+        for i in range(Sq):
+            do[:, h, i, (h % group) * Sq + i] = 1.0
+    spec = oracle.Spec(scale=0.5, dropout_p=p, seed=seed)
+    o, lse = oracle.forward(q, k, v, spec)
+    _, _, _, dv = oracle.backward(q, k, v, o, do, lse, spec)
+    flat = oracle.dropout_keep(seed, 0, 0, 1, B * Hq * Sq, np.arange(B * Hq * Sq), np.arange(Sk), p)
+    for b in range(B):
+        for h in range(Hq):
+            kvh, g = h // group, h % group
+            got = dv[b, kvh, :, g * Sq:(g + 1) * Sq].T != 0.0  # [i, j]
+            want = flat[(b * Hq + h) * Sq:(b * Hq + h + 1) * Sq]
+            np.testing.assert_array_equal(got, want)
+    assert 0 < flat.mean() < 1
