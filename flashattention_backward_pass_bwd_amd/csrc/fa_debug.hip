@@ -50,10 +50,9 @@ __global__ __launch_bounds__(256, 1) void calib_mfma_kernel(const bf16x8* __rest
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     av[i] = ops[t + 256 * i];
-    bv[i] = ld16_agpr(ops + 1024 + t + 256 * i);  // straight into AGPRs (no VALU write before the MFMAs)
+    bv[i] = ld16_op(ops + 1024 + t + 256 * i);
   }
   wait_all_vmem();
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   f32x16 acc[4] = {};
   // two wait states between the VALU zeroing of the accumulators and the first MFMA
   asm volatile("s_nop 1" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]));

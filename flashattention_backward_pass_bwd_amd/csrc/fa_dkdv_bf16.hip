@@ -45,6 +45,38 @@
 
 namespace fa {
 
+// Vector-memory operations of slot j of an S/dP + exp/dS section of the dK/dV
+// kernel below (E = 16/NSD elements per slot): the slot's tile copy (one every
+// NSD/PER slots, from slot 0), then its mask copies (MVEC: one per 4-element
+// group, in the slot of the group's last element; otherwise one per element).
+template <int NSD, int PER, bool MVEC>
+constexpr int sdp_slot_vmem(int j) {
+  constexpr int E = 16 / NSD, SG = 4 / E;
+  return (j % (NSD / PER) == 0 ? 1 : 0) + (MVEC ? (j % SG == SG - 1 ? 1 : 0) : E);
+}
+
+// Vector-memory operations a wave issues after the copy that stages mask
+// element r and before r is read, for the reads made ahead of slot kk - MF
+// (elements kk*E .. kk*E + E-1; the least of their counts): the copies after
+// it in the copying section, the DKV operations of the dV/dK section in
+// between, and those of the reading section's earlier slots.  vmcnt drops in
+// issue order, so waiting until at most that many are in flight means r landed.
+template <int NSD, int PER, bool MVEC, int MF, int DKV>
+constexpr int mask_read_wait(int kk) {
+  constexpr int E = 16 / NSD, SG = 4 / E;
+  int least = 63;
+  for (int i = 0; i < E; ++i) {
+    const int r = kk * E + i;
+    const int cs = MVEC ? SG * (r / 4) + SG - 1 : r / E;  // slot of r's copy
+    int n = MVEC ? 0 : E - 1 - r % E;                     // copies of that slot after it
+    for (int j = cs + 1; j < NSD; ++j) n += sdp_slot_vmem<NSD, PER, MVEC>(j);
+    n += DKV;
+    for (int j = 0; j < kk - MF; ++j) n += sdp_slot_vmem<NSD, PER, MVEC>(j);
+    least = n < least ? n : least;
+  }
+  return least;
+}
+
 // MK: 0 no mask, 1 a mask of any strides, 2 a mask whose keys are contiguous and
 // whose 4-key groups are 16-byte aligned (staged with one 16-byte copy per lane
 // for 8 rows of the wave's 32 keys).
@@ -130,12 +162,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     // K and V rows of this wave's keys in accumulation registers (keys past the
     // end repeat the last key; no element of theirs is counted).
     bf16x8 kr[KS], vr[KS];
-    const int64_t koff = (int64_t)b * a.ksb + (int64_t)jl * a.kss + (int64_t)kvh * a.ksh;
     const int64_t kclamp = (int64_t)b * a.ksb + (int64_t)min(jl, a.Sk - 1) * a.kss + (int64_t)kvh * a.ksh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      kr[s] = ld16_agpr(row_chunk(K + kclamp, 2 * s + h2, a.D / 8));  // zero past the head dimension
-      vr[s] = ld16_agpr(row_chunk(V + kclamp, 2 * s + h2, a.D / 8));
+      kr[s] = ld16_op(row_chunk(K + kclamp, 2 * s + h2, a.D / 8));  // zero past the head dimension
+      vr[s] = ld16_op(row_chunk(V + kclamp, 2 * s + h2, a.D / 8));
     }
     f32x16 acck[DB], accv[DB];
 #pragma unroll
@@ -143,7 +174,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       acck[d] = f32x16{};
       accv[d] = f32x16{};
     }
-    wait_vmcnt<0>();  // K and V rows landed before the copy ring starts
+    wait_all_vmem();  // K and V rows landed (a wait the compiler sees) before the copy ring starts
 
     // Mask reads: byte offset of element (row, key) in the (b, h) slice is
     // row*msq*4 + key*msk*4; lanes fix the key (clamped) and the 4-row group.
@@ -244,18 +275,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       static_assert(NC % 4 == 0, "a tile's copies spread over four sections");
       // Mask staging (MASK): element r of a half is copied into sM right after the
       // same element of the other half was used (sections A and C, the slot of
-      // element r), and read MF slots before its own use two sections later.  Of
-      // the copies issued after it, at least 16 - E*(MF+1) mask copies and
-      // PER - 1 tile copies are issued before that read (E elements per slot),
-      // so waiting for at most kMaskWait accesses in flight covers it.
-      constexpr int MF = 2;
-      constexpr int kMaskWait = 16 - (16 / NSD) * (MF + 1) + PER - 1;
-      static_assert(kMaskWait >= 0, "mask staging wait");
-      // MVEC: group g (elements 4g .. 4g+3, 8 rows) is one copy, issued after its
-      // last element's slot; any element read MF slots ahead has at least 2 group
-      // copies and PER tile copies issued after its group's copy.
+      // element r; MVEC: one copy per 4-element group, after its last element's
+      // slot), and read MF slots before its own use two sections later.  The
+      // wait before a read lets exactly the vector-memory operations issued
+      // after that copy stay in flight (mask_read_wait), so it holds up neither
+      // the later tile copies nor the dS stores.
+      constexpr int MF = 4;
       constexpr int SG = 4 / (16 / NSD);  // slots per group
-      constexpr int kMaskWaitV = 1 + PER;
       constexpr int sl = (PER - 1) * (NSD / PER);  // section A's last tile copy slot
       constexpr int kMaskLateA = MVEC ? (SG - 1 >= sl) + (2 * SG - 1 >= sl) + (3 * SG - 1 >= sl) + (4 * SG - 1 >= sl)
                                       : 16 / PER;
@@ -462,8 +488,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         auto mask_rd = [&](int kk) {
           if constexpr (MASK) {
             if (kk < NSD) {
-              // (WS: the two dS stores of the dV/dK section in between count too)
-              wait_vmcnt<(MVEC ? kMaskWaitV : kMaskWait) + (WS ? 2 : 0)>();
+              // (the dV/dK section in between: PER tile copies, the two dS stores
+              // with WS, and in section B the L/Delta copy, left out: a wait for
+              // one operation fewer is still sufficient)
+              wait_vmcnt_n(mask_read_wait<NSD, PER, MVEC, MF, PER + (WS ? 2 : 0)>(kk));
 #pragma unroll
               for (int i = 0; i < 16 / NSD; ++i) {
                 const int r = kk * (16 / NSD) + i;
@@ -737,6 +765,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     mfma_drain_acc(acck, accv);  // the accumulators' last MFMAs have finished before they are read
 
     if (jl < a.Sk) {
+      const int64_t koff = (int64_t)b * a.ksb + (int64_t)jl * a.kss + (int64_t)kvh * a.ksh;
 #pragma unroll
       for (int d = 0; d < DB; ++d) {
 #pragma unroll

@@ -115,8 +115,8 @@ __global__ __launch_bounds__(256, 1) void dq2_bf16_kernel(PrefillArgs a, const _
       const int64_t qclamp = (int64_t)b * a.qsb + (int64_t)min(il[rb], a.Sq - 1) * a.qss + (int64_t)h * a.qsh;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        qr[rb][s] = ld16_agpr(row_chunk(Q + qclamp, 2 * s + h2, a.D / 8));  // zero past the head dimension
-        gr[rb][s] = ld16_agpr(row_chunk(dO + qclamp, 2 * s + h2, a.D / 8));
+        qr[rb][s] = ld16_op(row_chunk(Q + qclamp, 2 * s + h2, a.D / 8));  // zero past the head dimension
+        gr[rb][s] = ld16_op(row_chunk(dO + qclamp, 2 * s + h2, a.D / 8));
       }
       const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq + min(il[rb], a.Sq - 1);
       nl[rb] = il[rb] < a.Sq ? -L[lrow] * a.inv_scale : 0.f;  // rows past the end: never counted

@@ -135,15 +135,15 @@ __global__ __launch_bounds__(256, 1) void dq_bf16_kernel(PrefillArgs a, const __
     const int qw0 = q0 + wave * kDqRowsPerWave;
     const int il = qw0 + l32;
 
-    // Q and dO rows of this wave's queries, straight into accumulation registers
+    // Q and dO rows of this wave's queries, in registers for the whole pass
     // (rows past the end repeat the last row; their results are not written).
     bf16x8 qr[KS], gr[KS];
     const int64_t qoff = (int64_t)b * a.qsb + (int64_t)il * a.qss + (int64_t)h * a.qsh;
     const int64_t qclamp = (int64_t)b * a.qsb + (int64_t)min(il, a.Sq - 1) * a.qss + (int64_t)h * a.qsh;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      qr[s] = ld16_agpr(row_chunk(Q + qclamp, 2 * s + h2, a.D / 8));  // zero past the head dimension
-      gr[s] = ld16_agpr(row_chunk(dO + qclamp, 2 * s + h2, a.D / 8));
+      qr[s] = ld16_op(row_chunk(Q + qclamp, 2 * s + h2, a.D / 8));  // zero past the head dimension
+      gr[s] = ld16_op(row_chunk(dO + qclamp, 2 * s + h2, a.D / 8));
     }
     const int64_t lrow = ((int64_t)b * a.Hq + h) * a.Sq + min(il, a.Sq - 1);
     const float nl = il < a.Sq ? -L[lrow] * a.inv_scale : 0.f;  // rows past the end: never counted

@@ -175,6 +175,22 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// wait_vmcnt for a count that becomes a constant only once the slot loops
+// around the call are unrolled (the instruction takes an immediate): the chain
+// of tests folds to the one wait.  A count above 63 waits for 63 (more than
+// asked, still sufficient).
+template <int N = 0>
+__device__ __forceinline__ void wait_vmcnt_n(int n) {
+  if constexpr (N >= 63) {
+    wait_vmcnt<63>();
+  } else {
+    if (n <= N)
+      wait_vmcnt<N>();
+    else
+      wait_vmcnt_n<N + 1>(n);
+  }
+}
+
 // v_mfma_f32_32x32x16_bf16 as inline assembly, with the register file of each
 // operand fixed: the accumulators of long sums (dK, dV) and the stationary B
 // operands (K, V rows) live in accumulation registers (AGPRs), the short-lived
@@ -237,10 +253,6 @@ __device__ __forceinline__ bool elem_visible(int r, int lb, uint32_t span) {
 // there as a B operand without a copy per use.
 __device__ __forceinline__ void to_agpr(bf16x8& v) { asm volatile("" : "+a"(v)); }
 
-// 16-byte global load straight into accumulation registers (the home of the
-// stationary B operands), as inline assembly: the compiler neither copies the
-// value between register files nor waits for it; the caller waits with
-// wait_vmcnt before the first MFMA that reads it.
 // Sixteen zero bytes in device memory: a lane whose chunk of a register-held
 // row lies past a padded head dimension loads its operand from here.
 static __device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
@@ -251,10 +263,14 @@ __device__ __forceinline__ const void* row_chunk(const __bf16* row, int c, int n
   return c < n ? static_cast<const void*>(row + 8 * c) : static_cast<const void*>(kZeroChunk);
 }
 
-__device__ __forceinline__ bf16x8 ld16_agpr(const void* p) {
-  bf16x8 v;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=a"(v) : "v"(p) : "memory");
-  return v;
+// 16-byte global load of a register-held MFMA operand (a row chunk of K, V, Q
+// or dO that stays in registers for a whole pass).  A plain load the compiler
+// sees, so it tracks the load and places the wait before the first use itself
+// (kernels that issue inline-assembly copies after such loads end the
+// compiler's view of them with wait_all_vmem before their copy loops).
+typedef const bf16x8 __attribute__((address_space(1))) global_bf16x8;
+__device__ __forceinline__ bf16x8 ld16_op(const void* p) {
+  return *(global_bf16x8*)(p);
 }
 
 // Wait states after the last MFMA of a group before its results are read by
