@@ -205,42 +205,51 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     const int ntiles = ntq * a.group;
 
     if (ntiles > 0) {
-      // Steps are numbered it = (ntq-1-t)*group + g (query tile t, query head
-      // g of the group).  A cursor names the tile whose copies are issued next; past
-      // the last tile it stays there, so the last copies repeat into stages
-      // that are never read and every step runs the same straight-line code.
+      // Steps walk the query tiles in one direction (see below), each tile for
+      // every query head of the group in turn.  A cursor names the tile whose
+      // copies are issued next; past the last tile of the walk it stays there, so
+      // the last copies repeat into stages that are never read and every step
+      // runs the same straight-line code.
       // The cursor also carries the element offsets of the tile's first row in
       // Q/dO and in L/Delta, moved on by per-pass increments (no multiplies per step).
       struct Cursor {
         int g, t, qt;
         int64_t qoff, loff;
       };
-      // Order: query tiles from the last down to the first, and for each tile
-      // the group's query heads in turn.  The blocks of one KV head run side by
-      // side on one XCD and start on the same last tile, so they read the same
-      // Q/dO tiles at about the same time and share them in L2 (causal blocks
-      // differ only in where they stop).
-      const int64_t inc_qh = a.qsh;                                                    // next head, same tile
-      const int64_t inc_qt = -(int64_t)(a.group - 1) * a.qsh - (int64_t)BQ * a.qss;   // first head, tile below
-      const int64_t inc_lt = -(int64_t)(a.group - 1) * a.Sq - (int64_t)BQ;
+      // Order: a block's first key block walks its query tiles from the last
+      // down to the first, its second one (paired causal blocks) from the first
+      // up to the last.  The blocks of one KV head run side by side on one XCD
+      // and start together on the last tile, so in the first pass they read the
+      // same Q/dO tiles at about the same time and share them in L2.  A block's
+      // second pass begins when its first one ends, on a first tile that lies
+      // as many tiles higher as its first pass was shorter: walking up, every
+      // block in its second pass is on the same tile at the same time as well,
+      // and shares those reads too (walking down, each would re-read the top
+      // tiles on its own).
+      const bool up = pass == 1;
+      const int tdir = up ? 1 : -1;
+      const int64_t inc_qh = a.qsh;  // next head, same tile
+      const int64_t inc_qt = -(int64_t)(a.group - 1) * a.qsh + (int64_t)(tdir * BQ) * a.qss;  // first head, next tile
+      const int64_t inc_lt = -(int64_t)(a.group - 1) * a.Sq + tdir * BQ;
+      const int tfirst = up ? 0 : ntq - 1;
       auto cursor0 = [&]() {
         const int h0 = kvh * a.group;
-        const int qt = qb + (ntq - 1) * BQ;
-        return Cursor{0, ntq - 1, qt, (int64_t)b * a.qsb + (int64_t)h0 * a.qsh + (int64_t)qt * a.qss,
+        const int qt = qb + tfirst * BQ;
+        return Cursor{0, tfirst, qt, (int64_t)b * a.qsb + (int64_t)h0 * a.qsh + (int64_t)qt * a.qss,
                       ((int64_t)b * a.Hq + h0) * a.Sq + qt};
       };
-      // Next head, else the first head of the tile below, else stay: the
+      // Next head, else the first head of the next tile, else stay: the
       // conditions, then one field per part (parts 0..4), so that a step can
       // spread the update over several pipeline slots.
       struct Turn {
         bool ng, nt;
       };
-      auto turn_of = [&](const Cursor& c) { return Turn{c.g + 1 < a.group, c.t > 0}; };
+      auto turn_of = [&](const Cursor& c) { return Turn{c.g + 1 < a.group, up ? c.t < ntq - 1 : c.t > 0}; };
       auto advance_part = [&](Cursor& c, const Turn& w, int part) {
         if (part == 0) c.qoff += w.ng ? inc_qh : (w.nt ? inc_qt : 0);
         if (part == 1) c.loff += w.ng ? (int64_t)a.Sq : (w.nt ? inc_lt : 0);
-        if (part == 2) c.qt = w.ng ? c.qt : (w.nt ? c.qt - BQ : c.qt);
-        if (part == 3) c.t = w.ng ? c.t : (w.nt ? c.t - 1 : c.t);
+        if (part == 2) c.qt = w.ng ? c.qt : (w.nt ? c.qt + tdir * BQ : c.qt);
+        if (part == 3) c.t = w.ng ? c.t : (w.nt ? c.t + tdir : c.t);
         if (part == 4) c.g = w.ng ? c.g + 1 : (w.nt ? 0 : c.g);
       };
       auto advance = [&](Cursor& c) {
@@ -744,20 +753,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       const std::integral_constant<int, 2> kInner;
       // This wave's tiles: [0,f0) boundary, [f0,f1) interior, [f1,ntq)
       // boundary (the visible key interval moves monotonically with the query
-      // row, so the interior tiles are contiguous), walked from the last down,
-      // each for every query head of the group.  Boundary tiles include tiles
-      // this wave cannot see at all; the predicate zeroes them.
+      // row, so the interior tiles are contiguous), walked in the pass's
+      // direction, each for every query head of the group.  Boundary tiles
+      // include tiles this wave cannot see at all; the predicate zeroes them.
       auto all = [&](int t) { return rect_all_visible(a, qb + t * BQ, qb + t * BQ + BQ - 1, kw0, kw0 + kDkdvKeysPerWave - 1); };
       int f0 = 0;
       while (f0 < ntq && !all(f0)) ++f0;
       int f1 = f0;
       while (f1 < ntq && all(f1)) ++f1;
-      int t = ntq - 1;
-      for (; t >= f1; --t)
+      const int n_first = up ? f0 : ntq - f1, n_last = up ? ntq - f1 : f0;
+      int t = tfirst;
+      for (int u = 0; u < n_first; ++u, t += tdir)
         for (int g = 0; g < a.group; ++g) step(kEdge, g, t);
-      for (; t >= f0; --t)
+      for (int u = f0; u < f1; ++u, t += tdir)
         for (int g = 0; g < a.group; ++g) step(kInner, g, t);
-      for (; t >= 0; --t)
+      for (int u = 0; u < n_last; ++u, t += tdir)
         for (int g = 0; g < a.group; ++g) step(kEdge, g, t);
       wait_vmcnt<0>();  // the repeated copies of the last steps have landed
       barrier_lds();    // every wave is done with the ring before the next pass refills it
