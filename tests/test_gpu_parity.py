@@ -50,6 +50,12 @@ CASES = {
                                                        causal_offset=220, window=130, seed=23),
     "noncausal_bf16_d128": synth.LONG_BF16.resized(batch=2, num_heads=4, num_kv_heads=2, seq_q=333, seq_k=190,
                                                    causal=False, seed=22),
+    # plain causal with mask and dropout (no window): paired key blocks, the second walked upwards,
+    # with the mask staged per element (Sk % 4 != 0) and per 4-key group (Sk % 4 == 0)
+    "causal_mask_drop_bf16_d128": synth.EXTRAS_BF16.resized(batch=1, num_heads=4, num_kv_heads=2, seq_q=333,
+                                                            seq_k=333, window=0, seed=35),
+    "causal_mask_drop_bf16_d64": synth.EXTRAS_BF16.resized(head_dim=64, batch=1, num_heads=4, num_kv_heads=1,
+                                                           seq_q=336, seq_k=336, window=0, scale=0.125, seed=36),
     "mask_noncausal_bf16": synth.EXTRAS_BF16.resized(batch=1, num_heads=4, num_kv_heads=4, seq_q=190, seq_k=260,
                                                      causal=False, window=0, mask_density=0.3, dropout_p=0.0,
                                                      seed=20),

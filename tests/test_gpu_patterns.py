@@ -46,6 +46,7 @@ PATTERN_CASES = {
     "mha_noncausal_mask_drop_d64": (BASE.resized(head_dim=64, num_heads=3, num_kv_heads=3, causal=False,
                                                  causal_offset=0, window=0, seq_q=200, seq_k=150, seed=63), "plain"),
     "causal_offset_d128_no_drop": (BASE.resized(window=0, mask_density=0.0, dropout_p=0.0, seed=64), None),
+    "causal_offset_mask_drop_d128_padded_mask": (BASE.resized(window=0, seed=67), "padded"),
     "noncausal_d128_no_drop": (BASE.resized(causal=False, causal_offset=0, window=0, mask_density=0.0,
                                             dropout_p=0.0, seq_q=290, seq_k=170, seed=65), None),
     "f32_gqa_offset_window_mask_drop_d64": (BASE.resized(dtype="f32", head_dim=64, seed=66), "plain"),
