@@ -225,26 +225,46 @@ __global__ __launch_bounds__(256, BK == 32 ? 2 : 1) void dqs_bf16_kernel(Prefill
   }
   mfma_drain_acc(acc);
 
-  if (active) {
+  // dQ of the wave's rows leaves through LDS, one 32-row half at a time, so
+  // that each store writes 16 bytes of a row and D/8 lanes a whole row: lane
+  // (l32, h2) puts its 4-element pieces of its row into a per-wave [32][D + 8]
+  // bf16 block of the dS ring (free once every wave has passed the barrier
+  // below), then lane l reads chunk l % (D/8) of rows RPS*i + l / (D/8) and
+  // stores it.
+  constexpr int SR = D + 8;
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPS = 64 / CPR;  // rows per read and store
+  static_assert(4 * 32 * SR <= (int)(sizeof(sS) / sizeof(__bf16)), "the staging blocks fit the dS ring");
+  barrier_lds();
+  __bf16* const stg = &sS[0][0][0][0] + wave * 32 * SR;
+  const int c = lane % CPR;
+  __bf16* const base = dQ + (int64_t)b * a.qsb + (int64_t)h * a.qsh + 8 * c;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      // Column l%32 of row half m holds the row the dK/dV pass's lane stored
-      // there: quads 1 and 2 of each 16 rows swapped.
-      const int p = l32;
-      const int row = kWsRows * qtile + 32 * m + ((p & 0x13) | ((p & 4) << 1) | ((p & 8) >> 1));
-      if (row < a.Sq) {
-        __bf16* out = dQ + (int64_t)b * a.qsb + (int64_t)row * a.qss + (int64_t)h * a.qsh;
+  for (int m = 0; m < 2; ++m) {
+    // Column l%32 of row half m holds the row the dK/dV pass's lane stored
+    // there: quads 1 and 2 of each 16 rows swapped.
+    const int p = l32;
+    const int rl = (p & 0x13) | ((p & 4) << 1) | ((p & 8) >> 1);
 #pragma unroll
-        for (int d = 0; d < DB; ++d) {
+    for (int d = 0; d < DB; ++d) {
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            if (32 * d + 8 * r4 + 4 * h2 >= a.D) continue;  // past the head dimension
-            bf16x4 o4;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        bf16x4 o4;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[2 * d + m][4 * r4 + e] * a.scale);
-            *reinterpret_cast<bf16x4*>(out + 32 * d + 8 * r4 + 4 * h2) = o4;
-          }
-        }
+        for (int e = 0; e < 4; ++e) o4[e] = (__bf16)(acc[2 * d + m][4 * r4 + e] * a.scale);
+        *reinterpret_cast<bf16x4*>(stg + rl * SR + 32 * d + 8 * r4 + 4 * h2) = o4;
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's writes land before its reads
+    bf16x8 v[32 / RPS];
+#pragma unroll
+    for (int i = 0; i < 32 / RPS; ++i) v[i] = *reinterpret_cast<const bf16x8*>(stg + (RPS * i + lane / CPR) * SR + 8 * c);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // and its reads before the next half's writes
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < 32 / RPS; ++i) {
+        const int row = kWsRows * qtile + 32 * m + RPS * i + lane / CPR;
+        if (row < a.Sq && 8 * c < a.D) *reinterpret_cast<bf16x8*>(base + (int64_t)row * a.qss) = v[i];
       }
     }
   }
