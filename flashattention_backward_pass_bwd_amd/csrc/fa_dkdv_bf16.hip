@@ -774,24 +774,46 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     }
     mfma_drain_acc(acck, accv);  // the accumulators' last MFMAs have finished before they are read
 
-    if (jl < a.Sk) {
-      const int64_t koff = (int64_t)b * a.ksb + (int64_t)jl * a.kss + (int64_t)kvh * a.ksh;
+    // dK and dV of this wave's 32 keys leave through LDS (the ring is free: every
+    // wave has passed this pass's last barrier), so that each store writes 16
+    // bytes of a row and D/8 lanes a whole row: lane (l32, h2) puts its
+    // 4-element pieces of key l32 into a per-wave [2][32][D + 8] bf16 block,
+    // then lane l reads chunk l % (D/8) of rows RPS*i + l / (D/8) and stores it.
+    {
+      constexpr int SR = D + 8;                 // staging row, elements (16 bytes of padding)
+      constexpr int CPR = D / 8, RPS = 64 / CPR;  // 16-byte chunks per row, rows per read and store
+      static_assert(4 * 2 * 32 * SR <= NST * 2 * TILE, "the staging blocks fit the ring");
+      __bf16* const stg = &sT[0][0][0] + wave * 2 * 32 * SR;
 #pragma unroll
       for (int d = 0; d < DB; ++d) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int dd = 32 * d + 8 * r4 + 4 * h2;
-          if (dd >= a.D) continue;  // past the head dimension
           bf16x4 ok4, ov4;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             ok4[e] = (__bf16)(acck[d][4 * r4 + e] * a.scale);
             ov4[e] = (__bf16)accv[d][4 * r4 + e];
           }
-          *reinterpret_cast<bf16x4*>(dK + koff + dd) = ok4;
-          *reinterpret_cast<bf16x4*>(dV + koff + dd) = ov4;
+          *reinterpret_cast<bf16x4*>(stg + l32 * SR + dd) = ok4;
+          *reinterpret_cast<bf16x4*>(stg + (32 + l32) * SR + dd) = ov4;
         }
       }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's writes land before its reads
+      const int c = lane % CPR;
+      const int64_t kvbase = (int64_t)b * a.ksb + (int64_t)kvh * a.ksh + 8 * c;
+#pragma unroll
+      for (int i = 0; i < 32 / RPS; ++i) {
+        const int r = RPS * i + lane / CPR;
+        const bf16x8 vk = *reinterpret_cast<const bf16x8*>(stg + r * SR + 8 * c);
+        const bf16x8 vv = *reinterpret_cast<const bf16x8*>(stg + (32 + r) * SR + 8 * c);
+        if (kw0 + r < a.Sk && 8 * c < a.D) {  // rows past the end, chunks past the head dimension: not written
+          const int64_t off = kvbase + (int64_t)(kw0 + r) * a.kss;
+          *reinterpret_cast<bf16x8*>(dK + off) = vk;
+          *reinterpret_cast<bf16x8*>(dV + off) = vv;
+        }
+      }
+      barrier_lds();  // every wave's reads are done before a next pass refills the ring
     }
   }
 }
