@@ -174,7 +174,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       acck[d] = f32x16{};
       accv[d] = f32x16{};
     }
-    wait_all_vmem();  // K and V rows landed (a wait the compiler sees) before the copy ring starts
 
     // Mask reads: byte offset of element (row, key) in the (b, h) slice is
     // row*msq*4 + key*msk*4; lanes fix the key (clamped) and the 4-row group.
@@ -587,9 +586,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         }
       };
 
-      // Prologue: L/Delta of tiles 0-3, Q/dO of tiles 0 and 1 and most of tile 2's
-      // copies; all landed; L/Delta of tiles 0 and 1 fixed (steps 0 and 1
-      // fix those of tiles 2 and 3).
+      // Prologue: L/Delta of tiles 0-3 and Q/dO of tile 0, landed together with
+      // the K and V rows; then Q/dO of tile 1 and most of tile 2's copies, which
+      // stream in while the first section computes (the first step waits for
+      // tile 1 itself); L/Delta of tiles 0 and 1 fixed (steps 0 and 1 fix those
+      // of tiles 2 and 3).
       // Mask staging: element r of half `half` of tile (g, t) into sM[wave][r].
       auto mask_src = [&](int g) {
         return raw_rsrc(a.mask + (int64_t)b * a.msb + (int64_t)(kvh * a.group + g) * a.msh, a.mask_rec);
@@ -628,11 +629,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         issue_ld(cl, s);
         advance(cl);
       }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        issue_qdo(cq, s);
-        advance(cq);
-      }
+      issue_qdo(cq, 0);
+      advance(cq);
+      wait_all_vmem();  // K, V, L/Delta and tile 0 landed (a wait the compiler sees)
+      issue_qdo(cq, 1);
+      advance(cq);
       // A tile's copies go out over four sections, from the barrier on (the
       // vector-memory unit takes a copy per ~16 cycles per CU, so a burst of them
       // would hold up the issuing wave): a quarter each in sections B, C and D of
@@ -641,7 +642,6 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
 #pragma unroll
       for (int u = 0; u < NC - PER; ++u) issue_job(pend, u);
       advance(cq);
-      wait_vmcnt<0>();
       barrier_lds();
       fix_rd(0);
       fix_wr(0);
@@ -708,6 +708,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           copies_at(pend, NC / 2 + PER, k, NSD);
           mask_refill(mrs_a, qt, 1, k);
         });
+        // Step 0: tile 1's copies went out in the prologue, followed only by tile
+        // 2's (NC) and section A's mask copies, fewer than the steady state has.
+        if (it == 0) wait_vmcnt<NC + (MASK ? kMaskPerStep / 2 : 0)>();
         wait_prev();  // tile it+1 landed everywhere once all waves pass the barrier
         barrier_only();
         const Cursor cl_now = cl;  // tile it+4: the copies' cursor of the next step
