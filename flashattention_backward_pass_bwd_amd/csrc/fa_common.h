@@ -96,6 +96,13 @@ __device__ __forceinline__ float halves_max(float x) {  // max(x[lane], x[lane ^
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
   return fmaxf(a, b);
 }
+// Integer sum over the 64 lanes of a wave, in every lane.
+__device__ __forceinline__ int wave_sum_i32(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
 // Sum over each aligned group of N consecutive lanes (N = 1, 2, 4, ..., 64), in
 // every lane of the group: quad_perm swaps lanes 1 and 2 apart, the half-row
 // mirror pairs the two quads of an 8-lane half, the row mirror the two halves

@@ -194,10 +194,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     int64_t ws_p = 0;  // WS: workspace tiles of the key blocks before this one, per (b, h)
     if constexpr (WS) {
       qb -= qb % BQ;
-      for (int k = 0; k < kb; ++k) {
+      // the key blocks before this one, one per lane (a run has at most 2^23
+      // tiles, so 64 of them sum exactly in 32 bits)
+      for (int c0 = 0; c0 < kb; c0 += 64) {
         int ql, n;
-        ws_run(a, k, ql, n);
-        ws_p += n;
+        ws_run(a, c0 + lane, ql, n);
+        ws_p += __builtin_amdgcn_readfirstlane(wave_sum_i32(c0 + lane < kb ? n : 0));
       }
     }
     const int ntq = (qe - qb + BQ - 1) / BQ;

@@ -71,24 +71,28 @@ __global__ __launch_bounds__(256, BK == 32 ? 2 : 1) void dqs_bf16_kernel(Prefill
   // Key blocks whose workspace tile holds this query tile: an interval
   // [kb0, kb1] (a key block's first and last visible rows never decrease with
   // it), and the workspace index of the first one's tile.
+  // Found 64 key blocks at a time, one per lane: kb0 and kb1 are the first and
+  // last lanes whose run holds the tile, tp0 the sum of the runs before kb0 (a
+  // run has at most 2^23 tiles, so 64 of them sum exactly in 32 bits).
   int kb0 = -1, kb1 = -2, ql0 = 0, n0 = 0;
   int64_t tp0 = 0;
-  {
-    int64_t tp = 0;
-    for (int k = 0; k < nkb; ++k) {
-      int ql, n;
-      ws_run(a, k, ql, n);
-      if (ql > qtile) break;
-      if (qtile < ql + n) {
-        if (kb0 < 0) {
-          kb0 = k;
-          tp0 = tp;
-          ql0 = ql;
-          n0 = n;
-        }
-        kb1 = k;
+  for (int c0 = 0; c0 < nkb; c0 += 64) {
+    const int k = c0 + lane;
+    int ql, n;
+    ws_run(a, k, ql, n);
+    const bool in_range = k < nkb;
+    const uint64_t holds = __ballot(in_range && qtile >= ql && qtile < ql + n);
+    if (holds != 0) {
+      const int f = __ffsll((unsigned long long)holds) - 1;
+      if (kb0 < 0) {
+        kb0 = c0 + f;
+        ql0 = __builtin_amdgcn_readfirstlane(__shfl(ql, f));
+        n0 = __builtin_amdgcn_readfirstlane(__shfl(n, f));
+        tp0 += __builtin_amdgcn_readfirstlane(wave_sum_i32(lane < f ? n : 0));
       }
-      tp += n;
+      kb1 = c0 + 63 - __clzll((unsigned long long)holds);
+    } else if (kb0 < 0) {
+      tp0 += __builtin_amdgcn_readfirstlane(wave_sum_i32(in_range ? n : 0));
     }
   }
   const int nsteps = kb0 >= 0 ? JS * (kb1 - kb0 + 1) : 0;
