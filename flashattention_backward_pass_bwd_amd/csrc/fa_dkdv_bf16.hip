@@ -30,8 +30,11 @@
 // into -Delta in place.  The S chain starts from the rows' -L/scale, so its
 // fp32 result times scale*log2(e) is the exponent and P is one multiply and an
 // exp2 (K enters the MFMAs as it is stored: no rounding of a scaled copy); without
-// dropout the dP chain starts from -Delta and yields dP - Delta directly.  For causal attention without a window, block i
-// also takes key block nkb-1-i, so every block carries the same work.
+// dropout the dP chain starts from -Delta and yields dP - Delta directly.  For
+// causal attention without a window, block i also takes key block nkb-1-i, so
+// every block carries the same work; it walks that second key block's tiles
+// upwards, which keeps the blocks of a KV head on the same tile (see the walk
+// order below).  At the end dK and dV leave through LDS as whole-row stores.
 //
 // Workspace mode (WS): the pass also stores every tile's dS, as the bf16 values
 // its dK contraction used, into the dS workspace (layout in fa_common.h) for
