@@ -394,9 +394,9 @@ __global__ __launch_bounds__(256, 1) void dq2_bf16_kernel(PrefillArgs a, const _
       const int last = ntiles - 1;
       const int e0 = min(f0, last);
       const int e1 = max(e0, min(f1 - 1, last));
-      for (; it < e0;) step(no);
-      for (; it < e1;) step(yes);
-      for (; it < last;) step(no);
+      while (it < e0) step(no);  // (step advances it)
+      while (it < e1) step(yes);
+      while (it < last) step(no);
 
       // Tile `last`: its second half, the dQ of its first half, then of its second.
       {
