@@ -196,7 +196,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
     static_assert(!WS || (BQ == kWsRows && kDkdvKeysPerBlock == kWsKeys), "workspace tiles are the pass's tiles");
     int64_t ws_p = 0;  // WS: workspace tiles of the key blocks before this one, per (b, h)
     if constexpr (WS) {
-      qb -= qb % BQ;
+      // Tiles start on a multiple of 64 rows; a key block no row sees keeps its
+      // empty range (aligning it down would make a tile the workspace has no
+      // room for: its run is empty).
+      if (qe > qb) qb -= qb % BQ;
       // the key blocks before this one, one per lane (a run has at most 2^23
       // tiles, so 64 of them sum exactly in 32 bits)
       for (int c0 = 0; c0 < kb; c0 += 64) {
