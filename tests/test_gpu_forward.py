@@ -16,7 +16,7 @@ import oracle
 from flashattention_backward_pass_bwd_amd import api, synth
 
 from fa_testlib import assert_close, dev, logical, say, spec_of
-from test_gpu_parity import CASES
+from test_gpu_parity import CASES, DEGENERATE
 
 pytestmark = pytest.mark.gpu
 
@@ -58,6 +58,20 @@ def _check(w, inp, mask_dev=None):
 def test_forward_parity(name):
     w = FWD_CASES[name]
     say(f"[forward] {name}: {w}")
+    _check(w, synth.prefill_inputs(w))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("sq,sk,causal", DEGENERATE)
+def test_forward_degenerate_sizes(dtype, sq, sk, causal):
+    """One query or one key, two of each, one past a tile edge (the backward's
+    degenerate cases), for O, L and the L-only sweep."""
+    base = synth.CAUSAL_F32 if dtype == "f32" else synth.LONG_BF16
+    w = base.resized(batch=1, num_heads=2, num_kv_heads=1, seq_q=sq, seq_k=sk, causal=causal, causal_offset=0,
+                     seed=60 + sq + 7 * sk)
+    if sq > 2 and sk > 2:
+        w = w.resized(dropout_p=0.2, dropout_seed=5)
+    say(f"[forward degenerate] {w}")
     _check(w, synth.prefill_inputs(w))
 
 

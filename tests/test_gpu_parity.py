@@ -114,6 +114,9 @@ DS_CASES.update({
     "ds_keys_past_the_rows_drop_d64": synth.EXTRAS_BF16.resized(head_dim=64, batch=2, num_heads=4, num_kv_heads=1,
                                                                 seq_q=100, seq_k=400, window=0, mask_density=0.0,
                                                                 scale=0.125, seed=38),
+    # a non-causal window with keys past every row's window: unseen key blocks there too
+    "ds_window_keys_past_the_rows_d128": synth.LONG_BF16.resized(num_heads=2, num_kv_heads=1, seq_q=100,
+                                                                 seq_k=400, causal=False, window=30, seed=39),
     "ds_mha_noncausal_d64": synth.LONG_BF16.resized(head_dim=64, batch=2, num_heads=3, num_kv_heads=3,
                                                     seq_q=190, seq_k=260, causal=False, seed=34),
 })
