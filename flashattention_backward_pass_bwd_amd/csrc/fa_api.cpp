@@ -21,6 +21,30 @@ constexpr int64_t kMaxSeq = int64_t(1) << 29;  // sequence lengths, causal offse
 constexpr int64_t kMaxRowStride = int64_t(1) << 24;  // elements between consecutive rows
 constexpr int64_t kMaxMaskStride = int64_t(1) << 22;  // mask row / column stride, elements (bf16 path)
 
+// The outputs share the inputs' strides (dQ and O Q's, dK and dV K's), so a
+// stride set must map distinct (b, s, h, d) to distinct elements, or blocks
+// would write the same memory.  Sufficient: taken by increasing stride, every
+// dimension of extent > 1 steps past the whole span of the smaller ones (the
+// head_dim elements of a row first).
+bool non_overlapping(int64_t head_dim, const int64_t (&st)[3], const int64_t (&ext)[3]) {
+  int order[3] = {0, 1, 2};
+  for (int i = 0; i < 3; ++i)
+    for (int j = i + 1; j < 3; ++j)
+      if (st[order[j]] < st[order[i]]) {
+        const int t = order[i];
+        order[i] = order[j];
+        order[j] = t;
+      }
+  int64_t span = head_dim;  // elements from a row's first to one past the last seen so far
+  for (int i = 0; i < 3; ++i) {
+    const int k = order[i];
+    if (ext[k] <= 1) continue;
+    if (st[k] < span) return false;
+    span += st[k] * (ext[k] - 1);
+  }
+  return true;
+}
+
 fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
   if (p == nullptr) return FA_ERR_NULL;
   if (p->dtype != FA_DTYPE_F32 && p->dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
@@ -46,6 +70,9 @@ fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
     if (qs[i] < 0 || ks[i] < 0) return FA_ERR_ARG;
     if (qs[i] % per16 != 0 || ks[i] % per16 != 0) return FA_ERR_ALIGN;
   }
+  const int64_t qe[3] = {p->batch, p->seq_q, p->num_heads};
+  const int64_t ke[3] = {p->batch, p->seq_k, p->num_kv_heads};
+  if (!non_overlapping(p->head_dim, qs, qe) || !non_overlapping(p->head_dim, ks, ke)) return FA_ERR_ARG;
   // Tile copies address rows by 32-bit byte offsets from a tile's first row.
   if (p->q_stride_s > kMaxRowStride || p->kv_stride_s > kMaxRowStride) return FA_ERR_UNSUPPORTED;
   int64_t mask_rec = 0;

@@ -71,6 +71,11 @@ typedef void* fa_stream_t;
  * key-side tensors), so both [B,S,H,D] and [B,H,S,D] storage are expressed
  * by choosing the strides.  head_dim is unit-stride.  The four query-side
  * tensors share one stride set; the four key-side tensors share the other.
+ * Since the outputs are written through them, each set must map distinct
+ * (b, s, h, d) to distinct elements (FA_ERR_ARG otherwise; checked as:
+ * taken by increasing stride, each dimension of extent > 1 steps past the
+ * whole span of the smaller ones, head_dim first), so no stride of such a
+ * dimension is 0.
  * The sequence strides q_stride_s and kv_stride_s may not exceed 2^24
  * elements (FA_ERR_UNSUPPORTED): tile copies use 32-bit row offsets.  For
  * bf16 with a mask, mask_stride_q and mask_stride_k must be below 2^22

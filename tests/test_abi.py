@@ -99,6 +99,11 @@ BAD = [
     ("q_stride_s", 8 * 128 + 4, _lib.FA_ERR_ALIGN),
     ("kv_stride_h", 130, _lib.FA_ERR_ALIGN),
     ("q_stride_b", -1, _lib.FA_ERR_ARG),
+    # outputs are written through the same strides: layouts whose rows overlap are rejected
+    ("q_stride_b", 0, _lib.FA_ERR_ARG),        # two batches on one row set
+    ("kv_stride_s", 0, _lib.FA_ERR_ARG),       # every key on one row
+    ("q_stride_h", 64, _lib.FA_ERR_ARG),       # heads 64 elements apart, rows of 128
+    ("kv_stride_b", 2 * 128, _lib.FA_ERR_ARG),  # batch 1 starts inside batch 0's keys
     # head_dim: any multiple of 8 up to 128
     ("head_dim", 0, _lib.FA_ERR_SHAPE),
     ("head_dim", 100, _lib.FA_ERR_UNSUPPORTED),
@@ -342,3 +347,24 @@ def test_general_head_dims_pass_validation(head_dim):
         assert L.fa_fwd(P, FAKE, FAKE, FAKE, None, FAKE, None) == _lib.FA_ERR_NULL
         if dtype == _lib.FA_DTYPE_BF16:
             assert _ws_bytes(L, p) > 0
+
+
+@pytest.mark.parametrize("layout", ["bshd", "bhsd", "padded_rows", "size_one_dims_any_stride"])
+def test_non_overlapping_layouts_are_accepted(layout):
+    """[B,S,H,D], [B,H,S,D], rows padded past head_dim, and dimensions of extent 1
+    with any stride pass the layout check (workspace sizing validates the
+    parameters without launching anything)."""
+    p = _valid()
+    if layout == "bhsd":
+        p.q_stride_b, p.q_stride_h, p.q_stride_s = 8 * 100 * 128, 100 * 128, 128
+        p.kv_stride_b, p.kv_stride_h, p.kv_stride_s = 2 * 120 * 128, 120 * 128, 128
+    elif layout == "padded_rows":
+        p.head_dim = 40
+        p.q_stride_b, p.q_stride_s, p.q_stride_h = 100 * 8 * 64, 8 * 64, 64
+        p.kv_stride_b, p.kv_stride_s, p.kv_stride_h = 120 * 2 * 64, 2 * 64, 64
+    elif layout == "size_one_dims_any_stride":
+        p.batch, p.num_kv_heads = 1, 1
+        p.q_stride_b, p.kv_stride_b, p.kv_stride_h = 0, 8, 0
+    size = ctypes.c_uint64(0)
+    assert _lib.lib().fa_bwd_ds_workspace_size(ctypes.byref(p), ctypes.byref(size)) == _lib.FA_OK
+    assert size.value > 0
