@@ -50,6 +50,11 @@ CASES = {
                                                        causal_offset=220, window=130, seed=23),
     "noncausal_bf16_d128": synth.LONG_BF16.resized(batch=2, num_heads=4, num_kv_heads=2, seq_q=333, seq_k=190,
                                                    causal=False, seed=22),
+    # a causal offset past every key (each row sees all keys) and a group of 16 query heads per KV head
+    "offset_past_keys_bf16_group16": synth.LONG_BF16.resized(num_heads=16, num_kv_heads=1, seq_q=150, seq_k=200,
+                                                             causal_offset=260, seed=41),
+    "offset_past_keys_f32": synth.CAUSAL_F32.resized(batch=1, num_heads=2, num_kv_heads=1, seq_q=90, seq_k=130,
+                                                     causal_offset=200, seed=42),
     # plain causal with mask and dropout (no window): paired key blocks, the second walked upwards,
     # with the mask staged per element (Sk % 4 != 0) and per 4-key group (Sk % 4 == 0)
     "causal_mask_drop_bf16_d128": synth.EXTRAS_BF16.resized(batch=1, num_heads=4, num_kv_heads=2, seq_q=333,
