@@ -75,3 +75,25 @@ def test_decode_full_workload():
     assert_close(ds, ref_s, "f32", "d_scores")
     assert_close(dq, ref_q, "f32", "d_q")
     _check_pass2(res, w.n_heads // w.n_kv_heads, [0, 17, w.num_seqs - 1])
+
+
+def _random_case(n):
+    r = np.random.default_rng(7000 + n)
+    d = int(r.choice([64, 128, 256]))
+    hkv = int(r.choice([1, 2, 4, 8]))
+    g = int(r.choice([1, 2, 4, 8]))
+    w = synth.DECODE_F32.resized(num_seqs=int(r.integers(1, 4)), n_heads=hkv * g, n_kv_heads=hkv, head_dim=d,
+                                 history_len=int(r.integers(1, 2500)), seed=int(r.integers(0, 2**31)))
+    return w
+
+
+@pytest.mark.parametrize("n", range(24))
+def test_decode_random_shapes(n):
+    """Seeded random head_dim, grouping, sequence count and history length (up to
+    2,500 rows), both passes against the oracle."""
+    w = _random_case(n)
+    say(f"[decode random {n}] {w}")
+    ds, dq, ref_s, ref_q, res = _run(w)
+    assert_close(ds, ref_s, "f32", "d_scores")
+    assert_close(dq, ref_q, "f32", "d_q")
+    _check_pass2(res, w.n_heads // w.n_kv_heads, None)
