@@ -249,10 +249,6 @@ __device__ __forceinline__ bool elem_visible(int r, int lb, uint32_t span) {
   return d < span;
 }
 
-// Moves a value into accumulation registers once, so that later MFMAs read it
-// there as a B operand without a copy per use.
-__device__ __forceinline__ void to_agpr(bf16x8& v) { asm volatile("" : "+a"(v)); }
-
 // Sixteen zero bytes in device memory: a lane whose chunk of a register-held
 // row lies past a padded head dimension loads its operand from here.
 static __device__ __attribute__((aligned(16))) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
