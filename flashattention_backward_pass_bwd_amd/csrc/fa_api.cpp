@@ -56,6 +56,11 @@ fa_status check_prefill(const fa_bwd_params* p, PrefillArgs* a) {
   if (p->head_dim > 128 || p->head_dim % 8 != 0) return FA_ERR_UNSUPPORTED;
   if (p->seq_q > kMaxSeq || p->seq_k > kMaxSeq || p->causal_offset > kMaxSeq || p->window > kMaxSeq)
     return FA_ERR_UNSUPPORTED;
+  // Grids count their blocks (a (b, head) pair times tiles of 32 or more rows
+  // or keys) and kernels index (b, head) pairs in 32 bits.
+  const int64_t heads = (int64_t)p->batch * p->num_heads;
+  if (heads * ((p->seq_q + 31) / 32) >= (int64_t(1) << 31) || heads * ((p->seq_k + 31) / 32) >= (int64_t(1) << 31))
+    return FA_ERR_UNSUPPORTED;
   if (p->causal != 0 && p->causal != 1) return FA_ERR_ARG;
   if (p->causal_offset < 0 || p->window < 0) return FA_ERR_ARG;
   if (!(p->dropout_p >= 0.0f && p->dropout_p < 1.0f)) return FA_ERR_ARG;  // also rejects NaN

@@ -44,7 +44,8 @@ typedef enum fa_status {
   FA_ERR_SHAPE = -2,       /* a size <= 0, or num_heads % num_kv_heads != 0 */
   FA_ERR_UNSUPPORTED = -3, /* head_dim (prefill: not a multiple of 8 up to 128), dtype, history length or
                               row stride outside the built kernels,
-                              or seq_q, seq_k, causal_offset or window above 2^29 */
+                              or seq_q, seq_k, causal_offset or window above 2^29,
+                              or batch * num_heads * ceil(max(seq_q, seq_k) / 32) >= 2^31 */
   FA_ERR_ALIGN = -4,       /* base or row stride not a multiple of 16 bytes, or D not unit-stride */
   FA_ERR_ARG = -5,         /* dropout_p not in [0,1), causal_offset < 0, window < 0, bad stride,
                               scale zero or not finite */

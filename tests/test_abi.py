@@ -104,6 +104,8 @@ BAD = [
     ("kv_stride_s", 0, _lib.FA_ERR_ARG),       # every key on one row
     ("q_stride_h", 64, _lib.FA_ERR_ARG),       # heads 64 elements apart, rows of 128
     ("kv_stride_b", 2 * 128, _lib.FA_ERR_ARG),  # batch 1 starts inside batch 0's keys
+    # block counts fit 32 bits: batch * num_heads * ceil(seq / 32) < 2^31
+    ("batch", 1 << 26, _lib.FA_ERR_UNSUPPORTED),
     # head_dim: any multiple of 8 up to 128
     ("head_dim", 0, _lib.FA_ERR_SHAPE),
     ("head_dim", 100, _lib.FA_ERR_UNSUPPORTED),
