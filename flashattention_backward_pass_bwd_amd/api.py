@@ -2,8 +2,10 @@
 
 Tensor convention: query-side tensors (q, o, do, dq) are indexed [B, Sq, Hq, D]
 and key-side tensors (k, v, dk, dv) [B, Sk, Hkv, D]; any strides are accepted
-as long as D is unit-stride, rows are 16-byte aligned and the tensors of one
-side share one stride set (so [B,H,S,D] storage is passed as ``x.transpose(1, 2)``).
+as long as D is unit-stride, rows are 16-byte aligned, the tensors of one side
+share one stride set (so [B,H,S,D] storage is passed as ``x.transpose(1, 2)``)
+and that set maps distinct elements to distinct memory (the outputs are
+written through it: no broadcast, stride-0 batch or sequence dimensions).
 lse and delta are fp32 contiguous [B, Hq, Sq].  All calls enqueue on torch's
 current HIP stream and return without synchronising.
 """
