@@ -445,6 +445,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
       // of tile (qt, h) (values se, dpe; L ring stage lste) and with the transposed
       // reads of the first NP MFMAs of that half's dV/dK (stage ste).  Operand
       // reads run PF MFMAs ahead; the 16 exp/dS elements are spread over the slots.
+      // The last XD elements of an exp/dS half: their exponent input is formed in
+      // the S/dP section (with the mask and the visibility test), their exp, P,
+      // dS and packing in the first slots of the dV/dK section that follows,
+      // whose MFMAs leave issue slots free (the S/dP sections have none), before
+      // its MFMAs that read them (the second eight).
+#ifndef FA_DKDV_XD
+#define FA_DKDV_XD 2
+#endif
+      constexpr int XD = FA_DKDV_XD;
+      static_assert(XD % 2 == 0 && XD <= 8, "deferred elements come in packed pairs of the second eight");
+      struct Defer {
+        float x[XD > 0 ? XD : 1], dpe[XD > 0 ? XD : 1], dl[XD > 0 ? XD : 1];
+        uint32_t rk[XD > 0 ? XD : 1];
+      };
+      Defer df;
       auto sec_sdp_ew = [&](auto full_c, int ms, int sts, f32x16& s, f32x16& dp, const SdpPre& pre, int me,
                             int ste, int qt, const f32x16& se, const f32x16& dpe,
                             bf16x8 (&pmc)[2], bf16x8 (&dsc)[2], bf16x4 (&trp)[2 * NP], auto&& slot_extra) {
@@ -478,10 +493,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
           float x = se[r] * a.scale_log2;
           if constexpr (MASK) x = __builtin_fmaf(mk[r], kLog2e, x);
           if constexpr (!FULL) x = elem_visible(r, lb, span) ? x : -__builtin_inff();
+          if (r >= 16 - XD) {  // finished in the next dV/dK section
+            const int u = r - (16 - XD);
+            df.x[u] = x;
+            df.dpe[u] = dpe[r];
+            if constexpr (DROP) {
+              df.rk[u] = pre.rk[r >> 2][r & 3];
+              df.dl[u] = pre.dl[r >> 2][r & 3];
+            }
+            return;
+          }
           pr[r] = __builtin_amdgcn_exp2f(x);
         };
         // P and dS of element r, one slot after its exp; odd r packs the pair.
         auto ew_ds = [&](int r) {
+          if (r >= 16 - XD) return;
           if constexpr (DROP) {
             const float mm = fmix32_tail(pre.rk[r >> 2][r & 3] ^ jg) >= a.drop_thr ? a.drop_inv : 0.f;
             pv[r] = pr[r] * mm;
@@ -568,6 +594,41 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         materialise(pmc, dsc);
         mfma_settle(s, dp);
         fence();
+      };
+      // Slots 0 and 1 of a dV/dK section: the exps of the deferred elements, then
+      // their P and dS, packed into the second operand block.
+      float prd[XD > 0 ? XD : 1];
+      auto defer_slot = [&](int n, bf16x8 (&pmc)[2], bf16x8 (&dsc)[2]) {
+        if constexpr (XD > 0) {
+          if (n == 0) {
+#pragma unroll
+            for (int u = 0; u < XD; ++u) prd[u] = __builtin_amdgcn_exp2f(df.x[u]);
+          }
+          if (n == 1) {
+            float pv[XD > 0 ? XD : 1], dv[XD > 0 ? XD : 1];
+#pragma unroll
+            for (int u = 0; u < XD; ++u) {
+              if constexpr (DROP) {
+                const float mm = fmix32_tail(df.rk[u] ^ jg) >= a.drop_thr ? a.drop_inv : 0.f;
+                pv[u] = prd[u] * mm;
+                dv[u] = prd[u] * (df.dpe[u] * mm - df.dl[u]);
+              } else {
+                pv[u] = prd[u];
+                dv[u] = prd[u] * df.dpe[u];
+              }
+            }
+#pragma unroll
+            for (int u = 0; u < XD; u += 2) {
+              const int r = 16 - XD + u;  // even: the pair r, r + 1
+              const bf16x2 tp = pack_here(pv[u], pv[u + 1]);
+              const bf16x2 td = pack_here(dv[u], dv[u + 1]);
+              pmc[1][r & 7] = tp[0];
+              pmc[1][(r & 7) + 1] = tp[1];
+              dsc[1][r & 7] = td[0];
+              dsc[1][(r & 7) + 1] = td[1];
+            }
+          }
+        }
       };
       // Section "dV/dK" of half m (stage stq): MFMAs 0 .. NP-1 take the transposed
       // operands read by the previous section; slot n reads those of MFMA n + NP.
@@ -731,6 +792,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         constexpr int kLd = NDK >= 16 ? 2 : 1, kTurn = NDK >= 16 ? 3 : 1, kAdv = kTurn + 1;
         static_assert(kAdv + 4 < NDK, "the cursor update fits section B");
         sec_dkv(0, stq, trp, pm, ds, [&](int n) {
+          defer_slot(n, pm, ds);
           if (n == 0) next = job_of(cq, stq3);
           if (n == kLd) issue_ld(cl, lst4);
           if (n == kTurn) turn = turn_of(cl);
@@ -750,6 +812,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_bf16_kernel(PrefillArgs a, const 
         });
         // D: dV/dK of half 1; prefetch for A of the next step
         sec_dkv(1, stq, trp, pm, ds, [&](int n) {
+          defer_slot(n, pm, ds);
           copies_at(next, 2 * PER, n, NDK);
           pre_at(n, 1, stq1, lst1, 0, lst1);
           store_ds(n, 1, ds);
