@@ -20,9 +20,10 @@
 //   B: copies of tile it+3 (and L/Delta of tile it+4) issued; dV/dK of half 0
 //   C: S/dP of half 0 of tile it+1 with exp/dS of half 1
 //   D: dV/dK of half 1
-// so the exp/dS arithmetic of one half always overlaps the MFMAs of another,
-// and the next tile's first MFMAs follow the current tile's last without a
-// barrier in between.  Q and dO tiles live in a 4-stage LDS ring (swizzled,
+// so the exp/dS arithmetic of one half always overlaps the MFMAs of another
+// (its last two elements finish in the first slots of the dV/dK section that
+// follows, whose MFMAs leave issue slots free), and the next tile's first
+// MFMAs follow the current tile's last without a barrier in between.  Q and dO tiles live in a 4-stage LDS ring (swizzled,
 // see fa_tiles.h) filled by direct global->LDS copies three tiles ahead; one
 // barrier per tile separates the last reads of a stage from its refill.  L and
 // Delta (64 floats per tile) travel through an 8-stage ring four tiles ahead;
