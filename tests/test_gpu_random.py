@@ -7,7 +7,9 @@ density, dropout and path (fp32, bf16 recompute, bf16 shared dS) come from
 one seeded generator, so combinations nobody wrote down by hand run too (the
 stray workspace tile of key blocks no row sees was such a combination).
 Every output element against the fp64 oracle at the dtype's bar, and the
-forward's O and L on the same problem.
+forward's O and L on the same problem.  A second, wider draw (up to three KV
+heads, batch 3, masks of density 0.3, dropout 0.5, head_dims such as 24, 104
+and 120, sequences up to 900) checks the backward the same way.
 """
 import numpy as np
 import pytest
@@ -46,9 +48,42 @@ def _case(n):
     return variant, w
 
 
+N_WIDE = 160  # a wider draw: three KV heads, batch 3, heavier masks and dropout, more head_dims
+
+
+def _wide_case(n):
+    r = np.random.default_rng(20000 + n)
+    variant = ("f32", "bf16_recompute", "bf16_shared_ds")[n % 3]
+    dtype = "f32" if variant == "f32" else "bf16"
+    hkv = int(r.choice([1, 2, 3]))
+    group = int(r.choice([1, 2, 4, 8]))
+    d = int(r.choice([8, 24, 32, 48, 64, 80, 104, 120, 128]))
+    sq = int(r.integers(1, 900))
+    sk = int(r.integers(1, 900))
+    causal = bool(r.random() < 0.6)
+    offset = int(r.choice([0, 0, int(r.integers(0, 300)), int(r.integers(300, 900))])) if causal else 0
+    window = int(r.choice([0, 0, int(r.integers(1, 64)), int(r.integers(64, 600))]))
+    base = synth.CAUSAL_F32 if dtype == "f32" else synth.LONG_BF16
+    w = base.resized(name=f"random_wide_{n}", batch=int(r.choice([1, 2, 3])), num_heads=hkv * group,
+                     num_kv_heads=hkv, seq_q=sq, seq_k=sk, head_dim=d, scale=float(1.0 / np.sqrt(d)),
+                     layout=str(r.choice(["bshd", "bhsd"])), causal=causal, causal_offset=offset, window=window,
+                     mask_density=float(r.choice([0.0, 0.0, 0.05, 0.3])),
+                     dropout_p=float(r.choice([0.0, 0.0, 0.1, 0.5])), dropout_seed=int(r.integers(0, 2**31)),
+                     seed=int(r.integers(0, 2**31)))
+    return variant, w
+
+
 @pytest.mark.parametrize("n", range(N_CASES))
 def test_random_geometry(n):
-    variant, w = _case(n)
+    _check_backward(n, *_case(n))
+
+
+@pytest.mark.parametrize("n", range(N_WIDE))
+def test_random_geometry_wide(n):
+    _check_backward(n, *_wide_case(n))
+
+
+def _check_backward(n, variant, w):
     say(f"[random {n}] {variant}: {w}")
     inp = synth.prefill_inputs(w)
     o, lse = forward_inputs(w, inp)
